@@ -1,0 +1,248 @@
+"""Plain CPU oracle for the fp4 routed-expert decode path.
+
+TEST INFRASTRUCTURE ONLY. The tests, the smoke check and the bench's
+``cpu_baseline`` leg are the only callers. The product package never imports
+this module, and this module imports nothing from the product package.
+
+The arithmetic lives in ``oracle.c`` (float64 definition, plus an fp32 replay
+of the per-row chains); this file only builds that C file with gcc and
+marshals numpy arrays to it. Function-level citations are in ``oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_HDR = os.path.join(_HERE, "oracle.h")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c with gcc (no fast-math, no contraction) into liboracle.so."""
+    stale = (not os.path.exists(_LIB)) or any(
+        os.path.getmtime(p) > os.path.getmtime(_LIB) for p in (_SRC, _HDR))
+    if force or stale:
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off",
+               "-fno-fast-math", "-fopenmp", "-o", tmp, _SRC, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(_LIB)
+        i32, f64, u = ctypes.c_int, ctypes.c_double, ctypes.c_uint
+        P = ctypes.c_void_p
+        L.or_e2m1.argtypes = [u]
+        L.or_e2m1.restype = f64
+        L.or_e4m3fn.argtypes = [u]
+        L.or_e4m3fn.restype = f64
+        L.or_bf16.argtypes = [ctypes.c_uint16]
+        L.or_bf16.restype = f64
+        L.or_route.argtypes = [i32, i32, i32, P, P, P]
+        L.or_route.restype = None
+        L.or_bucket.argtypes = [i32, i32, i32, P, P, P, P]
+        L.or_bucket.restype = None
+        L.or_passes.argtypes = [i32, P, i32, P, P, i32]
+        L.or_passes.restype = i32
+        L.or_plan.argtypes = [i32, P, P, P, i32, P, i32]
+        L.or_plan.restype = i32
+        L.or_matvec.argtypes = [i32, i32, P, P, P, P]
+        L.or_matvec.restype = None
+        L.or_swiglu.argtypes = [i32, P, P, P]
+        L.or_swiglu.restype = None
+        L.or_combine.argtypes = [i32, i32, P, P, P]
+        L.or_combine.restype = None
+        L.or_layer.argtypes = [i32] * 5 + [P] * 13
+        L.or_layer.restype = i32
+        L.or_chain32.argtypes = [i32, i32, P, P, P, P]
+        L.or_chain32.restype = None
+        L.or_combine32.argtypes = [i32, i32, P, P, P]
+        L.or_combine32.restype = None
+        L.or_omp_threads.argtypes = []
+        L.or_omp_threads.restype = i32
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# ------------------------------------------------------------------ codecs
+def e2m1(code: int) -> float:
+    return lib().or_e2m1(int(code))
+
+
+def e4m3fn(byte: int) -> float:
+    return lib().or_e4m3fn(int(byte))
+
+
+def bf16(bits: int) -> float:
+    return lib().or_bf16(int(bits))
+
+
+def decode_matrix(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """float64 W[N][K] from the plain layout (tables built from the oracle's codecs)."""
+    t4 = np.array([e2m1(c) for c in range(16)], dtype=np.float64)
+    t8 = np.array([e4m3fn(b) for b in range(256)], dtype=np.float64)
+    codes = np.asarray(codes, dtype=np.uint8)
+    N, half = codes.shape
+    K = half * 2
+    w = np.empty((N, K), dtype=np.float64)
+    w[:, 0::2] = t4[codes & 15]
+    w[:, 1::2] = t4[codes >> 4]
+    s = t8[np.asarray(scales, dtype=np.uint8)]
+    return w * np.repeat(s, 32, axis=1)
+
+
+# ----------------------------------------------------------------- routing
+def route(logits: np.ndarray, k: int):
+    logits = _c(logits, np.float32)
+    R, E = logits.shape
+    ids = np.zeros((R, k), dtype=np.int32)
+    w = np.zeros((R, k), dtype=np.float64)
+    lib().or_route(R, E, k, _p(logits), _p(ids), _p(w))
+    return ids, w
+
+
+def bucket(topk_id: np.ndarray, E: int):
+    topk_id = _c(topk_id, np.int32)
+    R, k = topk_id.shape
+    count = np.zeros(E, dtype=np.int32)
+    offset = np.zeros(E + 1, dtype=np.int32)
+    entry = np.zeros(R * k, dtype=np.int32)
+    lib().or_bucket(R, E, k, _p(topk_id), _p(count), _p(offset), _p(entry))
+    return count, offset, entry
+
+
+def passes(n: int, tiers):
+    t = _c(list(tiers), np.int32)
+    size = np.zeros(64, dtype=np.int32)
+    real = np.zeros(64, dtype=np.int32)
+    m = lib().or_passes(int(n), _p(t), len(t), _p(size), _p(real), 64)
+    return [(int(size[i]), int(real[i])) for i in range(m)]
+
+
+def plan(count: np.ndarray, offset: np.ndarray, tiers):
+    count = _c(count, np.int32)
+    offset = _c(offset, np.int32)
+    t = _c(list(tiers), np.int32)
+    cap = int(count.sum()) + 1
+    out = np.zeros((cap, 4), dtype=np.int32)
+    m = lib().or_plan(len(count), _p(count), _p(offset), _p(t), len(t), _p(out), cap)
+    assert m <= cap
+    return out[:m].copy()
+
+
+# -------------------------------------------------------- float64 layer math
+def matvec(codes, scales, x) -> np.ndarray:
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    x = _c(x, np.float64)
+    N = codes.shape[0]
+    K = codes.shape[1] * 2
+    assert scales.shape == (N, K // 32) and x.shape == (K,)
+    y = np.zeros(N, dtype=np.float64)
+    lib().or_matvec(N, K, _p(codes), _p(scales), _p(x), _p(y))
+    return y
+
+
+def swiglu(g, u) -> np.ndarray:
+    g = _c(g, np.float64)
+    u = _c(u, np.float64)
+    a = np.zeros_like(g)
+    lib().or_swiglu(g.size, _p(g), _p(u), _p(a))
+    return a
+
+
+def combine(w, out) -> np.ndarray:
+    w = _c(w, np.float64)
+    out = _c(out, np.float64)
+    k, H = out.shape
+    y = np.zeros(H, dtype=np.float64)
+    lib().or_combine(k, H, _p(w), _p(out), _p(y))
+    return y
+
+
+def bf16_to_f64(x_bits: np.ndarray) -> np.ndarray:
+    b = _c(x_bits, np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def layer(x_bf16: np.ndarray, logits: np.ndarray, experts: dict, H: int, I: int, E: int, k: int):
+    """float64 layer over R rows.
+
+    ``experts`` maps expert id -> dict with the six plain-layout arrays
+    (gate_codes, gate_scales, up_codes, up_scales, down_codes, down_scales).
+    Returns dict(topk_id, topk_w, act[R][k][I], out[R][k][H], y[R][H], threads).
+    """
+    x_bf16 = _c(x_bf16, np.uint16)
+    logits = _c(logits, np.float32)
+    R = x_bf16.shape[0]
+    assert x_bf16.shape == (R, H) and logits.shape == (R, E)
+    names = ("gate_codes", "gate_scales", "up_codes", "up_scales", "down_codes", "down_scales")
+    keep = []
+    tables = []
+    for nm in names:
+        arr = (ctypes.c_void_p * E)()
+        for e, ex in experts.items():
+            a = _c(ex[nm], np.uint8)
+            keep.append(a)
+            arr[e] = a.ctypes.data
+        tables.append(arr)
+    topk_id = np.zeros((R, k), dtype=np.int32)
+    topk_w = np.zeros((R, k), dtype=np.float64)
+    act = np.zeros((R, k, I), dtype=np.float64)
+    out = np.zeros((R, k, H), dtype=np.float64)
+    y = np.zeros((R, H), dtype=np.float64)
+    # every selected expert must be present
+    ids_chk, _ = route(logits, k)
+    missing = set(int(e) for e in np.unique(ids_chk)) - set(experts)
+    if missing:
+        raise KeyError("oracle.layer: experts %s are routed but not given" % sorted(missing))
+    threads = lib().or_layer(H, I, E, k, R, _p(x_bf16), _p(logits), *tables,
+                             _p(topk_id), _p(topk_w), _p(act), _p(out), _p(y))
+    return dict(topk_id=topk_id, topk_w=topk_w, act=act, out=out, y=y, threads=threads)
+
+
+# ------------------------------------------------------ fp32 chain replay
+def chain32(codes, scales, x_f32) -> np.ndarray:
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    x = _c(x_f32, np.float32)
+    N = codes.shape[0]
+    K = codes.shape[1] * 2
+    assert x.shape == (K,)
+    y = np.zeros(N, dtype=np.float32)
+    lib().or_chain32(N, K, _p(codes), _p(scales), _p(x), _p(y))
+    return y
+
+
+def combine32(w_f32, out_f32) -> np.ndarray:
+    w = _c(w_f32, np.float32)
+    out = _c(out_f32, np.float32)
+    k, H = out.shape
+    y = np.zeros(H, dtype=np.float32)
+    lib().or_combine32(k, H, _p(w), _p(out), _p(y))
+    return y
+
+
+def omp_threads() -> int:
+    return lib().or_omp_threads()
