@@ -1,0 +1,329 @@
+#!/usr/bin/env python3
+"""Bench: MoE decode rows/s and expert-weight HBM GB/s (% of peak) on one MI355X.
+
+A step is one 40-layer round: 40 independent synthetic release-width layers
+(hidden 4096, expert intermediate 2048, 256 experts, top-8), each running the
+whole hot path (route + bucket, gate/up + SwiGLU, down, combine) through the C
+ABI. The round is captured once as a HIP graph and replayed; all weights
+(40 x 256 experts, 13,369,344 B each) are resident in HBM before timing.
+
+The headline line is the one-row workload; the four-row same-expert and the
+sixteen-row random workloads are reported as extra cells on the same line.
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE decode rows/s + expert-weight HBM GB/s (% of peak), 1–16 rows/layer"
+HBM_PEAK_GBPS = 8000.0
+CUS, LANES, CLOCK_GHZ = 256, 64, 2.4     # fp32 vector fma lanes per CU per clock, unpacked
+
+
+def log(msg: str) -> None:
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=40)
+    ap.add_argument("--cells", default="one_row,four_same,sixteen_random")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU work budget of the oracle sample")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------- weights
+class Model:
+    """40 layers x 256 experts of packed weights, one uint8 buffer per layer."""
+
+    def __init__(self, cfg, layers: int):
+        import torch
+        import synth
+        from fp4_routed_expert_xp_amd import xp
+        self.cfg = cfg
+        H, I, E = cfg.H, cfg.I, cfg.E
+        self.expert_bytes = cfg.expert_bytes
+        plain = torch.empty(E * self.expert_bytes, dtype=torch.uint8, device="cuda")
+        self.buffers, self.tables = [], []
+        shapes = {"gate": (I, H), "up": (I, H), "down": (H, I)}
+        for l in range(layers):
+            lay = synth.device_layer_plain(cfg.weight_seed, l, H, I, E, cfg.emin, cfg.emax, plain)
+            stride, offs = lay["stride"], lay["offsets"]
+            packed = torch.empty_like(plain)
+            tab = []
+            for e in range(E):
+                row = []
+                for m in ("gate", "up", "down"):
+                    N, K = shapes[m]
+                    co, cn = offs[m + "_codes"]
+                    so, sn = offs[m + "_scales"]
+                    b = e * stride
+                    xp.xp_pack_matrix(plain[b + co:b + co + cn].view(N, K // 2), plain[b + so:b + so + sn],
+                                      packed[b + co:b + co + cn], packed[b + so:b + so + sn])
+                    row += [packed.data_ptr() + b + co, packed.data_ptr() + b + so]
+                tab.append(row)
+            self.buffers.append(packed)
+            self.tables.append(torch.tensor(tab, dtype=torch.int64).cuda())
+        torch.cuda.synchronize()
+        del plain
+
+
+def copy_bandwidth_gbps() -> float:
+    import torch
+    n = 2 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / reps
+    return 2 * n / sec / 1e9
+
+
+# ------------------------------------------------------------------ cells
+class Cell:
+    def __init__(self, model: Model, cfg, layers: int):
+        import numpy as np
+        import torch
+        import synth
+        from fp4_routed_expert_xp_amd import xp
+        self.model, self.cfg, self.layers = model, cfg, layers
+        R, k, H, I, E = cfg.R, cfg.k, cfg.H, cfg.I, cfg.E
+        self.d = xp.dims(H, I, E, k)
+        self.x, self.logits, self.ws = [], [], []
+        for l in range(layers):
+            xb, lg = synth.layer_inputs(cfg, l, plant=False)
+            self.x.append(torch.from_numpy(xb.view(np.int16).copy()).cuda())
+            self.logits.append(torch.from_numpy(lg).cuda())
+            self.ws.append(torch.zeros(xp.xp_workspace_bytes(self.d, R), dtype=torch.uint8, device="cuda"))
+        self.topk_id = torch.empty((R, k), dtype=torch.int32, device="cuda")
+        self.topk_w = torch.empty((R, k), dtype=torch.float32, device="cuda")
+        self.act = torch.empty((R, k, I), dtype=torch.float32, device="cuda")
+        self.out = torch.empty((R, k, H), dtype=torch.float32, device="cuda")
+        self.y = torch.empty((R, H), dtype=torch.float32, device="cuda")
+
+    def layer(self, l: int, ev=None) -> None:
+        from fp4_routed_expert_xp_amd import xp
+        c, d, R, tab = self.cfg, self.d, self.cfg.R, self.model.tables[l]
+        if ev: ev[0].record()
+        xp.xp_route_bucket(d, R, self.logits[l], self.topk_id, self.topk_w, self.ws[l])
+        if ev: ev[1].record()
+        xp.xp_gateup_rows(d, R, self.x[l], tab, self.ws[l], self.act)
+        if ev: ev[2].record()
+        xp.xp_down_rows(d, R, self.act, tab, self.ws[l], self.out)
+        if ev: ev[3].record()
+        xp.xp_combine(d, R, self.out, self.topk_w, self.y)
+        if ev: ev[4].record()
+
+    def round(self) -> None:
+        for l in range(self.layers):
+            self.layer(l)
+
+    def plan_stats(self) -> dict:
+        """Distinct experts and pass sizes per layer, read back from the workspaces."""
+        import numpy as np
+        from fp4_routed_expert_xp_amd import xp
+        off = xp.xp_workspace_layout(self.d, self.cfg.R)
+        E = self.cfg.E
+        distinct, gu_rows, dn_rows = [], [], []
+        for ws in self.ws:
+            b = ws.cpu().numpy()
+            hdr = b[off[0]:off[0] + 8].view(np.int32)
+            cnt = b[off[1]:off[1] + 4 * E].view(np.int32)
+            gu = b[off[4]:off[4] + 16 * int(hdr[0])].view(np.int32).reshape(-1, 4)
+            dn = b[off[5]:off[5] + 16 * int(hdr[1])].view(np.int32).reshape(-1, 4)
+            distinct.append(int((cnt > 0).sum()))
+            gu_rows.append(int(gu[:, 3].sum()))     # rows computed incl. padding
+            dn_rows.append(int(dn[:, 3].sum()))
+        return dict(distinct=distinct, gu_rows=gu_rows, dn_rows=dn_rows)
+
+
+def time_cell(cell: Cell, steps: int, warmup: int) -> dict:
+    import torch
+    torch.cuda.synchronize()
+    cell.round()                      # one eager round (plans in place, lazy init done)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cell.round()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / steps
+    # per-kernel durations: each call of one eager round bracketed by events on the launch stream
+    L = cell.layers
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(L)]
+    per = {"route": 0.0, "gateup": 0.0, "down": 0.0, "combine": 0.0}
+    reps = 3
+    for _ in range(reps):
+        for l in range(L):
+            cell.layer(l, evs[l])
+        torch.cuda.synchronize()
+        for l in range(L):
+            ev = evs[l]
+            for i, name in enumerate(("route", "gateup", "down", "combine")):
+                per[name] += ev[i].elapsed_time(ev[i + 1]) * 1e3
+    per = {k: v / (reps * L) for k, v in per.items()}
+    del g
+    return dict(ms_per_round=ms, wall_s=wall, kernel_us=per)
+
+
+def cell_report(cell: Cell, t: dict, copy_gbps: float) -> dict:
+    cfg = cell.cfg
+    st = cell.plan_stats()
+    L = cell.layers
+    H, I, k, R = cfg.H, cfg.I, cfg.k, cfg.R
+    gu_w = 2 * (I * H // 2 + I * H // 32)            # gate+up bytes of one expert
+    dn_w = H * I // 2 + H * I // 32
+    distinct = sum(st["distinct"]) / L
+    unique_bytes = distinct * cfg.expert_bytes
+    layer_us = t["ms_per_round"] * 1e3 / L
+    gbps = unique_bytes / (layer_us * 1e-6) / 1e9
+    # gate/up launch: weights of its distinct experts + x read + act written
+    gu_bytes = distinct * gu_w + R * H * 2 + R * k * I * 4
+    gu_us = t["kernel_us"]["gateup"]
+    dn_bytes = distinct * dn_w + R * k * I * 4 + R * k * H * 4
+    dn_us = t["kernel_us"]["down"]
+    # VALU lane-ops: one fma per weight per computed row (padding included), one
+    # decode per two weights per pass, one scaled fma per group per row
+    gu_rows = sum(st["gu_rows"]) / L
+    dn_rows = sum(st["dn_rows"]) / L
+    ops = gu_rows * 2 * I * H * (1 + 1 / 32) + dn_rows * H * I * (1 + 1 / 32)
+    ops += (distinct * (2 * I * H + H * I)) / 2     # at least one decode pass per expert
+    valu_us = ops / (CUS * LANES * CLOCK_GHZ * 1e9) * 1e6
+    return dict(
+        workload=cfg.name, rows=R, layers=L,
+        round_ms=round(t["ms_per_round"], 4), layer_us=round(layer_us, 3),
+        rows_per_s=round(R / (t["ms_per_round"] / 1e3), 2),
+        row_layers_per_s=round(R * L / (t["ms_per_round"] / 1e3), 1),
+        distinct_experts=round(distinct, 2), unique_weight_bytes=int(unique_bytes),
+        weight_gbps=round(gbps, 1), pct_hbm_peak=round(100 * gbps / HBM_PEAK_GBPS, 2),
+        pct_copy_bw=round(100 * gbps / copy_gbps, 2),
+        kernel_us={kk: round(v, 3) for kk, v in t["kernel_us"].items()},
+        gateup_gbps=round(gu_bytes / (gu_us * 1e-6) / 1e9, 1), gateup_bytes=int(gu_bytes),
+        down_gbps=round(dn_bytes / (dn_us * 1e-6) / 1e9, 1), down_bytes=int(dn_bytes),
+        valu_bound_us=round(valu_us, 2),
+    )
+
+
+# ------------------------------------------------------------ CPU baseline
+def cpu_baseline(budget_s: float) -> dict:
+    """The float64 oracle, untuned, on this host's cores: one-row layers of the
+    release-width synthetic model until about budget_s of CPU time is spent."""
+    import numpy as np
+    import oracle
+    import synth
+    cfg = synth.CONFIGS["one_row"]
+    times, threads = [], 1
+    cpu0 = time.process_time()
+    l = 0
+    while True:
+        x, lg = synth.layer_inputs(cfg, l, plant=False)
+        ids, _ = oracle.route(lg, cfg.k)
+        ex = {int(e): synth.layer_expert(cfg, l, int(e)) for e in np.unique(ids)}
+        c0 = time.process_time()
+        t0 = time.perf_counter()
+        res = oracle.layer(x, lg, ex, cfg.H, cfg.I, cfg.E, cfg.k)
+        times.append(time.perf_counter() - t0)
+        threads = min(res["threads"], cfg.R * cfg.k)
+        l += 1
+        if time.process_time() - cpu0 >= budget_s or l >= 8 or (time.process_time() - c0) * (l + 1) > 4 * budget_s:
+            break
+    per_layer = sum(times) / len(times)
+    return dict(value=round(cfg.R / (per_layer * 40), 4), unit="rows/s", cores=int(threads), kind="oracle",
+                sample="%d of the 40 layers of the one-row round (1 row x 8 experts each), float64 C oracle, "
+                       "OpenMP over (row, slot) pairs; %.3f s per layer, scaled to a 40-layer round" %
+                       (len(times), per_layer))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    from fp4_routed_expert_xp_amd import xp
+    xp.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cells = [c for c in args.cells.split(",") if c]
+    base = synth.CONFIGS["one_row"]
+    t0 = time.perf_counter()
+    log("materialising %d layers x %d experts (%.1f GB)" % (args.layers, base.E,
+                                                             args.layers * base.E * base.expert_bytes / 1e9))
+    model = Model(base, args.layers)
+    log("weights ready in %.1f s" % (time.perf_counter() - t0))
+    copy_gbps = copy_bandwidth_gbps()
+    log("plain copy bandwidth %.0f GB/s" % copy_gbps)
+    reports, timings = {}, {}
+    for name in cells:
+        cfg = synth.CONFIGS[name]
+        cell = Cell(model, cfg, args.layers)
+        t = time_cell(cell, args.steps, args.warmup)
+        timings[name] = t
+        reports[name] = cell_report(cell, t, copy_gbps)
+        log("%s: %s" % (name, json.dumps(reports[name])))
+    head = reports[cells[0]]
+    th = timings[cells[0]]
+    gu_us = head["kernel_us"]["gateup"]
+    achieved = head["gateup_bytes"] / (gu_us * 1e-6) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": head["rows_per_s"],
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["round_ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded fp4 e2m1 codes, E4M3 2^U{-6..0} scales, bf16 N(0,1) x, N(0,1) logits)",
+        "config": {"workload": "%s: %d-row decode through a %d-layer round of independent layers, hidden %d, "
+                               "intermediate %d, %d experts, top-%d" % (cells[0], head["rows"], args.layers,
+                                                                         base.H, base.I, base.E, base.k),
+                   "rows": head["rows"], "layers": args.layers, "hidden": base.H, "inter": base.I,
+                   "experts": base.E, "top_k": base.k},
+        "roofline": {"kernel": "gateup_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None},
+        "copy_gbps": round(copy_gbps, 1),
+        "wall_s_timed": round(th["wall_s"], 4),
+        "cells": reports,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle baseline")
+        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

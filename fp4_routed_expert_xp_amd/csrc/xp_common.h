@@ -1,0 +1,91 @@
+// xp_common.h — internal helpers shared by the libxp HIP sources (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "xp.h"
+
+#define XP_API extern "C" __attribute__((visibility("default")))
+
+namespace xp {
+
+constexpr int kTile = 64;        // output columns per tile (one wave's lanes)
+constexpr int kLeaves = 8;       // partial sums per output: the eight-leaf tree
+constexpr int kMaxPass = 8;      // largest pass size the kernels are built for
+constexpr int kMaxTopK = 16;
+constexpr int kMaxExperts = 1024;
+constexpr int kSmallRows = 64;   // route plans up to this many rows in one workgroup
+constexpr int kMaxItemsGrid = 8192;
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Pass sizes, passed by value to the route kernels.
+struct Tiers {
+    int32_t gu[8];
+    int32_t n_gu;
+    int32_t dn[8];
+    int32_t n_dn;
+};
+
+// Workspace byte offsets for a plan of up to max_rows rows.
+struct WsLayout {
+    size_t hdr, count, offset, entry, gu_pass, dn_pass, masks, base, total;
+};
+
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+inline bool dims_ok(const xp_dims* d) {
+    return d && d->hidden > 0 && d->inter > 0 && d->hidden % 64 == 0 && d->inter % 64 == 0 &&
+           d->n_experts >= 1 && d->n_experts <= kMaxExperts;
+}
+
+inline int check_dims(const xp_dims* d) {
+    if (!d) return XP_ERR_NULL;
+    if (d->top_k < 1 || d->top_k > kMaxTopK || (d->n_experts >= 1 && d->top_k > d->n_experts))
+        return XP_ERR_TOPK;
+    if (!dims_ok(d)) return XP_ERR_SHAPE;
+    return XP_OK;
+}
+
+inline WsLayout ws_layout(const xp_dims* d, int32_t max_rows) {
+    WsLayout L{};
+    size_t R = max_rows > 0 ? (size_t)max_rows : 1;
+    size_t E = (size_t)d->n_experts;
+    size_t entries = R * (size_t)d->top_k;
+    size_t nblk = (R + kSmallRows - 1) / kSmallRows;
+    size_t o = 0;
+    L.hdr = o;     o = align256(o + 64 * sizeof(int32_t));
+    L.count = o;   o = align256(o + E * sizeof(int32_t));
+    L.offset = o;  o = align256(o + (E + 1) * sizeof(int32_t));
+    L.entry = o;   o = align256(o + entries * sizeof(int32_t));
+    L.gu_pass = o; o = align256(o + entries * 4 * sizeof(int32_t));
+    L.dn_pass = o; o = align256(o + entries * 4 * sizeof(int32_t));
+    L.masks = o;   o = align256(o + nblk * E * sizeof(uint64_t));
+    L.base = o;    o = align256(o + nblk * E * sizeof(int32_t));
+    L.total = o;
+    return L;
+}
+
+inline int launch_status() {
+    return hipGetLastError() == hipSuccess ? XP_OK : XP_ERR_HIP;
+}
+
+// Device view of one plan inside a workspace.
+struct Plan {
+    const int32_t* hdr;
+    const int32_t* entry;
+    const int4* gu_pass;
+    const int4* dn_pass;
+};
+
+inline Plan plan_view(const void* ws, const xp_dims* d, int32_t rows) {
+    WsLayout L = ws_layout(d, rows);
+    const char* b = (const char*)ws;
+    return Plan{(const int32_t*)(b + L.hdr), (const int32_t*)(b + L.entry),
+                (const int4*)(b + L.gu_pass), (const int4*)(b + L.dn_pass)};
+}
+
+}  // namespace xp

@@ -1,0 +1,172 @@
+/* xp.h — C ABI of libxp.so: the routed-expert decode path of a top-k
+ * mixture-of-experts layer over fp4 (e2m1) weights with one E4M3 scale per 32
+ * weights, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation follows the pull-request page "dsv41 metal: decode experts
+ * decode an expert's weights once for all of its rows" (TensorFold #2983),
+ * cited below as [#2983, <section>]. In short: the rows routed to an expert
+ * are grouped into passes whose size follows the rows left (gate/up passes of
+ * 2, 4, 6 or 8 rows, down passes of 2 or 4; an expert with one row runs a
+ * one-row pass); each pass decodes every 32-weight group of the expert once
+ * and applies it to all of the pass's rows; and every row keeps the one-row
+ * arithmetic, so a row's output bits do not depend on which other rows share
+ * the launch or where they route. [#2983, "What this changes"]
+ *
+ * Per-row arithmetic (fixed; every pass size runs exactly this per row):
+ *   for each group g of 32 consecutive k:
+ *       p = +0; for t in 0..31: p = fma(w[32g+t], x[32g+t], p)      (fp32)
+ *       part[g mod 8] = fma(p, scale[g], part[g mod 8])             (parts start at +0)
+ *   y = ((part0+part1)+(part2+part3))+((part4+part5)+(part6+part7))
+ * gate/up epilogue: act = g / (1 + exp(-g)) * u        (fp32, stored as fp32)
+ * combine:          y[r] = fma chain from +0 over slots j = 0..k-1 of w[r][j] * out[r][j]
+ *
+ * Conventions for every call:
+ *  - Pointers are DEVICE pointers unless marked "host". The caller owns and
+ *    allocates every buffer; the library allocates nothing on these calls.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Calls enqueue work
+ *    and return without synchronising. Host-visible arguments are validated
+ *    synchronously and reported by the return value (an xp_status); device
+ *    faults surface at the caller's next synchronisation. XP_ERR_HIP means a
+ *    launch was refused by the HIP runtime.
+ *  - rows == 0 is valid and enqueues nothing.
+ *  - Shapes: hidden and inter are positive multiples of 64; 1 <= top_k <= 16;
+ *    top_k <= n_experts <= 1024.
+ *  - A workspace holds one routing plan. It is written by xp_route_bucket and
+ *    read by the xp_gateup_rows / xp_down_rows calls that follow on the same
+ *    stream; use one workspace per plan in flight.
+ */
+#ifndef XP_H
+#define XP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    XP_OK = 0,
+    XP_ERR_NULL = -1,      /* a required pointer is NULL */
+    XP_ERR_SHAPE = -2,     /* a dimension or row count is out of range */
+    XP_ERR_TOPK = -3,      /* top_k out of range */
+    XP_ERR_WORKSPACE = -4, /* workspace too small for this many rows */
+    XP_ERR_TIERS = -5,     /* malformed pass-size list */
+    XP_ERR_HIP = -6        /* the HIP runtime refused a launch */
+} xp_status;
+
+/* Layer widths (host struct). */
+typedef struct {
+    int32_t hidden;    /* H: width of x, y and out */
+    int32_t inter;     /* I: expert intermediate width (act) */
+    int32_t n_experts; /* E */
+    int32_t top_k;     /* k */
+} xp_dims;
+
+/* One expert's weights in the PACKED layout (see xp_pack_matrix). gate and up
+ * are N = inter columns over K = hidden; down is N = hidden over K = inter.
+ * An array of n_experts of these lives in device memory; entries of experts
+ * that no row selects are never read and may hold NULL. */
+typedef struct {
+    const uint8_t* gate_codes;
+    const uint8_t* gate_scales;
+    const uint8_t* up_codes;
+    const uint8_t* up_scales;
+    const uint8_t* down_codes;
+    const uint8_t* down_scales;
+} xp_expert;
+
+/* ---------------------------------------------------------------- weights
+ * Weight format [#2983, "What this changes"]: MXFP4-style e2m1 codes, one
+ * E4M3FN scale byte per 32 consecutive weights along K.
+ *
+ * Plain layout (input of xp_pack_matrix): codes [N][K/2] bytes, byte b of
+ * column n holds k = 2b in its low nibble and k = 2b+1 in its high nibble;
+ * scales [N][K/32] bytes.
+ *
+ * Packed layout (what the kernels read): columns are taken in tiles of 64;
+ * with G = K/32,
+ *   codes:  16-byte chunk (n, g) at byte offset ((n/64)*G + g)*1024 + (n%64)*16,
+ *           holding the plain bytes 16g .. 16g+15 of column n;
+ *   scales: byte (n, g) at ((n/64)*G + g)*64 + n%64.
+ * Sizes are those of the plain layout (N*K/2 and N*K/32 bytes). One wave of
+ * 64 lanes then reads one group of 64 columns as 1 KiB of contiguous codes
+ * and 64 contiguous scale bytes.
+ *
+ * N must be a positive multiple of 64 and K a positive multiple of 32.
+ * In and out buffers must not overlap. */
+int xp_pack_matrix(int32_t n, int32_t k, const uint8_t* codes, const uint8_t* scales,
+                   uint8_t* packed_codes, uint8_t* packed_scales, void* stream);
+
+/* --------------------------------------------------------------- workspace */
+
+/* Bytes of workspace needed to plan up to max_rows rows (host, pure; 0 on bad dims). */
+size_t xp_workspace_bytes(const xp_dims* dims, int32_t max_rows);
+
+/* Byte offsets of the plan's fields inside a workspace sized for max_rows
+ * (host, pure), for callers that read the plan back:
+ *   off[0] header: int32 [0] = gate/up passes, [1] = down passes
+ *   off[1] count  int32 [E]          rows per expert
+ *   off[2] offset int32 [E+1]        first entry of each expert
+ *   off[3] entry  int32 [R*k]        row*k + slot, experts ascending, rows ascending
+ *   off[4] gate/up passes int32 [R*k][4] = (expert, first entry, real rows, pass size)
+ *   off[5] down passes    int32 [R*k][4]
+ * Returns XP_OK or an error for bad dims. */
+int xp_workspace_layout(const xp_dims* dims, int32_t max_rows, size_t off[6]);
+
+/* ----------------------------------------------------------- the four calls */
+
+/* Route and bucket rows. For each row: the top_k experts by logit (larger
+ * first, equal logits by lower id, NaN after every number) into topk_id
+ * [rows][k] int32, and their softmax over the chosen logits, in fp32, into
+ * topk_w [rows][k]. Then the plan: a stable bucketing of the rows*k entries by
+ * expert and the gate/up and down pass lists under the current pass sizes
+ * (xp_set_tiers). logits: [rows][E] fp32.
+ * [#2983, "What this changes"; the routing rule itself is not on the page] */
+int xp_route_bucket(const xp_dims* dims, int32_t rows, const float* logits, int32_t* topk_id,
+                    float* topk_w, void* workspace, size_t ws_bytes, void* stream);
+
+/* Gate/up with the SwiGLU epilogue for every (row, slot) of the plan:
+ * act[row][slot][I] fp32 = silu(W_gate x_row) * (W_up x_row). x: [rows][H]
+ * bf16 bit patterns. Each pass decodes its expert's groups once for all of
+ * its rows; padding rows of a pass repeat its last real row and are never
+ * written. [#2983, "What this changes" and the rows commit] */
+int xp_gateup_rows(const xp_dims* dims, int32_t rows, const uint16_t* x, const xp_expert* experts,
+                   const void* workspace, size_t ws_bytes, float* act, void* stream);
+
+/* Diagnostic twin of xp_gateup_rows: the same passes and per-row chains, but
+ * writes the two projections before the epilogue, g and u [rows][k][I] fp32. */
+int xp_gateup_rows_split(const xp_dims* dims, int32_t rows, const uint16_t* x,
+                         const xp_expert* experts, const void* workspace, size_t ws_bytes,
+                         float* g, float* u, void* stream);
+
+/* Down projection for every (row, slot): out[row][slot][H] fp32 = W_down act[row][slot].
+ * act: [rows][k][I] fp32 (normally xp_gateup_rows' output). Passes of the
+ * down sizes; out is not weighted by the router. [#2983, "What this changes"] */
+int xp_down_rows(const xp_dims* dims, int32_t rows, const float* act, const xp_expert* experts,
+                 const void* workspace, size_t ws_bytes, float* out, void* stream);
+
+/* Combine: y[row][H] fp32 = fma chain from +0 over slots in order of
+ * topk_w[row][j] * out[row][j]. [#2983, "Receipt": the combine output] */
+int xp_combine(const xp_dims* dims, int32_t rows, const float* out, const float* topk_w, float* y,
+               void* stream);
+
+/* ------------------------------------------------------------ pass sizes */
+
+/* Set the pass sizes used by later xp_route_bucket calls (host, process-wide,
+ * not thread-safe against concurrent route calls). gu: 1..7 strictly
+ * increasing sizes in 2..8 for gate/up; dn: the same for down. NULL or a
+ * count of 0 restores that list's default ({2,4,6,8} and {2,4}). */
+int xp_set_tiers(const int32_t* gu, int32_t n_gu, const int32_t* dn, int32_t n_dn);
+
+/* Current pass sizes (host). gu and dn need room for 8 entries. */
+int xp_get_tiers(int32_t* gu, int32_t* n_gu, int32_t* dn, int32_t* n_dn);
+
+/* Human-readable name of a status code (static string). */
+const char* xp_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* XP_H */

@@ -220,3 +220,98 @@ def layer_inputs(cfg: Config, layer: int = 0, plant: bool | None = None):
 
 def layer_expert(cfg: Config, layer: int, e: int) -> dict:
     return expert(cfg.weight_seed, layer, e, cfg.H, cfg.I, cfg.emin, cfg.emax)
+
+
+# ------------------------------------------------------------ device twin
+_dev_lib = None
+
+
+def _device_lib():
+    """libxpsynth.so: the integer weight-byte streams written straight into GPU memory."""
+    global _dev_lib
+    if _dev_lib is None:
+        import ctypes
+        import os
+        import torch  # noqa: F401  (bind to torch's HIP runtime before loading)
+        path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libxpsynth.so")
+        if not os.path.exists(path):
+            raise RuntimeError("synth/libxpsynth.so is not built; run `python -m fp4_routed_expert_xp_amd.build`")
+        L = ctypes.CDLL(path)
+        u64, i64, P = ctypes.c_uint64, ctypes.c_int64, ctypes.c_void_p
+        L.xps_codes.argtypes = [u64, u64, u64, u64, i64, i64, P, P]
+        L.xps_codes.restype = ctypes.c_int
+        L.xps_scales.argtypes = [u64, u64, u64, u64, i64, i64, ctypes.c_int, ctypes.c_int, P, P]
+        L.xps_scales.restype = ctypes.c_int
+        L.xps_stream_key.argtypes = [u64, u64, u64, u64]
+        L.xps_stream_key.restype = u64
+        L.xps_codes_batch.argtypes = [P, ctypes.c_int, i64, i64, P, i64, P]
+        L.xps_codes_batch.restype = ctypes.c_int
+        L.xps_scales_batch.argtypes = [P, ctypes.c_int, i64, i64, ctypes.c_int, ctypes.c_int, P, i64, P]
+        L.xps_scales_batch.restype = ctypes.c_int
+        _dev_lib = L
+    return _dev_lib
+
+
+def device_codes(seed, layer, expert, tensor, N, K, out, stream=0):
+    """Fill the uint8 device tensor ``out`` ([N][K/2]) with the same bytes as :func:`codes`."""
+    assert out.dtype.itemsize == 1 and out.numel() >= N * K // 2 and out.is_contiguous()
+    rc = _device_lib().xps_codes(seed, layer, expert, tensor, N, K, out.data_ptr(), stream)
+    if rc != 0:
+        raise RuntimeError("xps_codes failed: %d" % rc)
+
+
+def device_scales(seed, layer, expert, tensor, N, K, emin, emax, out, stream=0):
+    """Fill the uint8 device tensor ``out`` ([N][K/32]) with the same bytes as :func:`scales`."""
+    assert out.dtype.itemsize == 1 and out.numel() >= N * (K // 32) and out.is_contiguous()
+    rc = _device_lib().xps_scales(seed, layer, expert, tensor, N, K, emin, emax, out.data_ptr(), stream)
+    if rc != 0:
+        raise RuntimeError("xps_scales failed: %d" % rc)
+
+
+def device_expert(seed, layer, e, H, I, emin, emax, device="cuda", stream=0) -> dict:
+    """The six plain-layout arrays of one expert, generated on the GPU."""
+    import torch
+    shapes = {"gate": (I, H), "up": (I, H), "down": (H, I)}
+    out = {}
+    for m, (tc, ts) in MATRICES.items():
+        N, K = shapes[m]
+        c = torch.empty((N, K // 2), dtype=torch.uint8, device=device)
+        s = torch.empty((N, K // 32), dtype=torch.uint8, device=device)
+        device_codes(seed, layer, e, tc, N, K, c, stream)
+        device_scales(seed, layer, e, ts, N, K, emin, emax, s, stream)
+        out[m + "_codes"], out[m + "_scales"] = c, s
+    return out
+
+
+def device_layer_plain(seed, layer, H, I, E, emin, emax, out, stream=0) -> dict:
+    """All E experts of one layer in the plain layout, written into the uint8 device
+    tensor ``out`` (E * expert_bytes). Expert e's arrays sit at e * expert_bytes plus
+    the offsets returned here: {name: (offset, nbytes)} in the order gate_codes,
+    gate_scales, up_codes, up_scales, down_codes, down_scales."""
+    import torch
+    L = _device_lib()
+    shapes = {"gate": (I, H), "up": (I, H), "down": (H, I)}
+    offs = {}
+    o = 0
+    for m in ("gate", "up", "down"):
+        N, K = shapes[m]
+        offs[m + "_codes"] = (o, N * K // 2)
+        o += N * K // 2
+        offs[m + "_scales"] = (o, N * K // 32)
+        o += N * K // 32
+    stride = o
+    assert out.numel() >= E * stride and out.dtype == torch.uint8
+    base = out.data_ptr()
+    for m, (tc, ts) in MATRICES.items():
+        N, K = shapes[m]
+        for t, name in ((tc, m + "_codes"), (ts, m + "_scales")):
+            keys = torch.from_numpy(np.array([stream_key(seed, layer, t, e) for e in range(E)], dtype=np.uint64))
+            keys_dev = keys.to(out.device)
+            if name.endswith("codes"):
+                rc = L.xps_codes_batch(keys_dev.data_ptr(), E, N, K, base + offs[name][0], stride, stream)
+            else:
+                rc = L.xps_scales_batch(keys_dev.data_ptr(), E, N, K, emin, emax, base + offs[name][0], stride,
+                                        stream)
+            if rc != 0:
+                raise RuntimeError("device generator failed: %d" % rc)
+    return dict(stride=stride, offsets=offs)

@@ -1,0 +1,110 @@
+"""The C ABI on the host: the library loads, exports what include/xp.h declares, and
+validates arguments synchronously. No kernel is launched here (no GPU needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from fp4_routed_expert_xp_amd import xp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "xp.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(xp_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared() == sorted(xp.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = xp.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", xp.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (xp_\w+)", out))
+    assert exported == set(_declared())
+
+
+def test_library_links_no_oracle_or_torch():
+    out = subprocess.run(["readelf", "-d", xp.LIB_PATH], capture_output=True, text=True).stdout
+    needed = re.findall(r"NEEDED.*\[(.*)\]", out)
+    assert not any("oracle" in n or "torch" in n or "c10" in n for n in needed), needed
+
+
+def test_status_strings():
+    for s in range(-6, 1):
+        assert xp.xp_status_string(s).startswith("XP_")
+    assert "unknown" in xp.xp_status_string(99)
+
+
+def test_workspace_layout_is_ordered_and_fits():
+    d = xp.dims(4096, 2048, 256, 8)
+    for rows in (1, 4, 16, 64, 65, 4096):
+        off = xp.xp_workspace_layout(d, rows)
+        assert off == sorted(off) and all(o % 256 == 0 for o in off)
+        total = xp.xp_workspace_bytes(d, rows)
+        assert total >= off[-1] + rows * 8 * 16
+    assert xp.xp_workspace_bytes(xp.dims(100, 2048, 256, 8), 4) == 0   # hidden not a multiple of 64
+
+
+@pytest.mark.parametrize("dims,status", [
+    ((4096, 2048, 256, 0), xp.XP_ERR_TOPK),
+    ((4096, 2048, 256, 17), xp.XP_ERR_TOPK),
+    ((4096, 2048, 4, 8), xp.XP_ERR_TOPK),
+    ((4000, 2048, 256, 8), xp.XP_ERR_SHAPE),
+    ((4096, 2000, 256, 8), xp.XP_ERR_SHAPE),
+    ((4096, 2048, 2048, 8), xp.XP_ERR_SHAPE),
+])
+def test_bad_dims_rejected_before_any_launch(dims, status):
+    L = xp.lib()
+    d = xp.dims(*dims)
+    P = ctypes.c_void_p(0x1000)
+    assert L.xp_route_bucket(ctypes.byref(d), 4, P, P, P, P, 1 << 30, None) == status
+    assert L.xp_gateup_rows(ctypes.byref(d), 4, P, P, P, 1 << 30, P, None) == status
+    assert L.xp_down_rows(ctypes.byref(d), 4, P, P, P, 1 << 30, P, None) == status
+    assert L.xp_combine(ctypes.byref(d), 4, P, P, P, None) == status
+
+
+def test_null_rows_and_workspace_checks():
+    L = xp.lib()
+    d = xp.dims(256, 128, 8, 2)
+    P = ctypes.c_void_p(0x1000)
+    assert L.xp_route_bucket(None, 4, P, P, P, P, 1 << 20, None) == xp.XP_ERR_NULL
+    assert L.xp_route_bucket(ctypes.byref(d), -1, P, P, P, P, 1 << 20, None) == xp.XP_ERR_SHAPE
+    assert L.xp_route_bucket(ctypes.byref(d), 0, None, None, None, None, 0, None) == xp.XP_OK  # empty batch
+    assert L.xp_gateup_rows(ctypes.byref(d), 0, None, None, None, 0, None, None) == xp.XP_OK
+    assert L.xp_down_rows(ctypes.byref(d), 0, None, None, None, 0, None, None) == xp.XP_OK
+    assert L.xp_combine(ctypes.byref(d), 0, None, None, None, None) == xp.XP_OK
+    assert L.xp_route_bucket(ctypes.byref(d), 4, None, P, P, P, 1 << 20, None) == xp.XP_ERR_NULL
+    need = xp.xp_workspace_bytes(d, 4)
+    assert L.xp_route_bucket(ctypes.byref(d), 4, P, P, P, P, need - 1, None) == xp.XP_ERR_WORKSPACE
+    assert L.xp_gateup_rows(ctypes.byref(d), 4, P, P, P, need - 1, P, None) == xp.XP_ERR_WORKSPACE
+    assert L.xp_down_rows(ctypes.byref(d), 4, P, P, P, need - 1, P, None) == xp.XP_ERR_WORKSPACE
+    assert L.xp_gateup_rows_split(ctypes.byref(d), 4, P, P, P, need, P, None, None) == xp.XP_ERR_NULL
+    assert L.xp_pack_matrix(100, 64, P, P, P, P, None) == xp.XP_ERR_SHAPE
+    assert L.xp_pack_matrix(64, 48, P, P, P, P, None) == xp.XP_ERR_SHAPE
+    assert L.xp_pack_matrix(64, 64, None, P, P, P, None) == xp.XP_ERR_NULL
+
+
+def test_tiers_set_get_and_refusals():
+    assert xp.xp_get_tiers() == ([2, 4, 6, 8], [2, 4])
+    try:
+        xp.xp_set_tiers([4], [4])
+        assert xp.xp_get_tiers() == ([4], [4])
+        xp.xp_set_tiers([2, 4, 8], None)
+        assert xp.xp_get_tiers() == ([2, 4, 8], [2, 4])
+        for bad in ([1, 2], [2, 2], [4, 2], [2, 9], [0], list(range(2, 10))):
+            with pytest.raises(xp.XPError) as ei:
+                xp.xp_set_tiers(bad, [2])
+            assert ei.value.status == xp.XP_ERR_TIERS
+        assert xp.xp_get_tiers() == ([2, 4, 8], [2, 4])    # refused lists change nothing
+    finally:
+        xp.xp_set_tiers(None, None)
+    assert xp.xp_get_tiers() == ([2, 4, 6, 8], [2, 4])

@@ -1,0 +1,90 @@
+"""GPU: generator twin, weight packing, routing and the pass plan (bit-exact against the oracle)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from fp4_routed_expert_xp_amd import xp
+
+from gpu_helpers import log, read_plan, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def test_device_generator_matches_host():
+    for (seed, layer, e, t, N, K) in [(1000, 0, 0, synth.GATE_CODES, 2048, 4096),
+                                       (1000, 39, 255, synth.DOWN_CODES, 4096, 2048),
+                                       (1001, 0, 7, synth.UP_CODES, 128, 256)]:
+        log("synth codes %s" % ((seed, layer, e, t, N, K),))
+        dev = torch.empty((N, K // 2), dtype=torch.uint8, device="cuda")
+        synth.device_codes(seed, layer, e, t, N, K, dev)
+        assert np.array_equal(dev.cpu().numpy(), synth.codes(seed, layer, e, t, N, K))
+        s = torch.empty((N, K // 32), dtype=torch.uint8, device="cuda")
+        synth.device_scales(seed, layer, e, t + 1, N, K, -6, 0, s)
+        assert np.array_equal(s.cpu().numpy(), synth.scales(seed, layer, e, t + 1, N, K, -6, 0))
+
+
+@pytest.mark.parametrize("N,K", [(64, 32), (128, 256), (256, 128), (2048, 4096)])
+def test_pack_layout(N, K):
+    rng = np.random.default_rng(N + K)
+    codes = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    scales = rng.integers(0, 256, size=(N, K // 32), dtype=np.uint8)
+    pc = torch.empty(N * K // 2, dtype=torch.uint8, device="cuda")
+    ps = torch.empty(N * K // 32, dtype=torch.uint8, device="cuda")
+    xp.xp_pack_matrix(to_dev(codes), to_dev(scales), pc, ps)
+    torch.cuda.synchronize()
+    G = K // 32
+    # the documented layout: tiles of 64 columns, group-major inside a tile
+    want_c = codes.reshape(N // 64, 64, G, 16).transpose(0, 2, 1, 3).reshape(-1)
+    want_s = scales.reshape(N // 64, 64, G).transpose(0, 2, 1).reshape(-1)
+    assert np.array_equal(pc.cpu().numpy(), want_c)
+    assert np.array_equal(ps.cpu().numpy(), want_s)
+
+
+def _route_case(R, E, k, lg, tiers=((2, 4, 6, 8), (2, 4))):
+    d = xp.dims(256, 128, E, k)
+    xp.xp_set_tiers(list(tiers[0]), list(tiers[1]))
+    try:
+        ws = torch.zeros(xp.xp_workspace_bytes(d, R), dtype=torch.uint8, device="cuda")
+        ids = torch.full((R, k), -1, dtype=torch.int32, device="cuda")
+        w = torch.zeros((R, k), dtype=torch.float32, device="cuda")
+        xp.xp_route_bucket(d, R, to_dev(lg), ids, w, ws)
+        torch.cuda.synchronize()
+    finally:
+        xp.xp_set_tiers(None, None)
+    ids, w, ws = ids.cpu().numpy(), w.cpu().numpy(), ws.cpu().numpy()
+    plan = read_plan(d, R, ws)
+    oid, ow = oracle.route(lg, k)
+    count, offset, entry = oracle.bucket(oid, E)
+    return ids, w, plan, (oid, ow, count, offset, entry, oracle.plan(count, offset, tiers[0]),
+                          oracle.plan(count, offset, tiers[1]))
+
+
+@pytest.mark.parametrize("R,E,k", [(1, 256, 8), (4, 8, 2), (16, 256, 8), (64, 256, 8), (3, 3, 3),
+                                   (65, 256, 8), (200, 64, 6), (1000, 1024, 16), (4096, 256, 8)])
+def test_route_and_plan_bit_exact(R, E, k):
+    log("route R=%d E=%d k=%d" % (R, E, k))
+    lg = synth.logits(77, R, R, E, bias_sigma=0.5 if R == 4096 else 0.0)
+    if R >= 3 and E >= 10:
+        lg[0, :] = np.nan                 # a row of NaN: ids ascending
+        lg[1, 3] = lg[1, 9] = lg[1, 1] = 9.0   # ties: lower id first
+        lg[2, 5] = np.inf
+    ids, w, plan, (oid, ow, count, offset, entry, gu, dn) = _route_case(R, E, k, lg)
+    assert np.array_equal(ids, oid)
+    fin = np.isfinite(ow)
+    assert np.array_equal(np.isfinite(w), fin)
+    assert np.all(np.abs(w[fin] - ow[fin]) <= 1e-6 * np.abs(ow[fin]) + 1e-30)
+    assert np.array_equal(plan["count"], count)
+    assert np.array_equal(plan["offset"], offset)
+    assert np.array_equal(plan["entry"], entry)
+    assert plan["n_gu"] == len(gu) and np.array_equal(plan["gu"], gu)
+    assert plan["n_dn"] == len(dn) and np.array_equal(plan["dn"], dn)
+
+
+@pytest.mark.parametrize("tiers", [((4,), (4,)), ((8,), (8,)), ((2, 4, 8), (2, 4, 8)), ((3, 5, 7), (2,))])
+def test_plan_other_tier_sets(tiers):
+    lg = synth.logits_same(5, 0, 16, 64)
+    lg[8:] = synth.logits(6, 0, 8, 64)
+    ids, w, plan, (oid, ow, count, offset, entry, gu, dn) = _route_case(16, 64, 8, lg, tiers)
+    assert np.array_equal(plan["gu"], gu) and np.array_equal(plan["dn"], dn)
