@@ -134,9 +134,10 @@ def bucket(topk_id: np.ndarray, E: int):
 
 def passes(n: int, tiers):
     t = _c(list(tiers), np.int32)
-    size = np.zeros(64, dtype=np.int32)
-    real = np.zeros(64, dtype=np.int32)
-    m = lib().or_passes(int(n), _p(t), len(t), _p(size), _p(real), 64)
+    cap = max(int(n), 1)               # at most one pass per row
+    size = np.zeros(cap, dtype=np.int32)
+    real = np.zeros(cap, dtype=np.int32)
+    m = lib().or_passes(int(n), _p(t), len(t), _p(size), _p(real), cap)
     return [(int(size[i]), int(real[i])) for i in range(m)]
 
 

@@ -165,11 +165,15 @@ int or_passes(int n, const int32_t* tiers, int n_tiers, int32_t* size, int32_t* 
 int or_plan(int E, const int32_t* count, const int32_t* offset, const int32_t* tiers, int n_tiers,
             int32_t* plan, int cap) {
     int np = 0;
-    int32_t size[64], real[64];
     for (int e = 0; e < E; ++e) {
+        int n = count[e];
+        if (n <= 0) continue;
+        /* an expert with n rows has at most n passes */
+        int32_t* size = (int32_t*)malloc(sizeof(int32_t) * (size_t)n);
+        int32_t* real = (int32_t*)malloc(sizeof(int32_t) * (size_t)n);
         int first = offset[e];
-        int n = or_passes(count[e], tiers, n_tiers, size, real, 64);
-        for (int i = 0; i < n; ++i) {
+        int m = or_passes(n, tiers, n_tiers, size, real, n);
+        for (int i = 0; i < m; ++i) {
             if (np < cap) {
                 plan[4 * np + 0] = e;
                 plan[4 * np + 1] = first;
@@ -179,6 +183,8 @@ int or_plan(int E, const int32_t* count, const int32_t* offset, const int32_t* t
             ++np;
             first += real[i];
         }
+        free(size);
+        free(real);
     }
     return np;
 }

@@ -144,3 +144,15 @@ def test_plan_layout_matches_passes():
     for e in range(32):
         assert pos.get(e, offset[e]) == offset[e + 1]
     assert list(plan[:, 0]) == sorted(plan[:, 0])
+
+
+def test_plan_for_an_expert_with_many_rows():
+    # 1000 rows on one expert: 125 passes of 8 (gate/up), 250 of 4 (down)
+    count = np.array([1000, 0, 3], dtype=np.int32)
+    offset = np.array([0, 1000, 1000, 1003], dtype=np.int32)
+    gu = oracle.plan(count, offset, [2, 4, 6, 8])
+    assert len(gu) == 126 and np.all(gu[:125, 3] == 8) and np.all(gu[:125, 2] == 8)
+    assert list(gu[125]) == [2, 1000, 3, 4]
+    assert list(gu[:125, 1]) == list(range(0, 1000, 8))
+    dn = oracle.plan(count, offset, [2, 4])
+    assert len(dn) == 251 and list(dn[-1]) == [2, 1000, 3, 4] and np.all(dn[:250, 3] == 4)
