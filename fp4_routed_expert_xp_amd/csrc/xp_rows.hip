@@ -1,27 +1,28 @@
 // xp_rows.hip — the multi-row gate/up and down passes.
 //
-// A work item is (pass, tile of 64 output columns). Its workgroup has eight
-// waves; wave j owns the 32-weight groups g = j, j+8, j+16, ... of the K axis,
-// and lane c owns output column tile*64 + c. For each of its groups a lane
-// loads the column's 16 bytes of codes (one coalesced 1 KiB read per wave in
-// the packed layout) and one scale byte, decodes the 32 weights once, and runs
-// every row of the pass through them: per row a fused multiply-add chain from
-// +0 over the group's 32 products in k order, then the group's scale applied
-// by one fused multiply-add into the row's partial for leaf j. The eight
-// leaves meet in LDS and are added by a fixed tree. Activations are
-// wave-uniform, so they are read with scalar loads into SGPRs.
-// [#2983, "What this changes" and the rows commit: a pass decodes each
-// 32-group once for all of its rows; each row's chain is the one-row chain]
+// A work item is (pass, tile of 64 output columns). Lane c of a wave owns column
+// tile*64 + c; each wave owns one leaf j of the eight-leaf tree, i.e. the
+// 32-weight groups g = j, j+8, j+16, ... of the K axis, which it walks in
+// ascending order. Gate/up items run 16 waves (waves 0-7: the gate leaves, 8-15:
+// the up leaves); down items run 8 waves. For each of its groups a lane loads
+// 16 bytes of codes (one coalesced 1 KiB read per wave in the packed layout) and
+// one scale byte, decodes the 32 weights once (v_cvt_scalef32_pk_f32_fp4 with
+// scale 1, exact) and runs every row of the pass through them: per row a fused
+// multiply-add chain from +0 over the 32 products in k order (Chain<P>), then
+// the group's scale applied by one fused multiply-add into the row's leaf. The
+// leaves meet in LDS and one thread per (row, column) adds them by the fixed
+// tree ((l0+l1)+(l2+l3))+((l4+l5)+(l6+l7)) and applies the epilogue.
+// [#2983, "What this changes" and the rows commit: a pass decodes each 32-group
+// once for all of its rows; each row's chain, scaled fma, tree and epilogue are
+// the one-row kernel's]
 //
-// The code for a pass of P rows is the code for one row repeated P times, with
-// no value crossing between rows: a row's bits are the same at every P.
-// Padding rows (P > real rows) re-read the last real row and are not stored.
+// The code for a pass of P rows is the one-row code repeated per row with no
+// value crossing between rows, so a row's bits do not depend on P. Padding rows
+// (P > real rows) re-read the last real row and are not stored.
+#include "xp_chain_asm.h"
 #include "xp_common.h"
 
 namespace xp {
-
-__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 
 // Two fp4 codes of byte `B` of `v` -> exact fp32 (low nibble first).
 template <int B>
@@ -31,6 +32,18 @@ __device__ __forceinline__ f32x2 fp4x2(uint32_t v) {
 
 __device__ __forceinline__ float e4m3(uint32_t byte) { return __builtin_amdgcn_cvt_f32_fp8((int)byte, 0); }
 
+__device__ __forceinline__ void decode32(u32x4 c, float (&w)[32]) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        f32x2 a;
+        a = fp4x2<0>(c[d]); w[8 * d + 0] = a.x; w[8 * d + 1] = a.y;
+        a = fp4x2<1>(c[d]); w[8 * d + 2] = a.x; w[8 * d + 3] = a.y;
+        a = fp4x2<2>(c[d]); w[8 * d + 4] = a.x; w[8 * d + 5] = a.y;
+        a = fp4x2<3>(c[d]); w[8 * d + 6] = a.x; w[8 * d + 7] = a.y;
+    }
+}
+
+// Leaves l0..l7 at a[0], a[stride], ..., a[7*stride].
 __device__ __forceinline__ float tree8(const float* a, int stride) {
     float s01 = a[0] + a[stride];
     float s23 = a[2 * stride] + a[3 * stride];
@@ -47,48 +60,67 @@ typedef const uint8_t __attribute__((address_space(1)))* gbytes_t;
 // Weight codes are read once: non-temporal loads keep them out of the caches' way.
 __device__ __forceinline__ u32x4 load_codes(gcodes_t p) { return __builtin_nontemporal_load(p); }
 
+// Groups kept in flight per wave: deep for small passes, shallower as rows add
+// registers (gate/up keeps within 128 VGPRs for 16-wave workgroups; down within
+// 128 so that two 8-wave workgroups share a CU).
+template <int P>
+struct GuDepth {
+    static constexpr int value = P <= 2 ? 8 : (P <= 4 ? 4 : 2);
+};
+template <int P>
+struct DnDepth {
+    static constexpr int value = P == 1 ? 8 : (P <= 4 ? 4 : 1);
+};
+
 // ------------------------------------------------------------------ gate/up
 
-// One group for P rows. The group's 32 gate and 32 up weights are decoded
-// once into registers; then each row runs its two 32-product chains from +0
-// in k order and folds them into its leaf with the group's scales.
+// One leaf of one matrix (gate or up) for one (pass, tile): returns the P leaf
+// values of this lane's column.
 template <int P>
-__device__ __forceinline__ void gu_group(u32x4 cg, u32x4 cu, uint32_t sg, uint32_t su,
-                                         const uint32_t* const (&xr)[P], int g, float (&ag)[P],
-                                         float (&au)[P]) {
-    float wg[32], wu[32];
+__device__ __forceinline__ void gu_leaf(gcodes_t cc, gbytes_t ss, const uint32_t* const (&xr)[P], int leaf, int ng,
+                                        int lane, float (&acc)[P]) {
+    constexpr int D = GuDepth<P>::value;
+    const int xl = lane & 15;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        f32x2 a;
-        a = fp4x2<0>(cg[d]); wg[8 * d + 0] = a.x; wg[8 * d + 1] = a.y;
-        a = fp4x2<1>(cg[d]); wg[8 * d + 2] = a.x; wg[8 * d + 3] = a.y;
-        a = fp4x2<2>(cg[d]); wg[8 * d + 4] = a.x; wg[8 * d + 5] = a.y;
-        a = fp4x2<3>(cg[d]); wg[8 * d + 6] = a.x; wg[8 * d + 7] = a.y;
-        a = fp4x2<0>(cu[d]); wu[8 * d + 0] = a.x; wu[8 * d + 1] = a.y;
-        a = fp4x2<1>(cu[d]); wu[8 * d + 2] = a.x; wu[8 * d + 3] = a.y;
-        a = fp4x2<2>(cu[d]); wu[8 * d + 4] = a.x; wu[8 * d + 5] = a.y;
-        a = fp4x2<3>(cu[d]); wu[8 * d + 6] = a.x; wu[8 * d + 7] = a.y;
-    }
-    const float s_g = e4m3(sg), s_u = e4m3(su);
+    for (int r = 0; r < P; ++r) acc[r] = 0.0f;
+    u32x4 bc[D];
+    uint32_t bs[D];
+    uint32_t bx[D][P];
 #pragma unroll
-    for (int r = 0; r < P; ++r) {
-        // keep one row's activations live at a time (16 SGPRs of bf16 pairs)
-        __builtin_amdgcn_sched_barrier(0);
-        const uint32_t* xp = xr[r] + 16 * g;
-        float pg = 0.0f, pu = 0.0f;
+    for (int s = 0; s < D; ++s) {
+        if (s < ng) {
+            const int g = leaf + 8 * s;
+            bc[s] = load_codes(cc + (size_t)g * kTile);
+            bs[s] = ss[(size_t)g * kTile];
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const uint32_t v = xp[q];
-            const float x0 = bf16_lo(v), x1 = bf16_hi(v);
-            pg = __builtin_fmaf(wg[2 * q], x0, pg);
-            pu = __builtin_fmaf(wu[2 * q], x0, pu);
-            pg = __builtin_fmaf(wg[2 * q + 1], x1, pg);
-            pu = __builtin_fmaf(wu[2 * q + 1], x1, pu);
+            for (int r = 0; r < P; ++r) bx[s][r] = xr[r][16 * g + xl];
         }
-        ag[r] = __builtin_fmaf(pg, s_g, ag[r]);
-        au[r] = __builtin_fmaf(pu, s_u, au[r]);
     }
-    __builtin_amdgcn_sched_barrier(0);
+    for (int i0 = 0; i0 < ng; i0 += D) {
+#pragma unroll
+        for (int s = 0; s < D; ++s) {
+            const int i = i0 + s;
+            if (i < ng) {
+                float w[32];
+                decode32(bc[s], w);
+                const float sc = e4m3(bs[s]);
+                uint32_t xc[P];
+#pragma unroll
+                for (int r = 0; r < P; ++r) xc[r] = bx[s][r];
+                if (i + D < ng) {
+                    const int g = leaf + 8 * (i + D);
+                    bc[s] = load_codes(cc + (size_t)g * kTile);
+                    bs[s] = ss[(size_t)g * kTile];
+#pragma unroll
+                    for (int r = 0; r < P; ++r) bx[s][r] = xr[r][16 * g + xl];
+                }
+                float p[P];
+                Chain<P>::bf16(w, xc, p);
+#pragma unroll
+                for (int r = 0; r < P; ++r) acc[r] = __builtin_fmaf(p[r], sc, acc[r]);
+            }
+        }
+    }
 }
 
 template <int P, bool SPLIT>
@@ -97,16 +129,15 @@ __device__ void gu_item(const xp_expert* __restrict__ experts, const uint16_t* _
                         float* __restrict__ out0, float* __restrict__ out1, float* red) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
+    const int leaf = wave & 7, up = wave >> 3;
     const int e = ps.x, first = ps.y, real = ps.z;
     const int G = H >> 5;
-    const int ng = (G > wave) ? (G - wave + 7) >> 3 : 0;
+    const int ng = (G > leaf) ? (G - leaf + 7) >> 3 : 0;
 
     const xp_expert ex = experts[e];
     const size_t tile_chunks = (size_t)tile * G * kTile;
-    const gcodes_t gc = (gcodes_t)ex.gate_codes + tile_chunks + lane;
-    const gcodes_t uc = (gcodes_t)ex.up_codes + tile_chunks + lane;
-    const gbytes_t gs = (gbytes_t)ex.gate_scales + tile_chunks + lane;
-    const gbytes_t us = (gbytes_t)ex.up_scales + tile_chunks + lane;
+    const gcodes_t cc = (gcodes_t)(up ? ex.up_codes : ex.gate_codes) + tile_chunks + lane;
+    const gbytes_t ss = (gbytes_t)(up ? ex.up_scales : ex.gate_scales) + tile_chunks + lane;
 
     const uint32_t* xr[P];
 #pragma unroll
@@ -114,55 +145,20 @@ __device__ void gu_item(const xp_expert* __restrict__ experts, const uint16_t* _
         const int ent = entry[first + (r < real ? r : real - 1)];
         xr[r] = (const uint32_t*)(x + (size_t)(ent / k) * H);
     }
+    float acc[P];
+    gu_leaf<P>(cc, ss, xr, leaf, ng, lane, acc);
 
-    float ag[P], au[P];
+    // leaves -> LDS: red[wave][row][lane], gate leaves in waves 0-7, up in 8-15
 #pragma unroll
-    for (int r = 0; r < P; ++r) { ag[r] = 0.0f; au[r] = 0.0f; }
-
-    constexpr int D = 4;  // groups in flight per wave
-    u32x4 bg[D], bu[D];
-    uint32_t bsg[D], bsu[D];
-#pragma unroll
-    for (int s = 0; s < D; ++s) {
-        if (s < ng) {
-            const size_t o = (size_t)(wave + 8 * s) * kTile;
-            bg[s] = load_codes(gc + o);
-            bu[s] = load_codes(uc + o);
-            bsg[s] = gs[o];
-            bsu[s] = us[o];
-        }
-    }
-    for (int i0 = 0; i0 < ng; i0 += D) {
-#pragma unroll
-        for (int s = 0; s < D; ++s) {
-            const int i = i0 + s;
-            if (i < ng) {
-                gu_group<P>(bg[s], bu[s], bsg[s], bsu[s], xr, wave + 8 * i, ag, au);
-                if (i + D < ng) {
-                    const size_t o = (size_t)(wave + 8 * (i + D)) * kTile;
-                    bg[s] = load_codes(gc + o);
-                    bu[s] = load_codes(uc + o);
-                    bsg[s] = gs[o];
-                    bsu[s] = us[o];
-                }
-            }
-        }
-    }
-
-    // leaves -> LDS: red[wave][row][gate|up][lane]
-#pragma unroll
-    for (int r = 0; r < P; ++r) {
-        red[((wave * P + r) * 2 + 0) * kTile + lane] = ag[r];
-        red[((wave * P + r) * 2 + 1) * kTile + lane] = au[r];
-    }
+    for (int r = 0; r < P; ++r) red[(wave * P + r) * kTile + lane] = acc[r];
     __syncthreads();
     const int t = threadIdx.x;
     if (t < P * kTile) {
         const int r = t >> 6, c = t & 63;
         if (r < real) {
-            const int stride = P * 2 * kTile;
-            const float g = tree8(red + (r * 2 + 0) * kTile + c, stride);
-            const float u = tree8(red + (r * 2 + 1) * kTile + c, stride);
+            const int stride = P * kTile;
+            const float g = tree8(red + r * kTile + c, stride);
+            const float u = tree8(red + 8 * stride + r * kTile + c, stride);
             const size_t o = (size_t)entry[first + r] * I + (size_t)tile * kTile + c;
             if (SPLIT) {
                 out0[o] = g;
@@ -176,13 +172,13 @@ __device__ void gu_item(const xp_expert* __restrict__ experts, const uint16_t* _
 }
 
 template <bool SPLIT>
-__global__ __launch_bounds__(512) void gateup_kernel(const xp_expert* __restrict__ experts,
-                                                     const uint16_t* __restrict__ x,
-                                                     const int32_t* __restrict__ hdr,
-                                                     const int32_t* __restrict__ entry,
-                                                     const int4* __restrict__ passes, int H, int I, int k,
-                                                     float* __restrict__ out0, float* __restrict__ out1) {
-    __shared__ float red[kLeaves * kMaxPass * 2 * kTile];
+__global__ __launch_bounds__(1024) void gateup_kernel(const xp_expert* __restrict__ experts,
+                                                      const uint16_t* __restrict__ x,
+                                                      const int32_t* __restrict__ hdr,
+                                                      const int32_t* __restrict__ entry,
+                                                      const int4* __restrict__ passes, int H, int I, int k,
+                                                      float* __restrict__ out0, float* __restrict__ out1) {
+    __shared__ float red[2 * kLeaves * kMaxPass * kTile];
     const int n_tiles = I / kTile;
     const int n_items = hdr[0] * n_tiles;
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
@@ -206,44 +202,21 @@ __global__ __launch_bounds__(512) void gateup_kernel(const xp_expert* __restrict
 // --------------------------------------------------------------------- down
 
 template <int P>
-__device__ __forceinline__ void dn_group(u32x4 c, uint32_t sb, const float* const (&ar)[P], int g,
-                                         float (&acc)[P]) {
-    float w[32];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        f32x2 a;
-        a = fp4x2<0>(c[d]); w[8 * d + 0] = a.x; w[8 * d + 1] = a.y;
-        a = fp4x2<1>(c[d]); w[8 * d + 2] = a.x; w[8 * d + 3] = a.y;
-        a = fp4x2<2>(c[d]); w[8 * d + 4] = a.x; w[8 * d + 5] = a.y;
-        a = fp4x2<3>(c[d]); w[8 * d + 6] = a.x; w[8 * d + 7] = a.y;
-    }
-    const float s = e4m3(sb);
-#pragma unroll
-    for (int r = 0; r < P; ++r) {
-        __builtin_amdgcn_sched_barrier(0);
-        const float* xp = ar[r] + 32 * g;
-        float p = 0.0f;
-#pragma unroll
-        for (int t = 0; t < 32; ++t) p = __builtin_fmaf(w[t], xp[t], p);
-        acc[r] = __builtin_fmaf(p, s, acc[r]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-}
-
-template <int P>
 __device__ void dn_item(const xp_expert* __restrict__ experts, const float* __restrict__ act,
                         const int32_t* __restrict__ entry, int4 ps, int tile, int H, int I,
                         float* __restrict__ out, float* red) {
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    constexpr int D = DnDepth<P>::value;
+    const int leaf = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int e = ps.x, first = ps.y, real = ps.z;
     const int G = I >> 5;
-    const int ng = (G > wave) ? (G - wave + 7) >> 3 : 0;
+    const int ng = (G > leaf) ? (G - leaf + 7) >> 3 : 0;
+    const int xl = 2 * (lane & 15);
 
     const xp_expert ex = experts[e];
     const size_t tile_chunks = (size_t)tile * G * kTile;
-    const gcodes_t dc = (gcodes_t)ex.down_codes + tile_chunks + lane;
-    const gbytes_t ds = (gbytes_t)ex.down_scales + tile_chunks + lane;
+    const gcodes_t cc = (gcodes_t)ex.down_codes + tile_chunks + lane;
+    const gbytes_t ss = (gbytes_t)ex.down_scales + tile_chunks + lane;
 
     const float* ar[P];
 #pragma unroll
@@ -252,16 +225,17 @@ __device__ void dn_item(const xp_expert* __restrict__ experts, const float* __re
     float acc[P];
 #pragma unroll
     for (int r = 0; r < P; ++r) acc[r] = 0.0f;
-
-    constexpr int D = 4;
     u32x4 bc[D];
     uint32_t bs[D];
+    float2 bx[D][P];
 #pragma unroll
     for (int s = 0; s < D; ++s) {
         if (s < ng) {
-            const size_t o = (size_t)(wave + 8 * s) * kTile;
-            bc[s] = load_codes(dc + o);
-            bs[s] = ds[o];
+            const int g = leaf + 8 * s;
+            bc[s] = load_codes(cc + (size_t)g * kTile);
+            bs[s] = ss[(size_t)g * kTile];
+#pragma unroll
+            for (int r = 0; r < P; ++r) bx[s][r] = *(const float2*)(ar[r] + 32 * g + xl);
         }
     }
     for (int i0 = 0; i0 < ng; i0 += D) {
@@ -269,18 +243,29 @@ __device__ void dn_item(const xp_expert* __restrict__ experts, const float* __re
         for (int s = 0; s < D; ++s) {
             const int i = i0 + s;
             if (i < ng) {
-                dn_group<P>(bc[s], bs[s], ar, wave + 8 * i, acc);
+                float w[32];
+                decode32(bc[s], w);
+                const float sc = e4m3(bs[s]);
+                float xa[P], xb[P];
+#pragma unroll
+                for (int r = 0; r < P; ++r) { xa[r] = bx[s][r].x; xb[r] = bx[s][r].y; }
                 if (i + D < ng) {
-                    const size_t o = (size_t)(wave + 8 * (i + D)) * kTile;
-                    bc[s] = load_codes(dc + o);
-                    bs[s] = ds[o];
+                    const int g = leaf + 8 * (i + D);
+                    bc[s] = load_codes(cc + (size_t)g * kTile);
+                    bs[s] = ss[(size_t)g * kTile];
+#pragma unroll
+                    for (int r = 0; r < P; ++r) bx[s][r] = *(const float2*)(ar[r] + 32 * g + xl);
                 }
+                float p[P];
+                Chain<P>::f32(w, xa, xb, p);
+#pragma unroll
+                for (int r = 0; r < P; ++r) acc[r] = __builtin_fmaf(p[r], sc, acc[r]);
             }
         }
     }
 
 #pragma unroll
-    for (int r = 0; r < P; ++r) red[(wave * P + r) * kTile + lane] = acc[r];
+    for (int r = 0; r < P; ++r) red[(leaf * P + r) * kTile + lane] = acc[r];
     __syncthreads();
     const int t = threadIdx.x;
     if (t < P * kTile) {
@@ -293,7 +278,7 @@ __device__ void dn_item(const xp_expert* __restrict__ experts, const float* __re
     __syncthreads();
 }
 
-__global__ __launch_bounds__(512) void down_kernel(const xp_expert* __restrict__ experts,
+__global__ __launch_bounds__(512, 4) void down_kernel(const xp_expert* __restrict__ experts,
                                                    const float* __restrict__ act,
                                                    const int32_t* __restrict__ hdr,
                                                    const int32_t* __restrict__ entry,
@@ -337,10 +322,10 @@ static int gateup_common(const xp_dims* dims, int32_t rows, const uint16_t* x, c
     const int grid = grid_for(rows, dims->top_k, dims->inter / kTile);
     hipStream_t s = (hipStream_t)stream;
     if (split)
-        hipLaunchKernelGGL(gateup_kernel<true>, dim3(grid), dim3(512), 0, s, experts, x, pl.hdr, pl.entry,
+        hipLaunchKernelGGL(gateup_kernel<true>, dim3(grid), dim3(1024), 0, s, experts, x, pl.hdr, pl.entry,
                            pl.gu_pass, dims->hidden, dims->inter, dims->top_k, o0, o1);
     else
-        hipLaunchKernelGGL(gateup_kernel<false>, dim3(grid), dim3(512), 0, s, experts, x, pl.hdr, pl.entry,
+        hipLaunchKernelGGL(gateup_kernel<false>, dim3(grid), dim3(1024), 0, s, experts, x, pl.hdr, pl.entry,
                            pl.gu_pass, dims->hidden, dims->inter, dims->top_k, o0, (float*)nullptr);
     return launch_status();
 }
