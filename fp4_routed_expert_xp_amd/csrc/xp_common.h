@@ -32,7 +32,7 @@ struct Tiers {
 
 // Workspace byte offsets for a plan of up to max_rows rows.
 struct WsLayout {
-    size_t hdr, count, offset, entry, gu_pass, dn_pass, masks, base, total;
+    size_t hdr, count, offset, entry, gu_pass, dn_pass, cnt, masks, base, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -63,6 +63,7 @@ inline WsLayout ws_layout(const xp_dims* d, int32_t max_rows) {
     L.entry = o;   o = align256(o + entries * sizeof(int32_t));
     L.gu_pass = o; o = align256(o + entries * 4 * sizeof(int32_t));
     L.dn_pass = o; o = align256(o + entries * 4 * sizeof(int32_t));
+    L.cnt = o;     o = align256(o + R * (size_t)(d->hidden / kTile) * sizeof(int32_t));
     L.masks = o;   o = align256(o + nblk * E * sizeof(uint64_t));
     L.base = o;    o = align256(o + nblk * E * sizeof(int32_t));
     L.total = o;
@@ -71,6 +72,30 @@ inline WsLayout ws_layout(const xp_dims* d, int32_t max_rows) {
 
 inline int launch_status() {
     return hipGetLastError() == hipSuccess ? XP_OK : XP_ERR_HIP;
+}
+
+// Pass sizes in force (set by xp_set_tiers).
+Tiers current_tiers();
+
+// Pointers to the fields of one plan inside a workspace.
+struct WsPtrs {
+    int32_t* hdr;
+    int32_t* count;
+    int32_t* offset;
+    int32_t* entry;
+    int4* gu_pass;
+    int4* dn_pass;
+    int32_t* cnt;   // combine arrivals per (row, column tile); zero between launches
+    unsigned long long* masks;
+    int32_t* base;
+};
+
+inline WsPtrs ws_ptrs(void* ws, const xp_dims* d, int32_t rows) {
+    WsLayout L = ws_layout(d, rows);
+    char* b = (char*)ws;
+    return WsPtrs{(int32_t*)(b + L.hdr),   (int32_t*)(b + L.count),  (int32_t*)(b + L.offset),
+                  (int32_t*)(b + L.entry), (int4*)(b + L.gu_pass),   (int4*)(b + L.dn_pass),
+                  (int32_t*)(b + L.cnt),   (unsigned long long*)(b + L.masks), (int32_t*)(b + L.base)};
 }
 
 // Device view of one plan inside a workspace.
@@ -86,6 +111,50 @@ inline Plan plan_view(const void* ws, const xp_dims* d, int32_t rows) {
     const char* b = (const char*)ws;
     return Plan{(const int32_t*)(b + L.hdr), (const int32_t*)(b + L.entry),
                 (const int4*)(b + L.gu_pass), (const int4*)(b + L.dn_pass)};
+}
+
+}  // namespace xp
+
+// ---------------------------------------------------------------- wave helpers
+// Cross-lane steps by DPP (no LDS traffic). Lanes whose DPP source is outside
+// their row, or whose row is masked off, receive `old` = the identity (0).
+namespace xp {
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_or0(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t x) {
+    const uint32_t lo = dpp_or0<CTRL, ROW_MASK>((uint32_t)x);
+    const uint32_t hi = dpp_or0<CTRL, ROW_MASK>((uint32_t)(x >> 32));
+    const uint64_t y = ((uint64_t)hi << 32) | lo;
+    return y > x ? y : x;
+}
+
+// Largest unsigned 64-bit value over the wave (identity 0), returned to every lane.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+    x = dpp_max_step<0x111, 0xF>(x);  // row_shr:1
+    x = dpp_max_step<0x112, 0xF>(x);  // row_shr:2
+    x = dpp_max_step<0x114, 0xF>(x);  // row_shr:4
+    x = dpp_max_step<0x118, 0xF>(x);  // row_shr:8  -> lane 15 of each row holds the row's max
+    x = dpp_max_step<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
+    x = dpp_max_step<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3 -> lane 63 holds the max
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Inclusive prefix sum over the wave's lanes.
+__device__ __forceinline__ int wave_incl_sum(int x) {
+    x += (int)dpp_or0<0x111, 0xF>((uint32_t)x);
+    x += (int)dpp_or0<0x112, 0xF>((uint32_t)x);
+    x += (int)dpp_or0<0x114, 0xF>((uint32_t)x);
+    x += (int)dpp_or0<0x118, 0xF>((uint32_t)x);
+    x += (int)dpp_or0<0x142, 0xA>((uint32_t)x);
+    x += (int)dpp_or0<0x143, 0xC>((uint32_t)x);
+    return x;
 }
 
 }  // namespace xp

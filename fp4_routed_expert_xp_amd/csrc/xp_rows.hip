@@ -21,6 +21,7 @@
 // (P > real rows) re-read the last real row and are not stored.
 #include "xp_chain_asm.h"
 #include "xp_common.h"
+#include "xp_route_dev.h"
 
 namespace xp {
 
@@ -171,16 +172,79 @@ __device__ void gu_item(const xp_expert* __restrict__ experts, const uint16_t* _
     __syncthreads();
 }
 
-template <bool SPLIT>
+// Routing inputs for the fused route + gate/up launch (unused otherwise).
+struct RouteIn {
+    const float* logits;
+    int R, E;
+    int32_t* topk_id;
+    float* topk_w;
+    WsPtrs w;
+    Tiers T;
+};
+
+// Without ROUTE the plan comes from the workspace. With ROUTE (at most 64 rows)
+// every workgroup routes and plans the batch itself into LDS, so no separate
+// routing launch precedes this one; workgroup 0 also publishes the plan
+// (top-k, weights, entries, both pass lists, header) and clears the combine
+// counters for the down launch that follows.
+template <bool SPLIT, bool ROUTE>
 __global__ __launch_bounds__(1024) void gateup_kernel(const xp_expert* __restrict__ experts,
                                                       const uint16_t* __restrict__ x,
                                                       const int32_t* __restrict__ hdr,
-                                                      const int32_t* __restrict__ entry,
-                                                      const int4* __restrict__ passes, int H, int I, int k,
-                                                      float* __restrict__ out0, float* __restrict__ out1) {
+                                                      const int32_t* __restrict__ entry_g,
+                                                      const int4* __restrict__ passes_g, RouteIn ri, int H, int I,
+                                                      int k, float* __restrict__ out0, float* __restrict__ out1) {
     __shared__ float red[2 * kLeaves * kMaxPass * kTile];
     const int n_tiles = I / kTile;
-    const int n_items = hdr[0] * n_tiles;
+    int n_pass;
+    const int32_t* entry;
+    const int4* passes;
+    if (ROUTE) {
+        __shared__ unsigned long long smask[kMaxExperts];
+        __shared__ int32_t sid[kSmallRows][kMaxTopK];
+        __shared__ int32_t scnt[kMaxExperts];
+        __shared__ int32_t soff[kMaxExperts + 1];
+        __shared__ int32_t sentry[kSmallRows * kMaxTopK];
+        __shared__ int4 sgu[kSmallRows * kMaxTopK];
+        __shared__ int32_t sn_gu;
+        const bool lead = blockIdx.x == 0;
+        const int E = ri.E, R = ri.R;
+        for (int e = threadIdx.x; e < E; e += blockDim.x) smask[e] = 0ull;
+        __syncthreads();
+        const int wave = threadIdx.x >> 6;
+        for (int r = wave; r < R; r += 16)
+            topk_row(ri.logits, E, k, r, r, lead ? ri.topk_id : nullptr, ri.topk_w, sid[r], smask);
+        __syncthreads();
+        for (int e = threadIdx.x; e < E; e += blockDim.x) scnt[e] = __popcll(smask[e]);
+        __syncthreads();
+        if (wave == 0)
+            plan_wave(E, scnt, ri.T, soff, sgu, lead ? ri.w.dn_pass : nullptr, lead ? ri.w.count : nullptr,
+                      lead ? ri.w.offset : nullptr, lead ? ri.w.hdr : nullptr, &sn_gu);
+        __syncthreads();
+        const int t = threadIdx.x;
+        if (t < R * k) {
+            const int r = t / k, j = t - r * k;
+            const int e = sid[r][j];
+            const unsigned long long below = (r == 0) ? 0ull : (smask[e] & ((1ull << r) - 1ull));
+            const int pos = soff[e] + __popcll(below);
+            sentry[pos] = t;
+            if (lead) ri.w.entry[pos] = t;
+        }
+        __syncthreads();
+        n_pass = sn_gu;
+        if (lead) {
+            for (int i = t; i < n_pass; i += blockDim.x) ri.w.gu_pass[i] = sgu[i];
+            const int n_cnt = R * (H / kTile);
+            for (int i = t; i < n_cnt; i += blockDim.x) ri.w.cnt[i] = 0;
+        }
+        entry = sentry;
+        passes = sgu;
+    } else {
+        n_pass = hdr[0];
+        entry = entry_g;
+        passes = passes_g;
+    }
+    const int n_items = n_pass * n_tiles;
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
         const int pass = item / n_tiles;
         const int tile = item - pass * n_tiles;
@@ -201,10 +265,18 @@ __global__ __launch_bounds__(1024) void gateup_kernel(const xp_expert* __restric
 
 // --------------------------------------------------------------------- down
 
-template <int P>
+// Combine inputs for the fused down + combine launch (unused otherwise).
+struct CombineIn {
+    const float* topk_w;
+    float* y;
+    int32_t* cnt;
+    int k;
+};
+
+template <int P, bool COMBINE>
 __device__ void dn_item(const xp_expert* __restrict__ experts, const float* __restrict__ act,
                         const int32_t* __restrict__ entry, int4 ps, int tile, int H, int I,
-                        float* __restrict__ out, float* red) {
+                        float* __restrict__ out, float* red, const CombineIn& ci) {
     constexpr int D = DnDepth<P>::value;
     const int leaf = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -271,19 +343,39 @@ __device__ void dn_item(const xp_expert* __restrict__ experts, const float* __re
     if (t < P * kTile) {
         const int r = t >> 6, c = t & 63;
         if (r < real) {
+            const int ent = entry[first + r];
             const float v = tree8(red + r * kTile + c, P * kTile);
-            out[(size_t)entry[first + r] * H + (size_t)tile * kTile + c] = v;
+            out[(size_t)ent * H + (size_t)tile * kTile + c] = v;
+            if (COMBINE) {
+                // Wave r wrote this (row, slot, tile). The wave that brings the
+                // row's count to k sums the k slots in slot order, exactly as
+                // combine_kernel does, and resets the count for the next launch.
+                const int row = ent / ci.k;
+                int32_t* ctr = ci.cnt + (size_t)row * (H / kTile) + tile;
+                int old = 0;
+                if (c == 0) old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+                old = __builtin_amdgcn_readfirstlane(old);
+                if (old == ci.k - 1) {
+                    const float* o = out + (size_t)row * ci.k * H + (size_t)tile * kTile + c;
+                    const float* wr = ci.topk_w + (size_t)row * ci.k;
+                    float sum = 0.0f;
+                    for (int j = 0; j < ci.k; ++j) sum = __builtin_fmaf(wr[j], o[(size_t)j * H], sum);
+                    ci.y[(size_t)row * H + (size_t)tile * kTile + c] = sum;
+                    if (c == 0) *ctr = 0;
+                }
+            }
         }
     }
     __syncthreads();
 }
 
+template <bool COMBINE>
 __global__ __launch_bounds__(512, 4) void down_kernel(const xp_expert* __restrict__ experts,
-                                                   const float* __restrict__ act,
-                                                   const int32_t* __restrict__ hdr,
-                                                   const int32_t* __restrict__ entry,
-                                                   const int4* __restrict__ passes, int H, int I,
-                                                   float* __restrict__ out) {
+                                                      const float* __restrict__ act,
+                                                      const int32_t* __restrict__ hdr,
+                                                      const int32_t* __restrict__ entry,
+                                                      const int4* __restrict__ passes, int H, int I,
+                                                      float* __restrict__ out, CombineIn ci) {
     __shared__ float red[kLeaves * kMaxPass * kTile];
     const int n_tiles = H / kTile;
     const int n_items = hdr[1] * n_tiles;
@@ -292,14 +384,14 @@ __global__ __launch_bounds__(512, 4) void down_kernel(const xp_expert* __restric
         const int tile = item - pass * n_tiles;
         const int4 ps = passes[pass];
         switch (ps.w) {
-            case 1: dn_item<1>(experts, act, entry, ps, tile, H, I, out, red); break;
-            case 2: dn_item<2>(experts, act, entry, ps, tile, H, I, out, red); break;
-            case 3: dn_item<3>(experts, act, entry, ps, tile, H, I, out, red); break;
-            case 4: dn_item<4>(experts, act, entry, ps, tile, H, I, out, red); break;
-            case 5: dn_item<5>(experts, act, entry, ps, tile, H, I, out, red); break;
-            case 6: dn_item<6>(experts, act, entry, ps, tile, H, I, out, red); break;
-            case 7: dn_item<7>(experts, act, entry, ps, tile, H, I, out, red); break;
-            case 8: dn_item<8>(experts, act, entry, ps, tile, H, I, out, red); break;
+            case 1: dn_item<1, COMBINE>(experts, act, entry, ps, tile, H, I, out, red, ci); break;
+            case 2: dn_item<2, COMBINE>(experts, act, entry, ps, tile, H, I, out, red, ci); break;
+            case 3: dn_item<3, COMBINE>(experts, act, entry, ps, tile, H, I, out, red, ci); break;
+            case 4: dn_item<4, COMBINE>(experts, act, entry, ps, tile, H, I, out, red, ci); break;
+            case 5: dn_item<5, COMBINE>(experts, act, entry, ps, tile, H, I, out, red, ci); break;
+            case 6: dn_item<6, COMBINE>(experts, act, entry, ps, tile, H, I, out, red, ci); break;
+            case 7: dn_item<7, COMBINE>(experts, act, entry, ps, tile, H, I, out, red, ci); break;
+            case 8: dn_item<8, COMBINE>(experts, act, entry, ps, tile, H, I, out, red, ci); break;
             default: break;
         }
     }
@@ -321,12 +413,35 @@ static int gateup_common(const xp_dims* dims, int32_t rows, const uint16_t* x, c
     Plan pl = plan_view(ws, dims, rows);
     const int grid = grid_for(rows, dims->top_k, dims->inter / kTile);
     hipStream_t s = (hipStream_t)stream;
+    RouteIn none{};
     if (split)
-        hipLaunchKernelGGL(gateup_kernel<true>, dim3(grid), dim3(1024), 0, s, experts, x, pl.hdr, pl.entry,
-                           pl.gu_pass, dims->hidden, dims->inter, dims->top_k, o0, o1);
+        hipLaunchKernelGGL((gateup_kernel<true, false>), dim3(grid), dim3(1024), 0, s, experts, x, pl.hdr, pl.entry,
+                           pl.gu_pass, none, dims->hidden, dims->inter, dims->top_k, o0, o1);
     else
-        hipLaunchKernelGGL(gateup_kernel<false>, dim3(grid), dim3(1024), 0, s, experts, x, pl.hdr, pl.entry,
-                           pl.gu_pass, dims->hidden, dims->inter, dims->top_k, o0, (float*)nullptr);
+        hipLaunchKernelGGL((gateup_kernel<false, false>), dim3(grid), dim3(1024), 0, s, experts, x, pl.hdr, pl.entry,
+                           pl.gu_pass, none, dims->hidden, dims->inter, dims->top_k, o0, (float*)nullptr);
+    return launch_status();
+}
+
+static int down_common(const xp_dims* dims, int32_t rows, const float* act, const xp_expert* experts,
+                       const float* topk_w, void* ws, size_t ws_bytes, float* out, float* y, bool combine,
+                       void* stream) {
+    int st = check_dims(dims);
+    if (st != XP_OK) return st;
+    if (rows < 0) return XP_ERR_SHAPE;
+    if (rows == 0) return XP_OK;
+    if (!act || !experts || !ws || !out || (combine && (!topk_w || !y))) return XP_ERR_NULL;
+    if (ws_bytes < ws_layout(dims, rows).total) return XP_ERR_WORKSPACE;
+    Plan pl = plan_view(ws, dims, rows);
+    WsPtrs w = ws_ptrs(ws, dims, rows);
+    const int grid = grid_for(rows, dims->top_k, dims->hidden / kTile);
+    CombineIn ci{topk_w, y, w.cnt, dims->top_k};
+    if (combine)
+        hipLaunchKernelGGL(down_kernel<true>, dim3(grid), dim3(512), 0, (hipStream_t)stream, experts, act, pl.hdr,
+                           pl.entry, pl.dn_pass, dims->hidden, dims->inter, out, ci);
+    else
+        hipLaunchKernelGGL(down_kernel<false>, dim3(grid), dim3(512), 0, (hipStream_t)stream, experts, act, pl.hdr,
+                           pl.entry, pl.dn_pass, dims->hidden, dims->inter, out, ci);
     return launch_status();
 }
 
@@ -346,15 +461,35 @@ XP_API int xp_gateup_rows_split(const xp_dims* dims, int32_t rows, const uint16_
 
 XP_API int xp_down_rows(const xp_dims* dims, int32_t rows, const float* act, const xp_expert* experts,
                         const void* workspace, size_t ws_bytes, float* out, void* stream) {
+    return down_common(dims, rows, act, experts, nullptr, (void*)workspace, ws_bytes, out, nullptr, false, stream);
+}
+
+XP_API int xp_route_gateup(const xp_dims* dims, int32_t rows, const float* logits, const uint16_t* x,
+                           const xp_expert* experts, int32_t* topk_id, float* topk_w, void* workspace,
+                           size_t ws_bytes, float* act, void* stream) {
     int st = check_dims(dims);
     if (st != XP_OK) return st;
     if (rows < 0) return XP_ERR_SHAPE;
     if (rows == 0) return XP_OK;
-    if (!act || !experts || !workspace || !out) return XP_ERR_NULL;
+    if (!logits || !x || !experts || !topk_id || !topk_w || !workspace || !act) return XP_ERR_NULL;
     if (ws_bytes < ws_layout(dims, rows).total) return XP_ERR_WORKSPACE;
-    Plan pl = plan_view(workspace, dims, rows);
-    const int grid = grid_for(rows, dims->top_k, dims->hidden / kTile);
-    hipLaunchKernelGGL(down_kernel, dim3(grid), dim3(512), 0, (hipStream_t)stream, experts, act, pl.hdr, pl.entry,
-                       pl.dn_pass, dims->hidden, dims->inter, out);
+    if (rows > kSmallRows) {
+        // larger batches: the separate routing launch, then gate/up
+        st = xp_route_bucket(dims, rows, logits, topk_id, topk_w, workspace, ws_bytes, stream);
+        if (st != XP_OK) return st;
+        return xp_gateup_rows(dims, rows, x, experts, workspace, ws_bytes, act, stream);
+    }
+    WsPtrs w = ws_ptrs(workspace, dims, rows);
+    RouteIn ri{logits, rows, dims->n_experts, topk_id, topk_w, w, current_tiers()};
+    const int grid = grid_for(rows, dims->top_k, dims->inter / kTile);
+    hipLaunchKernelGGL((gateup_kernel<false, true>), dim3(grid), dim3(1024), 0, (hipStream_t)stream, experts, x,
+                       (const int32_t*)nullptr, (const int32_t*)nullptr, (const int4*)nullptr, ri, dims->hidden,
+                       dims->inter, dims->top_k, act, (float*)nullptr);
     return launch_status();
+}
+
+XP_API int xp_down_combine(const xp_dims* dims, int32_t rows, const float* act, const xp_expert* experts,
+                           const float* topk_w, void* workspace, size_t ws_bytes, float* out, float* y,
+                           void* stream) {
+    return down_common(dims, rows, act, experts, topk_w, workspace, ws_bytes, out, y, true, stream);
 }

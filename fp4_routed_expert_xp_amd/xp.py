@@ -21,7 +21,7 @@ XP_OK, XP_ERR_NULL, XP_ERR_SHAPE, XP_ERR_TOPK, XP_ERR_WORKSPACE, XP_ERR_TIERS, X
 EXPORTS = (
     "xp_pack_matrix", "xp_workspace_bytes", "xp_workspace_layout", "xp_route_bucket",
     "xp_gateup_rows", "xp_gateup_rows_split", "xp_down_rows", "xp_combine",
-    "xp_set_tiers", "xp_get_tiers", "xp_status_string",
+    "xp_set_tiers", "xp_get_tiers", "xp_status_string", "xp_route_gateup", "xp_down_combine",
 )
 
 
@@ -66,12 +66,15 @@ def lib():
         L.xp_gateup_rows_split.argtypes = [D, i32, P, P, P, sz, P, P, P]
         L.xp_down_rows.argtypes = [D, i32, P, P, P, sz, P, P]
         L.xp_combine.argtypes = [D, i32, P, P, P, P]
+        L.xp_route_gateup.argtypes = [D, i32, P, P, P, P, P, P, sz, P, P]
+        L.xp_down_combine.argtypes = [D, i32, P, P, P, P, sz, P, P, P]
         L.xp_set_tiers.argtypes = [P, i32, P, i32]
         L.xp_get_tiers.argtypes = [P, P, P, P]
         L.xp_status_string.argtypes = [ctypes.c_int]
         L.xp_status_string.restype = ctypes.c_char_p
         for name in ("xp_pack_matrix", "xp_workspace_layout", "xp_route_bucket", "xp_gateup_rows",
-                     "xp_gateup_rows_split", "xp_down_rows", "xp_combine", "xp_set_tiers", "xp_get_tiers"):
+                     "xp_gateup_rows_split", "xp_down_rows", "xp_combine", "xp_set_tiers", "xp_get_tiers",
+                     "xp_route_gateup", "xp_down_combine"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -122,7 +125,7 @@ def xp_workspace_bytes(d: xp_dims, max_rows: int) -> int:
 
 
 def xp_workspace_layout(d: xp_dims, max_rows: int) -> list:
-    off = (ctypes.c_size_t * 6)()
+    off = (ctypes.c_size_t * 7)()
     _check(lib().xp_workspace_layout(ctypes.byref(d), int(max_rows), off), "xp_workspace_layout")
     return list(off)
 
@@ -208,6 +211,35 @@ def xp_combine(d: xp_dims, rows: int, out, topk_w, y, stream=None) -> None:
         _dev(y, torch.float32, "y", rows * d.hidden)
     _check(lib().xp_combine(ctypes.byref(d), int(rows), _ptr(out), _ptr(topk_w), _ptr(y), _stream(stream)),
            "xp_combine")
+
+
+def xp_route_gateup(d: xp_dims, rows: int, logits, x, experts, topk_id, topk_w, workspace, act,
+                    stream=None) -> None:
+    if rows > 0:
+        _dev(logits, torch.float32, "logits", rows * d.n_experts)
+        _dev_bf16(x, "x", rows * d.hidden)
+        _dev(experts, torch.int64, "experts", d.n_experts * 6)
+        _dev(topk_id, torch.int32, "topk_id", rows * d.top_k)
+        _dev(topk_w, torch.float32, "topk_w", rows * d.top_k)
+        _dev(workspace, torch.uint8, "workspace")
+        _dev(act, torch.float32, "act", rows * d.top_k * d.inter)
+    nbytes = workspace.numel() if workspace is not None else 0
+    _check(lib().xp_route_gateup(ctypes.byref(d), int(rows), _ptr(logits), _ptr(x), _ptr(experts), _ptr(topk_id),
+                                 _ptr(topk_w), _ptr(workspace), nbytes, _ptr(act), _stream(stream)),
+           "xp_route_gateup")
+
+
+def xp_down_combine(d: xp_dims, rows: int, act, experts, topk_w, workspace, out, y, stream=None) -> None:
+    if rows > 0:
+        _dev(act, torch.float32, "act", rows * d.top_k * d.inter)
+        _dev(experts, torch.int64, "experts", d.n_experts * 6)
+        _dev(topk_w, torch.float32, "topk_w", rows * d.top_k)
+        _dev(workspace, torch.uint8, "workspace")
+        _dev(out, torch.float32, "out", rows * d.top_k * d.hidden)
+        _dev(y, torch.float32, "y", rows * d.hidden)
+    nbytes = workspace.numel() if workspace is not None else 0
+    _check(lib().xp_down_combine(ctypes.byref(d), int(rows), _ptr(act), _ptr(experts), _ptr(topk_w),
+                                 _ptr(workspace), nbytes, _ptr(out), _ptr(y), _stream(stream)), "xp_down_combine")
 
 
 # -------------------------------------------------------------- conveniences

@@ -103,16 +103,18 @@ int xp_pack_matrix(int32_t n, int32_t k, const uint8_t* codes, const uint8_t* sc
 /* Bytes of workspace needed to plan up to max_rows rows (host, pure; 0 on bad dims). */
 size_t xp_workspace_bytes(const xp_dims* dims, int32_t max_rows);
 
-/* Byte offsets of the plan's fields inside a workspace sized for max_rows
- * (host, pure), for callers that read the plan back:
+/* Byte offsets of the fields of the plan for max_rows rows (host, pure), for
+ * callers that read the plan back. A plan made for R rows uses the offsets for
+ * R, so the calls that read one plan must pass the same row count:
  *   off[0] header: int32 [0] = gate/up passes, [1] = down passes
  *   off[1] count  int32 [E]          rows per expert
  *   off[2] offset int32 [E+1]        first entry of each expert
  *   off[3] entry  int32 [R*k]        row*k + slot, experts ascending, rows ascending
  *   off[4] gate/up passes int32 [R*k][4] = (expert, first entry, real rows, pass size)
  *   off[5] down passes    int32 [R*k][4]
+ *   off[6] combine counts int32 [R][hidden/64] (zero between launches)
  * Returns XP_OK or an error for bad dims. */
-int xp_workspace_layout(const xp_dims* dims, int32_t max_rows, size_t off[6]);
+int xp_workspace_layout(const xp_dims* dims, int32_t max_rows, size_t off[7]);
 
 /* ----------------------------------------------------------- the four calls */
 
@@ -150,6 +152,27 @@ int xp_down_rows(const xp_dims* dims, int32_t rows, const float* act, const xp_e
  * topk_w[row][j] * out[row][j]. [#2983, "Receipt": the combine output] */
 int xp_combine(const xp_dims* dims, int32_t rows, const float* out, const float* topk_w, float* y,
                void* stream);
+
+/* ------------------------------------------------------------ fused calls
+ * The same path in two launches instead of four, with the same bits. */
+
+/* xp_route_bucket followed by xp_gateup_rows. With rows <= 64 this is one
+ * launch: every workgroup routes and plans the batch itself, so no launch
+ * boundary separates routing from the weight stream; the plan, topk_id and
+ * topk_w are still written to the workspace and outputs. More rows run the
+ * two calls. */
+int xp_route_gateup(const xp_dims* dims, int32_t rows, const float* logits, const uint16_t* x,
+                    const xp_expert* experts, int32_t* topk_id, float* topk_w, void* workspace,
+                    size_t ws_bytes, float* act, void* stream);
+
+/* xp_down_rows followed by xp_combine in one launch: for each (row, 64-column
+ * tile) the down workgroup that writes the last of the row's k slots sums
+ * them in slot order (the combine's arithmetic) into y. Uses the workspace's
+ * combine counts, which xp_route_bucket / xp_route_gateup clear and this call
+ * leaves cleared; calls on one workspace must not overlap. */
+int xp_down_combine(const xp_dims* dims, int32_t rows, const float* act, const xp_expert* experts,
+                    const float* topk_w, void* workspace, size_t ws_bytes, float* out, float* y,
+                    void* stream);
 
 /* ------------------------------------------------------------ pass sizes */
 

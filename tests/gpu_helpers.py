@@ -115,3 +115,30 @@ def same_class(gpu: np.ndarray, ref: np.ndarray) -> bool:
 
 def bits(a: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+
+
+def run_fused(layer: DeviceLayer, x_bits: np.ndarray, logits: np.ndarray, repeat_down: int = 1) -> dict:
+    """The two-launch path: xp_route_gateup then xp_down_combine (optionally repeated on one plan)."""
+    d = layer.d
+    R = x_bits.shape[0]
+    k, H, I = d.top_k, d.hidden, d.inter
+    x = to_dev(x_bits)
+    lg = to_dev(logits.astype(np.float32))
+    ws = torch.zeros(max(xp.xp_workspace_bytes(d, R), 256), dtype=torch.uint8, device="cuda")
+    nan = float("nan")
+    topk_id = torch.full((R, k), -1, dtype=torch.int32, device="cuda")
+    topk_w = torch.full((R, k), nan, dtype=torch.float32, device="cuda")
+    act = torch.full((R, k, I), nan, dtype=torch.float32, device="cuda")
+    out = torch.full((R, k, H), nan, dtype=torch.float32, device="cuda")
+    y = torch.full((R, H), nan, dtype=torch.float32, device="cuda")
+    xp.xp_route_gateup(d, R, lg, x, layer.table, topk_id, topk_w, ws, act)
+    ys = []
+    for _ in range(repeat_down):
+        y.fill_(nan)
+        xp.xp_down_combine(d, R, act, layer.table, topk_w, ws, out, y)
+        ys.append(y.clone())
+    torch.cuda.synchronize()
+    res = dict(topk_id=topk_id, topk_w=topk_w, act=act, out=out, y=y, ws=ws)
+    res = {kk: v.cpu().numpy() for kk, v in res.items()}
+    res["y_each"] = [t.cpu().numpy() for t in ys]
+    return res

@@ -1,0 +1,82 @@
+"""GPU: the two-launch path (xp_route_gateup, xp_down_combine) against the four calls.
+
+Both paths run the same per-row arithmetic, so every output must be bit-equal,
+the published plan must be the same, and repeated down+combine launches on one
+plan must keep giving the same y (the combine counts are left cleared)."""
+import numpy as np
+import pytest
+
+import synth
+from fp4_routed_expert_xp_amd import xp
+
+from gpu_helpers import DeviceLayer, bits, log, read_plan, run_fused, run_path
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tiny_layer():
+    return DeviceLayer(synth.CONFIGS["tiny"], 0)
+
+
+@pytest.fixture(scope="module")
+def release_layer():
+    log("materialising release-width layer 0 (256 experts)")
+    return DeviceLayer(synth.CONFIGS["one_row"], 0)
+
+
+def _compare(layer, x, lg, tag):
+    a = run_path(layer, x, lg)
+    b = run_fused(layer, x, lg, repeat_down=3)
+    assert np.array_equal(a["topk_id"], b["topk_id"]), tag
+    for n in ("topk_w", "act", "out", "y"):
+        assert np.array_equal(bits(a[n]), bits(b[n])), (tag, n)
+    for yy in b["y_each"]:
+        assert np.array_equal(bits(yy), bits(a["y"])), (tag, "repeat")
+    pa, pb = read_plan(layer.d, x.shape[0], a["ws"]), read_plan(layer.d, x.shape[0], b["ws"])
+    for n in ("count", "offset", "entry", "gu", "dn"):
+        assert np.array_equal(pa[n], pb[n]), (tag, n)
+    assert (pa["n_gu"], pa["n_dn"]) == (pb["n_gu"], pb["n_dn"]), tag
+
+
+@pytest.mark.parametrize("R", [1, 2, 4, 5, 16, 64, 65, 100])
+def test_fused_equals_four_calls_tiny(tiny_layer, R):
+    cfg = tiny_layer.cfg
+    x = synth.activations(cfg.seed + 5, R, R, cfg.H)
+    lg = synth.logits(cfg.seed + 5, R, R, cfg.E)
+    if R >= 2:
+        x, _, _ = synth.plant_nan_inf(cfg.seed, R, x)
+    _compare(tiny_layer, x, lg, "tiny R=%d" % R)
+
+
+@pytest.mark.parametrize("name", ["one_row", "four_same", "sixteen_random"])
+def test_fused_equals_four_calls_release(release_layer, name):
+    cfg = synth.CONFIGS[name]
+    x, lg = synth.layer_inputs(cfg, 0)
+    log("fused %s" % name)
+    _compare(release_layer, x, lg, name)
+
+
+@pytest.mark.parametrize("tiers", [((4,), (4,)), ((2, 4, 8), (2, 4, 8))])
+def test_fused_other_tiers(release_layer, tiers):
+    cfg = synth.CONFIGS["sixteen_random"]
+    x = synth.activations(cfg.seed, 7, 16, cfg.H)
+    lg = synth.logits_same(cfg.seed, 7, 16, cfg.E)
+    lg[8:] = synth.logits(cfg.seed, 7, 8, cfg.E)
+    xp.xp_set_tiers(list(tiers[0]), list(tiers[1]))
+    try:
+        _compare(release_layer, x, lg, "tiers %s" % (tiers,))
+    finally:
+        xp.xp_set_tiers(None, None)
+
+
+def test_fused_probe_tiny(tiny_layer):
+    cfg = tiny_layer.cfg
+    for R in (3, 9, 16):
+        x = synth.activations(cfg.seed + 9, R, R, cfg.H)
+        lg = synth.logits_same(cfg.seed + 9, R, R, cfg.E)
+        batch = run_fused(tiny_layer, x, lg)
+        for r in range(R):
+            solo = run_fused(tiny_layer, x[r:r + 1], lg[r:r + 1])
+            for n in ("act", "out", "y"):
+                assert np.array_equal(bits(batch[n][r]), bits(solo[n][0])), (R, r, n)
