@@ -7,8 +7,10 @@ whole hot path (route + bucket, gate/up + SwiGLU, down, combine) through the C
 ABI. The round is captured once as a HIP graph and replayed; all weights
 (40 x 256 experts, 13,369,344 B each) are resident in HBM before timing.
 
-The headline line is the one-row workload; the four-row same-expert and the
-sixteen-row random workloads are reported as extra cells on the same line.
+The headline is the one-row workload on the two-launch path (xp_route_gateup,
+xp_down_combine); every workload is also timed on the four-call path, and the
+four-row same-expert and sixteen-row random workloads are extra cells on the
+same line.
 Prints ONE JSON line.
 """
 from __future__ import annotations
@@ -120,22 +122,29 @@ class Cell:
         self.out = torch.empty((R, k, H), dtype=torch.float32, device="cuda")
         self.y = torch.empty((R, H), dtype=torch.float32, device="cuda")
 
-    def layer(self, l: int, ev=None) -> None:
+    def call(self, kind: str, l: int) -> None:
+        """One library call of layer l."""
         from fp4_routed_expert_xp_amd import xp
-        c, d, R, tab = self.cfg, self.d, self.cfg.R, self.model.tables[l]
-        if ev: ev[0].record()
-        xp.xp_route_bucket(d, R, self.logits[l], self.topk_id, self.topk_w, self.ws[l])
-        if ev: ev[1].record()
-        xp.xp_gateup_rows(d, R, self.x[l], tab, self.ws[l], self.act)
-        if ev: ev[2].record()
-        xp.xp_down_rows(d, R, self.act, tab, self.ws[l], self.out)
-        if ev: ev[3].record()
-        xp.xp_combine(d, R, self.out, self.topk_w, self.y)
-        if ev: ev[4].record()
+        d, R, tab, ws = self.d, self.cfg.R, self.model.tables[l], self.ws[l]
+        if kind == "route":
+            xp.xp_route_bucket(d, R, self.logits[l], self.topk_id, self.topk_w, ws)
+        elif kind == "gateup":
+            xp.xp_gateup_rows(d, R, self.x[l], tab, ws, self.act)
+        elif kind == "down":
+            xp.xp_down_rows(d, R, self.act, tab, ws, self.out)
+        elif kind == "combine":
+            xp.xp_combine(d, R, self.out, self.topk_w, self.y)
+        elif kind == "route_gateup":
+            xp.xp_route_gateup(d, R, self.logits[l], self.x[l], tab, self.topk_id, self.topk_w, ws, self.act)
+        elif kind == "down_combine":
+            xp.xp_down_combine(d, R, self.act, tab, self.topk_w, ws, self.out, self.y)
+        else:
+            raise ValueError(kind)
 
-    def round(self) -> None:
+    def round(self, kinds) -> None:
         for l in range(self.layers):
-            self.layer(l)
+            for kind in kinds:
+                self.call(kind, l)
 
     def plan_stats(self) -> dict:
         """Distinct experts and pass sizes per layer, read back from the workspaces."""
@@ -156,14 +165,38 @@ class Cell:
         return dict(distinct=distinct, gu_rows=gu_rows, dn_rows=dn_rows)
 
 
-def time_cell(cell: Cell, steps: int, warmup: int) -> dict:
+PATHS = {"four_calls": ("route", "gateup", "down", "combine"), "two_calls": ("route_gateup", "down_combine")}
+
+
+def _graph(fn):
     import torch
-    torch.cuda.synchronize()
-    cell.round()                      # one eager round (plans in place, lazy init done)
-    torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        cell.round()
+        fn()
+    return g
+
+
+def _replay_ms(g, reps: int) -> float:
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def time_cell(cell: Cell, path: str, steps: int, warmup: int) -> dict:
+    """Round time of one path (graph of the 40-layer round), then each call's
+    average duration: a graph of that call for every layer, back to back, timed
+    with events on the launch stream (the plans are in place from the rounds)."""
+    import torch
+    kinds = PATHS[path]
+    torch.cuda.synchronize()
+    cell.round(kinds)                 # one eager round: plans in place, lazy init done
+    torch.cuda.synchronize()
+    g = _graph(lambda: cell.round(kinds))
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
@@ -176,40 +209,35 @@ def time_cell(cell: Cell, steps: int, warmup: int) -> dict:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / steps
-    # per-kernel durations: each call of one eager round bracketed by events on the launch stream
-    L = cell.layers
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(L)]
-    per = {"route": 0.0, "gateup": 0.0, "down": 0.0, "combine": 0.0}
-    reps = 3
-    for _ in range(reps):
-        for l in range(L):
-            cell.layer(l, evs[l])
+    per = {}
+    for kind in kinds:
+        gk = _graph(lambda: [cell.call(kind, l) for l in range(cell.layers)])
+        gk.replay()
         torch.cuda.synchronize()
-        for l in range(L):
-            ev = evs[l]
-            for i, name in enumerate(("route", "gateup", "down", "combine")):
-                per[name] += ev[i].elapsed_time(ev[i + 1]) * 1e3
-    per = {k: v / (reps * L) for k, v in per.items()}
+        per[kind] = _replay_ms(gk, 5) * 1e3 / cell.layers
+        del gk
     del g
-    return dict(ms_per_round=ms, wall_s=wall, kernel_us=per)
+    return dict(path=path, ms_per_round=ms, wall_s=wall, kernel_us=per)
 
 
 def cell_report(cell: Cell, t: dict, copy_gbps: float) -> dict:
     cfg = cell.cfg
     st = cell.plan_stats()
     L = cell.layers
-    H, I, k, R = cfg.H, cfg.I, cfg.k, cfg.R
+    H, I, k, R, E = cfg.H, cfg.I, cfg.k, cfg.R, cfg.E
     gu_w = 2 * (I * H // 2 + I * H // 32)            # gate+up bytes of one expert
     dn_w = H * I // 2 + H * I // 32
     distinct = sum(st["distinct"]) / L
     unique_bytes = distinct * cfg.expert_bytes
     layer_us = t["ms_per_round"] * 1e3 / L
     gbps = unique_bytes / (layer_us * 1e-6) / 1e9
-    # gate/up launch: weights of its distinct experts + x read + act written
-    gu_bytes = distinct * gu_w + R * H * 2 + R * k * I * 4
-    gu_us = t["kernel_us"]["gateup"]
-    dn_bytes = distinct * dn_w + R * k * I * 4 + R * k * H * 4
-    dn_us = t["kernel_us"]["down"]
+    fused = t["path"] == "two_calls"
+    gu_kind, dn_kind = ("route_gateup", "down_combine") if fused else ("gateup", "down")
+    # algorithmic bytes of the gate/up launch: its distinct experts' gate+up weights, x read,
+    # act written (+ logits read, top-k and plan written when it routes)
+    gu_bytes = distinct * gu_w + R * H * 2 + R * k * I * 4 + ((R * E * 4 + R * k * 8) if fused else 0)
+    dn_bytes = distinct * dn_w + R * k * I * 4 + R * k * H * 4 + ((R * k * H * 4 + R * H * 4) if fused else 0)
+    gu_us, dn_us = t["kernel_us"][gu_kind], t["kernel_us"][dn_kind]
     # VALU lane-ops: one fma per weight per computed row (padding included), one
     # decode per two weights per pass, one scaled fma per group per row
     gu_rows = sum(st["gu_rows"]) / L
@@ -218,7 +246,7 @@ def cell_report(cell: Cell, t: dict, copy_gbps: float) -> dict:
     ops += (distinct * (2 * I * H + H * I)) / 2     # at least one decode pass per expert
     valu_us = ops / (CUS * LANES * CLOCK_GHZ * 1e9) * 1e6
     return dict(
-        workload=cfg.name, rows=R, layers=L,
+        workload=cfg.name, path=t["path"], rows=R, layers=L,
         round_ms=round(t["ms_per_round"], 4), layer_us=round(layer_us, 3),
         rows_per_s=round(R / (t["ms_per_round"] / 1e3), 2),
         row_layers_per_s=round(R * L / (t["ms_per_round"] / 1e3), 1),
@@ -226,8 +254,8 @@ def cell_report(cell: Cell, t: dict, copy_gbps: float) -> dict:
         weight_gbps=round(gbps, 1), pct_hbm_peak=round(100 * gbps / HBM_PEAK_GBPS, 2),
         pct_copy_bw=round(100 * gbps / copy_gbps, 2),
         kernel_us={kk: round(v, 3) for kk, v in t["kernel_us"].items()},
-        gateup_gbps=round(gu_bytes / (gu_us * 1e-6) / 1e9, 1), gateup_bytes=int(gu_bytes),
-        down_gbps=round(dn_bytes / (dn_us * 1e-6) / 1e9, 1), down_bytes=int(dn_bytes),
+        gateup_kernel=gu_kind, gateup_gbps=round(gu_bytes / (gu_us * 1e-6) / 1e9, 1), gateup_bytes=int(gu_bytes),
+        down_kernel=dn_kind, down_gbps=round(dn_bytes / (dn_us * 1e-6) / 1e9, 1), down_bytes=int(dn_bytes),
         valu_bound_us=round(valu_us, 2),
     )
 
@@ -286,14 +314,16 @@ def main():
     for name in cells:
         cfg = synth.CONFIGS[name]
         cell = Cell(model, cfg, args.layers)
-        t = time_cell(cell, args.steps, args.warmup)
-        timings[name] = t
-        reports[name] = cell_report(cell, t, copy_gbps)
-        log("%s: %s" % (name, json.dumps(reports[name])))
-    head = reports[cells[0]]
-    th = timings[cells[0]]
-    gu_us = head["kernel_us"]["gateup"]
-    achieved = head["gateup_bytes"] / (gu_us * 1e-6) / 1e9
+        for path in ("two_calls", "four_calls"):
+            t = time_cell(cell, path, args.steps, args.warmup)
+            key = "%s/%s" % (name, path)
+            timings[key] = t
+            reports[key] = cell_report(cell, t, copy_gbps)
+            log("%s: %s" % (key, json.dumps(reports[key])))
+    head_key = "%s/two_calls" % cells[0]
+    head = reports[head_key]
+    th = timings[head_key]
+    achieved = head["gateup_gbps"]
     line = {
         "metric": METRIC,
         "value": head["rows_per_s"],
@@ -308,11 +338,14 @@ def main():
         "dtype": "f32",
         "data": "synthetic (seeded fp4 e2m1 codes, E4M3 2^U{-6..0} scales, bf16 N(0,1) x, N(0,1) logits)",
         "config": {"workload": "%s: %d-row decode through a %d-layer round of independent layers, hidden %d, "
-                               "intermediate %d, %d experts, top-%d" % (cells[0], head["rows"], args.layers,
-                                                                         base.H, base.I, base.E, base.k),
+                               "intermediate %d, %d experts, top-%d; two launches per layer "
+                               "(xp_route_gateup, xp_down_combine)" % (cells[0], head["rows"], args.layers,
+                                                                        base.H, base.I, base.E, base.k),
                    "rows": head["rows"], "layers": args.layers, "hidden": base.H, "inter": base.I,
-                   "experts": base.E, "top_k": base.k},
-        "roofline": {"kernel": "gateup_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+                   "experts": base.E, "top_k": base.k, "path": "two_calls"},
+        "roofline": {"kernel": "gateup_kernel<false,true> (xp_route_gateup)", "bound": "hbm",
+                     "achieved": round(achieved, 1), "bytes_per_launch": head["gateup_bytes"],
+                     "launch_us": head["kernel_us"]["route_gateup"],
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": None},
         "copy_gbps": round(copy_gbps, 1),

@@ -22,17 +22,15 @@ constexpr int kMaxItemsGrid = 8192;
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// Pass sizes, passed by value to the route kernels.
+// Pass sizes as bit sets: bit p is set when a pass of p rows is allowed (2 <= p <= 8).
 struct Tiers {
-    int32_t gu[8];
-    int32_t n_gu;
-    int32_t dn[8];
-    int32_t n_dn;
+    uint32_t gu;
+    uint32_t dn;
 };
 
 // Workspace byte offsets for a plan of up to max_rows rows.
 struct WsLayout {
-    size_t hdr, count, offset, entry, gu_pass, dn_pass, cnt, masks, base, total;
+    size_t hdr, count, offset, entry, gu_pass, dn_pass, masks, base, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -63,7 +61,6 @@ inline WsLayout ws_layout(const xp_dims* d, int32_t max_rows) {
     L.entry = o;   o = align256(o + entries * sizeof(int32_t));
     L.gu_pass = o; o = align256(o + entries * 4 * sizeof(int32_t));
     L.dn_pass = o; o = align256(o + entries * 4 * sizeof(int32_t));
-    L.cnt = o;     o = align256(o + R * (size_t)(d->hidden / kTile) * sizeof(int32_t));
     L.masks = o;   o = align256(o + nblk * E * sizeof(uint64_t));
     L.base = o;    o = align256(o + nblk * E * sizeof(int32_t));
     L.total = o;
@@ -85,7 +82,6 @@ struct WsPtrs {
     int32_t* entry;
     int4* gu_pass;
     int4* dn_pass;
-    int32_t* cnt;   // combine arrivals per (row, column tile); zero between launches
     unsigned long long* masks;
     int32_t* base;
 };
@@ -95,7 +91,7 @@ inline WsPtrs ws_ptrs(void* ws, const xp_dims* d, int32_t rows) {
     char* b = (char*)ws;
     return WsPtrs{(int32_t*)(b + L.hdr),   (int32_t*)(b + L.count),  (int32_t*)(b + L.offset),
                   (int32_t*)(b + L.entry), (int4*)(b + L.gu_pass),   (int4*)(b + L.dn_pass),
-                  (int32_t*)(b + L.cnt),   (unsigned long long*)(b + L.masks), (int32_t*)(b + L.base)};
+                  (unsigned long long*)(b + L.masks), (int32_t*)(b + L.base)};
 }
 
 // Device view of one plan inside a workspace.
@@ -144,6 +140,34 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, 63);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), 63);
     return ((uint64_t)hi << 32) | lo;
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_self(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Largest / smallest unsigned 32-bit value over the wave, returned to every
+// lane. Lanes whose DPP source is outside the row keep their own value, which
+// max and min leave unchanged.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+    x = max(x, dpp_self<0x111, 0xF>(x));
+    x = max(x, dpp_self<0x112, 0xF>(x));
+    x = max(x, dpp_self<0x114, 0xF>(x));
+    x = max(x, dpp_self<0x118, 0xF>(x));
+    x = max(x, dpp_self<0x142, 0xA>(x));
+    x = max(x, dpp_self<0x143, 0xC>(x));
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+    x = min(x, dpp_self<0x111, 0xF>(x));
+    x = min(x, dpp_self<0x112, 0xF>(x));
+    x = min(x, dpp_self<0x114, 0xF>(x));
+    x = min(x, dpp_self<0x118, 0xF>(x));
+    x = min(x, dpp_self<0x142, 0xA>(x));
+    x = min(x, dpp_self<0x143, 0xC>(x));
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
 // Inclusive prefix sum over the wave's lanes.

@@ -8,19 +8,21 @@
 
 namespace xp {
 
-static Tiers g_tiers = {{2, 4, 6, 8, 0, 0, 0, 0}, 4, {2, 4, 0, 0, 0, 0, 0, 0}, 2};
+constexpr uint32_t kDefaultGu = (1u << 2) | (1u << 4) | (1u << 6) | (1u << 8);
+constexpr uint32_t kDefaultDn = (1u << 2) | (1u << 4);
+static Tiers g_tiers = {kDefaultGu, kDefaultDn};
 
 Tiers current_tiers() { return g_tiers; }
 
 // ---- up to 64 rows: one workgroup of 1024 threads does everything
 __global__ __launch_bounds__(1024) void route_small_kernel(const float* __restrict__ logits, int R, int E, int k,
                                                            int32_t* __restrict__ topk_id,
-                                                           float* __restrict__ topk_w, WsPtrs w, Tiers T,
-                                                           int n_cnt) {
+                                                           float* __restrict__ topk_w, WsPtrs w, Tiers T) {
     __shared__ unsigned long long smask[kMaxExperts];
     __shared__ int32_t sid[kSmallRows][kMaxTopK];
     __shared__ int32_t scnt[kMaxExperts];
     __shared__ int32_t soff[kMaxExperts + 1];
+    __shared__ int wsum[48];
     for (int e = threadIdx.x; e < E; e += blockDim.x) smask[e] = 0ull;
     __syncthreads();
     const int wave = threadIdx.x >> 6;
@@ -28,7 +30,7 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const float* __restri
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += blockDim.x) scnt[e] = __popcll(smask[e]);
     __syncthreads();
-    if (wave == 0) plan_wave(E, scnt, T, soff, w.gu_pass, w.dn_pass, w.count, w.offset, w.hdr, nullptr);
+    plan_block(E, scnt, T, soff, w.gu_pass, w.dn_pass, w.count, w.offset, w.hdr, nullptr, wsum);
     __syncthreads();
     const int t = threadIdx.x;
     if (t < R * k) {
@@ -37,7 +39,6 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const float* __restri
         const unsigned long long below = (r == 0) ? 0ull : (smask[e] & ((1ull << r) - 1ull));
         w.entry[soff[e] + __popcll(below)] = t;
     }
-    for (int i = threadIdx.x; i < n_cnt; i += blockDim.x) w.cnt[i] = 0;
 }
 
 // ---- more rows: (1) top-k and masks per 64-row block
@@ -62,6 +63,7 @@ __global__ __launch_bounds__(1024) void route_blocks_kernel(const float* __restr
 __global__ __launch_bounds__(1024) void route_plan_kernel(int E, int nblk, WsPtrs w, Tiers T) {
     __shared__ int32_t scnt[kMaxExperts];
     __shared__ int32_t soff[kMaxExperts + 1];
+    __shared__ int wsum[48];
     const int e = threadIdx.x;
     if (e < E) {
         int c = 0;
@@ -72,17 +74,14 @@ __global__ __launch_bounds__(1024) void route_plan_kernel(int E, int nblk, WsPtr
         scnt[e] = c;
     }
     __syncthreads();
-    if ((threadIdx.x >> 6) == 0) plan_wave(E, scnt, T, soff, w.gu_pass, w.dn_pass, w.count, w.offset, w.hdr, nullptr);
+    plan_block(E, scnt, T, soff, w.gu_pass, w.dn_pass, w.count, w.offset, w.hdr, nullptr, wsum);
 }
 
 // (3) scatter entries
 __global__ __launch_bounds__(1024) void route_scatter_kernel(int R, int E, int k, const int32_t* __restrict__ topk_id,
-                                                             WsPtrs w, int tiles_h) {
+                                                             WsPtrs w) {
     const int b = blockIdx.x;
     const int t = threadIdx.x;
-    // this block's rows' combine counters start at zero
-    const int r0 = b * kSmallRows, r1 = min(R, r0 + kSmallRows);
-    for (int i = r0 * tiles_h + t; i < r1 * tiles_h; i += blockDim.x) w.cnt[i] = 0;
     if (t >= kSmallRows * k) return;
     int rl = t / k, j = t - rl * k;
     int r = b * kSmallRows + rl;
@@ -112,14 +111,14 @@ XP_API size_t xp_workspace_bytes(const xp_dims* dims, int32_t max_rows) {
     return ws_layout(dims, max_rows).total;
 }
 
-XP_API int xp_workspace_layout(const xp_dims* dims, int32_t max_rows, size_t off[7]) {
+XP_API int xp_workspace_layout(const xp_dims* dims, int32_t max_rows, size_t off[6]) {
     int st = check_dims(dims);
     if (st != XP_OK) return st;
     if (!off) return XP_ERR_NULL;
     if (max_rows < 0) return XP_ERR_SHAPE;
     WsLayout L = ws_layout(dims, max_rows);
     off[0] = L.hdr; off[1] = L.count; off[2] = L.offset;
-    off[3] = L.entry; off[4] = L.gu_pass; off[5] = L.dn_pass; off[6] = L.cnt;
+    off[3] = L.entry; off[4] = L.gu_pass; off[5] = L.dn_pass;
     return XP_OK;
 }
 
@@ -136,7 +135,7 @@ XP_API int xp_route_bucket(const xp_dims* dims, int32_t rows, const float* logit
     WsPtrs w = ws_ptrs(workspace, dims, rows);
     if (rows <= kSmallRows) {
         hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(1024), 0, s, logits, rows, E, k, topk_id, topk_w, w,
-                           g_tiers, rows * (dims->hidden / kTile));
+                           g_tiers);
         return launch_status();
     }
     int nblk = (rows + kSmallRows - 1) / kSmallRows;
@@ -144,34 +143,37 @@ XP_API int xp_route_bucket(const xp_dims* dims, int32_t rows, const float* logit
     if (launch_status() != XP_OK) return XP_ERR_HIP;
     hipLaunchKernelGGL(route_plan_kernel, dim3(1), dim3(1024), 0, s, E, nblk, w, g_tiers);
     if (launch_status() != XP_OK) return XP_ERR_HIP;
-    hipLaunchKernelGGL(route_scatter_kernel, dim3(nblk), dim3(1024), 0, s, rows, E, k, (const int32_t*)topk_id, w,
-                       dims->hidden / kTile);
+    hipLaunchKernelGGL(route_scatter_kernel, dim3(nblk), dim3(1024), 0, s, rows, E, k, (const int32_t*)topk_id, w);
     return launch_status();
+}
+
+static uint32_t tier_mask(const int32_t* t, int32_t n) {
+    uint32_t m = 0;
+    for (int i = 0; i < n; ++i) m |= 1u << t[i];
+    return m;
+}
+
+static int tier_list(uint32_t m, int32_t* out) {
+    int n = 0;
+    for (int p = 2; p <= kMaxPass; ++p)
+        if (m & (1u << p)) out[n++] = p;
+    for (int i = n; i < 8; ++i) out[i] = 0;
+    return n;
 }
 
 XP_API int xp_set_tiers(const int32_t* gu, int32_t n_gu, const int32_t* dn, int32_t n_dn) {
     Tiers t = g_tiers;
     if (!gu || n_gu == 0) {
-        const int32_t d[4] = {2, 4, 6, 8};
-        memset(t.gu, 0, sizeof t.gu);
-        memcpy(t.gu, d, sizeof d);
-        t.n_gu = 4;
+        t.gu = kDefaultGu;
     } else {
         if (!tiers_valid(gu, n_gu)) return XP_ERR_TIERS;
-        memset(t.gu, 0, sizeof t.gu);
-        memcpy(t.gu, gu, sizeof(int32_t) * n_gu);
-        t.n_gu = n_gu;
+        t.gu = tier_mask(gu, n_gu);
     }
     if (!dn || n_dn == 0) {
-        const int32_t d[2] = {2, 4};
-        memset(t.dn, 0, sizeof t.dn);
-        memcpy(t.dn, d, sizeof d);
-        t.n_dn = 2;
+        t.dn = kDefaultDn;
     } else {
         if (!tiers_valid(dn, n_dn)) return XP_ERR_TIERS;
-        memset(t.dn, 0, sizeof t.dn);
-        memcpy(t.dn, dn, sizeof(int32_t) * n_dn);
-        t.n_dn = n_dn;
+        t.dn = tier_mask(dn, n_dn);
     }
     g_tiers = t;
     return XP_OK;
@@ -179,10 +181,8 @@ XP_API int xp_set_tiers(const int32_t* gu, int32_t n_gu, const int32_t* dn, int3
 
 XP_API int xp_get_tiers(int32_t* gu, int32_t* n_gu, int32_t* dn, int32_t* n_dn) {
     if (!gu || !n_gu || !dn || !n_dn) return XP_ERR_NULL;
-    memcpy(gu, g_tiers.gu, sizeof g_tiers.gu);
-    memcpy(dn, g_tiers.dn, sizeof g_tiers.dn);
-    *n_gu = g_tiers.n_gu;
-    *n_dn = g_tiers.n_dn;
+    *n_gu = tier_list(g_tiers.gu, gu);
+    *n_dn = tier_list(g_tiers.dn, dn);
     return XP_OK;
 }
 

@@ -14,63 +14,71 @@
 
 namespace xp {
 
-// Larger key = ranks earlier: logit order, then lower id. NaN -> order 0 (last).
-__device__ __forceinline__ uint64_t cand_key(float v, int id) {
+// Rank order of a logit as an unsigned key: larger logit = larger key, -0
+// equal to +0, NaN = 0 (after every number, -Inf included).
+__device__ __forceinline__ uint32_t logit_order(float v) {
     uint32_t u = __float_as_uint(v);
-    uint32_t o;
-    if (v != v) {
-        o = 0u;
-    } else {
-        if (u == 0x80000000u) u = 0u;  // -0 ties with +0
-        o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    }
-    return ((uint64_t)o << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id);
+    if (v != v) return 0u;
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ int key_id(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
-
-// The logit a key was made from (-0 comes back as +0, any NaN as a NaN).
-__device__ __forceinline__ float key_logit(uint64_t key) {
-    const uint32_t o = (uint32_t)(key >> 32);
+// The logit an order key was made from (-0 comes back as +0, NaN as a NaN).
+__device__ __forceinline__ float order_logit(uint32_t o) {
     if (o == 0u) return __builtin_nanf("");
     return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 
-// One wave selects row r's top-k by k rounds of a wave-wide maximum. Writes the
-// ids and the softmax weights (fp32: exp of each chosen logit minus the largest,
-// summed in slot order, one division) to global memory when topk_id is given,
-// the ids to sid[0..k) in LDS, and sets bit r_local of each chosen expert's mask.
-__device__ void topk_row(const float* __restrict__ logits, int E, int k, int r, int r_local,
-                         int32_t* __restrict__ topk_id, float* __restrict__ topk_w, int32_t* sid,
-                         unsigned long long* smask) {
+// One wave selects row r's top-k: k rounds, each taking the largest order over
+// the wave and, among the lanes holding it, the smallest expert id (so equal
+// logits go to the lower id and NaN comes last). Lane j keeps round j's pick.
+// Writes ids and softmax weights (fp32: exp of each chosen logit minus the
+// largest, summed in slot order, one division) to global memory when topk_id is
+// given, ids to sid[0..k) in LDS, and sets bit r_local of each chosen expert's mask.
+// CPL = candidates per lane (E <= 64 * CPL).
+template <int CPL>
+__device__ void topk_row_n(const float* __restrict__ logits, int E, int k, int r, int r_local,
+                           int32_t* __restrict__ topk_id, float* __restrict__ topk_w, int32_t* sid,
+                           unsigned long long* smask) {
     const int lane = threadIdx.x & 63;
     const float* lr = logits + (size_t)r * E;
-    const int cpl = (E + 63) >> 6;  // candidates per lane
-    uint64_t cand[kMaxExperts / 64];
+    float v[CPL];
 #pragma unroll
-    for (int i = 0; i < kMaxExperts / 64; ++i) {
+    for (int i = 0; i < CPL; ++i) {
         const int e = lane + 64 * i;
-        cand[i] = (i < cpl && e < E) ? cand_key(lr[e], e) : 0ull;
+        v[i] = lr[e < E ? e : E - 1];
     }
-    uint64_t mine = 0ull;  // lane j keeps the key chosen in round j
+    uint32_t ord[CPL];   // order keys of this lane's candidates
+    bool live[CPL];      // present and not yet taken
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        live[i] = lane + 64 * i < E;
+        ord[i] = logit_order(v[i]);
+    }
+    uint32_t mine_ord = 0u, mine_id = 0u;
     for (int j = 0; j < k; ++j) {
-        uint64_t best = 0ull;
+        // this lane's best live candidate: larger order, then smaller id
+        uint32_t bo = 0u, bi = 0xFFFFFFFFu;
+        bool any = false;
 #pragma unroll
-        for (int i = 0; i < kMaxExperts / 64; ++i)
-            if (i < cpl) best = cand[i] > best ? cand[i] : best;
-        best = wave_max_u64(best);
+        for (int i = 0; i < CPL; ++i) {
+            const uint32_t id = (uint32_t)(lane + 64 * i);
+            if (live[i] && (!any || ord[i] > bo)) { bo = ord[i]; bi = id; any = true; }
+        }
+        const uint32_t wo = wave_max_u32(any ? bo : 0u);
+        const uint32_t wi = wave_min_u32((any && bo == wo) ? bi : 0xFFFFFFFFu);
 #pragma unroll
-        for (int i = 0; i < kMaxExperts / 64; ++i)
-            if (i < cpl && cand[i] == best) cand[i] = 0ull;
-        if (lane == j) mine = best;
+        for (int i = 0; i < CPL; ++i)
+            if ((uint32_t)(lane + 64 * i) == wi) live[i] = false;
+        if (lane == j) { mine_ord = wo; mine_id = wi; }
     }
     // lane 0 holds the largest chosen logit; every lane j < k its own exp term
-    const float top = __uint_as_float((uint32_t)__builtin_amdgcn_readfirstlane((int)__float_as_uint(key_logit(mine))));
-    const float ex = expf(key_logit(mine) - top);
+    const float top = order_logit((uint32_t)__builtin_amdgcn_readfirstlane((int)mine_ord));
+    const float ex = expf(order_logit(mine_ord) - top);
     float s = 0.0f;
     for (int j = 0; j < k; ++j) s = s + __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(ex), j));
     if (lane < k) {
-        const int id = key_id(mine);
+        const int id = (int)mine_id;
         sid[lane] = id;
         if (topk_id) {
             topk_id[(size_t)r * k + lane] = id;
@@ -80,69 +88,78 @@ __device__ void topk_row(const float* __restrict__ logits, int E, int k, int r, 
     }
 }
 
-__device__ __forceinline__ int n_passes(int n, const int32_t* t, int nt) {
-    if (n <= 0) return 0;
-    if (n == 1) return 1;
-    int mx = t[nt - 1];
-    return n / mx + (n % mx != 0);
+__device__ __forceinline__ void topk_row(const float* __restrict__ logits, int E, int k, int r, int r_local,
+                                         int32_t* __restrict__ topk_id, float* __restrict__ topk_w, int32_t* sid,
+                                         unsigned long long* smask) {
+    if (E <= 64) topk_row_n<1>(logits, E, k, r, r_local, topk_id, topk_w, sid, smask);
+    else if (E <= 128) topk_row_n<2>(logits, E, k, r, r_local, topk_id, topk_w, sid, smask);
+    else if (E <= 256) topk_row_n<4>(logits, E, k, r, r_local, topk_id, topk_w, sid, smask);
+    else if (E <= 512) topk_row_n<8>(logits, E, k, r, r_local, topk_id, topk_w, sid, smask);
+    else topk_row_n<16>(logits, E, k, r, r_local, topk_id, topk_w, sid, smask);
 }
 
-__device__ void write_passes(int e, int n, int first, const int32_t* t, int nt, int4* out) {
+__device__ __forceinline__ int largest_tier(uint32_t t) { return 31 - __clz(t); }
+
+// Smallest allowed size holding `left` rows (left below the largest size).
+__device__ __forceinline__ int tier_at_least(uint32_t t, int left) { return __ffs(t & ~((1u << left) - 1u)) - 1; }
+
+__device__ __forceinline__ int n_passes(int n, uint32_t t) {
+    if (n <= 0) return 0;
+    if (n == 1) return 1;
+    const int mx = largest_tier(t);
+    return (n + mx - 1) / mx;
+}
+
+__device__ void write_passes(int e, int n, int first, uint32_t t, int4* out) {
     if (n <= 0) return;
     if (n == 1) {
         out[0] = make_int4(e, first, 1, 1);
         return;
     }
-    int mx = t[nt - 1];
+    const int mx = largest_tier(t);
     int left = n, i = 0;
     while (left > 0) {
-        int p = mx;
-        if (left < mx)
-            for (int q = 0; q < nt; ++q)
-                if (t[q] >= left) { p = t[q]; break; }
-        int real = left < p ? left : p;
+        const int p = left >= mx ? mx : tier_at_least(t, left);
+        const int real = left < p ? left : p;
         out[i++] = make_int4(e, first, real, p);
         first += real;
         left -= real;
     }
 }
 
-
-// Offsets and both pass lists from per-expert row counts cnt[e] (LDS), by one
-// wave: lane l takes a contiguous run of experts, so the scans are one wave
-// prefix sum each. Writes soff[0..E] (LDS), gu (LDS or global), and, when
-// given, dn, count, offset and the header in global memory.
-__device__ void plan_wave(int E, const int32_t* cnt, const Tiers& T, int32_t* soff, int4* gu, int4* dn,
-                          int32_t* count, int32_t* offset, int32_t* hdr, int32_t* n_gu_out) {
-    const int lane = threadIdx.x & 63;
-    const int epl = (E + 63) >> 6;
-    const int e0 = lane * epl;
-    const int e1 = min(E, e0 + epl);
-    int sc = 0, sg = 0, sd = 0;
-    for (int e = e0; e < e1; ++e) {
-        const int c = cnt[e];
-        sc += c;
-        sg += n_passes(c, T.gu, T.n_gu);
-        sd += n_passes(c, T.dn, T.n_dn);
+// Offsets and both pass lists from per-expert row counts cnt[e] (LDS). Thread
+// e (of a 1024-thread workgroup) takes expert e; the three exclusive scans are
+// wave prefix sums joined through LDS. Writes soff[0..E] (LDS), gu (LDS or
+// global), and, when given, dn, count, offset and the header in global memory;
+// *n_gu_out (LDS) gets the gate/up pass count. Every thread must call this.
+__device__ void plan_block(int E, const int32_t* cnt, const Tiers& T, int32_t* soff, int4* gu, int4* dn,
+                           int32_t* count, int32_t* offset, int32_t* hdr, int32_t* n_gu_out, int* wsum /*[48]*/) {
+    const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
+    const int c = e < E ? cnt[e] : 0;
+    const int pg = n_passes(c, T.gu), pd = n_passes(c, T.dn);
+    const int ic = wave_incl_sum(c), ig = wave_incl_sum(pg), id = wave_incl_sum(pd);
+    if (lane == 63) { wsum[3 * wave] = ic; wsum[3 * wave + 1] = ig; wsum[3 * wave + 2] = id; }
+    __syncthreads();
+    int bc = 0, bg = 0, bd = 0, tc = 0, tg = 0, td = 0;
+    const int nw = (blockDim.x + 63) >> 6;
+    for (int w = 0; w < nw; ++w) {
+        const int a0 = wsum[3 * w], a1 = wsum[3 * w + 1], a2 = wsum[3 * w + 2];
+        if (w < wave) { bc += a0; bg += a1; bd += a2; }
+        tc += a0; tg += a1; td += a2;
     }
-    const int ic = wave_incl_sum(sc), ig = wave_incl_sum(sg), id = wave_incl_sum(sd);
-    int oc = ic - sc, og = ig - sg, od = id - sd;
-    for (int e = e0; e < e1; ++e) {
-        const int c = cnt[e];
+    const int oc = bc + ic - c, og = bg + ig - pg, od = bd + id - pd;
+    if (e < E) {
         soff[e] = oc;
         if (count) count[e] = c;
         if (offset) offset[e] = oc;
-        write_passes(e, c, oc, T.gu, T.n_gu, gu + og);
-        if (dn) write_passes(e, c, oc, T.dn, T.n_dn, dn + od);
-        oc += c;
-        og += n_passes(c, T.gu, T.n_gu);
-        od += n_passes(c, T.dn, T.n_dn);
+        write_passes(e, c, oc, T.gu, gu + og);
+        if (dn) write_passes(e, c, oc, T.dn, dn + od);
     }
-    if (lane == 63) {
-        soff[E] = ic;
-        if (offset) offset[E] = ic;
-        if (hdr) { hdr[0] = ig; hdr[1] = id; }
-        if (n_gu_out) *n_gu_out = ig;
+    if (e == 0) {
+        soff[E] = tc;
+        if (offset) offset[E] = tc;
+        if (hdr) { hdr[0] = tg; hdr[1] = td; }
+        if (n_gu_out) *n_gu_out = tg;
     }
 }
 

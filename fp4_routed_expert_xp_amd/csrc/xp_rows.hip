@@ -23,6 +23,8 @@
 #include "xp_common.h"
 #include "xp_route_dev.h"
 
+#include <algorithm>
+
 namespace xp {
 
 // Two fp4 codes of byte `B` of `v` -> exact fp32 (low nibble first).
@@ -125,7 +127,7 @@ __device__ __forceinline__ void gu_leaf(gcodes_t cc, gbytes_t ss, const uint32_t
 }
 
 template <int P, bool SPLIT>
-__device__ void gu_item(const xp_expert* __restrict__ experts, const uint16_t* __restrict__ x,
+__device__ __forceinline__ void gu_item(const xp_expert* __restrict__ experts, const uint16_t* __restrict__ x,
                         const int32_t* __restrict__ entry, int4 ps, int tile, int H, int I, int k,
                         float* __restrict__ out0, float* __restrict__ out1, float* red) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -185,8 +187,9 @@ struct RouteIn {
 // Without ROUTE the plan comes from the workspace. With ROUTE (at most 64 rows)
 // every workgroup routes and plans the batch itself into LDS, so no separate
 // routing launch precedes this one; workgroup 0 also publishes the plan
-// (top-k, weights, entries, both pass lists, header) and clears the combine
-// counters for the down launch that follows.
+// (top-k, weights, entries, both pass lists, header) for the down launch that
+// follows. The grid is capped at two workgroups per CU, so each workgroup plans
+// once and then walks several items.
 template <bool SPLIT, bool ROUTE>
 __global__ __launch_bounds__(1024) void gateup_kernel(const xp_expert* __restrict__ experts,
                                                       const uint16_t* __restrict__ x,
@@ -207,6 +210,7 @@ __global__ __launch_bounds__(1024) void gateup_kernel(const xp_expert* __restric
         __shared__ int32_t sentry[kSmallRows * kMaxTopK];
         __shared__ int4 sgu[kSmallRows * kMaxTopK];
         __shared__ int32_t sn_gu;
+        __shared__ int wsum[48];
         const bool lead = blockIdx.x == 0;
         const int E = ri.E, R = ri.R;
         for (int e = threadIdx.x; e < E; e += blockDim.x) smask[e] = 0ull;
@@ -217,9 +221,8 @@ __global__ __launch_bounds__(1024) void gateup_kernel(const xp_expert* __restric
         __syncthreads();
         for (int e = threadIdx.x; e < E; e += blockDim.x) scnt[e] = __popcll(smask[e]);
         __syncthreads();
-        if (wave == 0)
-            plan_wave(E, scnt, ri.T, soff, sgu, lead ? ri.w.dn_pass : nullptr, lead ? ri.w.count : nullptr,
-                      lead ? ri.w.offset : nullptr, lead ? ri.w.hdr : nullptr, &sn_gu);
+        plan_block(E, scnt, ri.T, soff, sgu, lead ? ri.w.dn_pass : nullptr, lead ? ri.w.count : nullptr,
+                   lead ? ri.w.offset : nullptr, lead ? ri.w.hdr : nullptr, &sn_gu, wsum);
         __syncthreads();
         const int t = threadIdx.x;
         if (t < R * k) {
@@ -232,11 +235,8 @@ __global__ __launch_bounds__(1024) void gateup_kernel(const xp_expert* __restric
         }
         __syncthreads();
         n_pass = sn_gu;
-        if (lead) {
+        if (lead)
             for (int i = t; i < n_pass; i += blockDim.x) ri.w.gu_pass[i] = sgu[i];
-            const int n_cnt = R * (H / kTile);
-            for (int i = t; i < n_cnt; i += blockDim.x) ri.w.cnt[i] = 0;
-        }
         entry = sentry;
         passes = sgu;
     } else {
@@ -265,18 +265,10 @@ __global__ __launch_bounds__(1024) void gateup_kernel(const xp_expert* __restric
 
 // --------------------------------------------------------------------- down
 
-// Combine inputs for the fused down + combine launch (unused otherwise).
-struct CombineIn {
-    const float* topk_w;
-    float* y;
-    int32_t* cnt;
-    int k;
-};
-
-template <int P, bool COMBINE>
-__device__ void dn_item(const xp_expert* __restrict__ experts, const float* __restrict__ act,
+template <int P>
+__device__ __forceinline__ void dn_item(const xp_expert* __restrict__ experts, const float* __restrict__ act,
                         const int32_t* __restrict__ entry, int4 ps, int tile, int H, int I,
-                        float* __restrict__ out, float* red, const CombineIn& ci) {
+                        float* __restrict__ out, float* red) {
     constexpr int D = DnDepth<P>::value;
     const int leaf = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -343,39 +335,19 @@ __device__ void dn_item(const xp_expert* __restrict__ experts, const float* __re
     if (t < P * kTile) {
         const int r = t >> 6, c = t & 63;
         if (r < real) {
-            const int ent = entry[first + r];
             const float v = tree8(red + r * kTile + c, P * kTile);
-            out[(size_t)ent * H + (size_t)tile * kTile + c] = v;
-            if (COMBINE) {
-                // Wave r wrote this (row, slot, tile). The wave that brings the
-                // row's count to k sums the k slots in slot order, exactly as
-                // combine_kernel does, and resets the count for the next launch.
-                const int row = ent / ci.k;
-                int32_t* ctr = ci.cnt + (size_t)row * (H / kTile) + tile;
-                int old = 0;
-                if (c == 0) old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-                old = __builtin_amdgcn_readfirstlane(old);
-                if (old == ci.k - 1) {
-                    const float* o = out + (size_t)row * ci.k * H + (size_t)tile * kTile + c;
-                    const float* wr = ci.topk_w + (size_t)row * ci.k;
-                    float sum = 0.0f;
-                    for (int j = 0; j < ci.k; ++j) sum = __builtin_fmaf(wr[j], o[(size_t)j * H], sum);
-                    ci.y[(size_t)row * H + (size_t)tile * kTile + c] = sum;
-                    if (c == 0) *ctr = 0;
-                }
-            }
+            out[(size_t)entry[first + r] * H + (size_t)tile * kTile + c] = v;
         }
     }
     __syncthreads();
 }
 
-template <bool COMBINE>
 __global__ __launch_bounds__(512, 4) void down_kernel(const xp_expert* __restrict__ experts,
                                                       const float* __restrict__ act,
                                                       const int32_t* __restrict__ hdr,
                                                       const int32_t* __restrict__ entry,
                                                       const int4* __restrict__ passes, int H, int I,
-                                                      float* __restrict__ out, CombineIn ci) {
+                                                      float* __restrict__ out) {
     __shared__ float red[kLeaves * kMaxPass * kTile];
     const int n_tiles = H / kTile;
     const int n_items = hdr[1] * n_tiles;
@@ -384,14 +356,14 @@ __global__ __launch_bounds__(512, 4) void down_kernel(const xp_expert* __restric
         const int tile = item - pass * n_tiles;
         const int4 ps = passes[pass];
         switch (ps.w) {
-            case 1: dn_item<1, COMBINE>(experts, act, entry, ps, tile, H, I, out, red, ci); break;
-            case 2: dn_item<2, COMBINE>(experts, act, entry, ps, tile, H, I, out, red, ci); break;
-            case 3: dn_item<3, COMBINE>(experts, act, entry, ps, tile, H, I, out, red, ci); break;
-            case 4: dn_item<4, COMBINE>(experts, act, entry, ps, tile, H, I, out, red, ci); break;
-            case 5: dn_item<5, COMBINE>(experts, act, entry, ps, tile, H, I, out, red, ci); break;
-            case 6: dn_item<6, COMBINE>(experts, act, entry, ps, tile, H, I, out, red, ci); break;
-            case 7: dn_item<7, COMBINE>(experts, act, entry, ps, tile, H, I, out, red, ci); break;
-            case 8: dn_item<8, COMBINE>(experts, act, entry, ps, tile, H, I, out, red, ci); break;
+            case 1: dn_item<1>(experts, act, entry, ps, tile, H, I, out, red); break;
+            case 2: dn_item<2>(experts, act, entry, ps, tile, H, I, out, red); break;
+            case 3: dn_item<3>(experts, act, entry, ps, tile, H, I, out, red); break;
+            case 4: dn_item<4>(experts, act, entry, ps, tile, H, I, out, red); break;
+            case 5: dn_item<5>(experts, act, entry, ps, tile, H, I, out, red); break;
+            case 6: dn_item<6>(experts, act, entry, ps, tile, H, I, out, red); break;
+            case 7: dn_item<7>(experts, act, entry, ps, tile, H, I, out, red); break;
+            case 8: dn_item<8>(experts, act, entry, ps, tile, H, I, out, red); break;
             default: break;
         }
     }
@@ -423,26 +395,16 @@ static int gateup_common(const xp_dims* dims, int32_t rows, const uint16_t* x, c
     return launch_status();
 }
 
-static int down_common(const xp_dims* dims, int32_t rows, const float* act, const xp_expert* experts,
-                       const float* topk_w, void* ws, size_t ws_bytes, float* out, float* y, bool combine,
-                       void* stream) {
-    int st = check_dims(dims);
-    if (st != XP_OK) return st;
-    if (rows < 0) return XP_ERR_SHAPE;
-    if (rows == 0) return XP_OK;
-    if (!act || !experts || !ws || !out || (combine && (!topk_w || !y))) return XP_ERR_NULL;
-    if (ws_bytes < ws_layout(dims, rows).total) return XP_ERR_WORKSPACE;
-    Plan pl = plan_view(ws, dims, rows);
-    WsPtrs w = ws_ptrs(ws, dims, rows);
-    const int grid = grid_for(rows, dims->top_k, dims->hidden / kTile);
-    CombineIn ci{topk_w, y, w.cnt, dims->top_k};
-    if (combine)
-        hipLaunchKernelGGL(down_kernel<true>, dim3(grid), dim3(512), 0, (hipStream_t)stream, experts, act, pl.hdr,
-                           pl.entry, pl.dn_pass, dims->hidden, dims->inter, out, ci);
-    else
-        hipLaunchKernelGGL(down_kernel<false>, dim3(grid), dim3(512), 0, (hipStream_t)stream, experts, act, pl.hdr,
-                           pl.entry, pl.dn_pass, dims->hidden, dims->inter, out, ci);
-    return launch_status();
+static int fused_grid_cap() {
+    static int cap = 0;
+    if (cap == 0) {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        cap = 2 * cus;
+    }
+    return cap;
 }
 
 }  // namespace xp
@@ -461,7 +423,17 @@ XP_API int xp_gateup_rows_split(const xp_dims* dims, int32_t rows, const uint16_
 
 XP_API int xp_down_rows(const xp_dims* dims, int32_t rows, const float* act, const xp_expert* experts,
                         const void* workspace, size_t ws_bytes, float* out, void* stream) {
-    return down_common(dims, rows, act, experts, nullptr, (void*)workspace, ws_bytes, out, nullptr, false, stream);
+    int st = check_dims(dims);
+    if (st != XP_OK) return st;
+    if (rows < 0) return XP_ERR_SHAPE;
+    if (rows == 0) return XP_OK;
+    if (!act || !experts || !workspace || !out) return XP_ERR_NULL;
+    if (ws_bytes < ws_layout(dims, rows).total) return XP_ERR_WORKSPACE;
+    Plan pl = plan_view(workspace, dims, rows);
+    const int grid = grid_for(rows, dims->top_k, dims->hidden / kTile);
+    hipLaunchKernelGGL(down_kernel, dim3(grid), dim3(512), 0, (hipStream_t)stream, experts, act, pl.hdr, pl.entry,
+                       pl.dn_pass, dims->hidden, dims->inter, out);
+    return launch_status();
 }
 
 XP_API int xp_route_gateup(const xp_dims* dims, int32_t rows, const float* logits, const uint16_t* x,
@@ -481,7 +453,7 @@ XP_API int xp_route_gateup(const xp_dims* dims, int32_t rows, const float* logit
     }
     WsPtrs w = ws_ptrs(workspace, dims, rows);
     RouteIn ri{logits, rows, dims->n_experts, topk_id, topk_w, w, current_tiers()};
-    const int grid = grid_for(rows, dims->top_k, dims->inter / kTile);
+    const int grid = std::min(grid_for(rows, dims->top_k, dims->inter / kTile), fused_grid_cap());
     hipLaunchKernelGGL((gateup_kernel<false, true>), dim3(grid), dim3(1024), 0, (hipStream_t)stream, experts, x,
                        (const int32_t*)nullptr, (const int32_t*)nullptr, (const int4*)nullptr, ri, dims->hidden,
                        dims->inter, dims->top_k, act, (float*)nullptr);
@@ -491,5 +463,12 @@ XP_API int xp_route_gateup(const xp_dims* dims, int32_t rows, const float* logit
 XP_API int xp_down_combine(const xp_dims* dims, int32_t rows, const float* act, const xp_expert* experts,
                            const float* topk_w, void* workspace, size_t ws_bytes, float* out, float* y,
                            void* stream) {
-    return down_common(dims, rows, act, experts, topk_w, workspace, ws_bytes, out, y, true, stream);
+    int st = check_dims(dims);
+    if (st != XP_OK) return st;
+    if (rows < 0) return XP_ERR_SHAPE;
+    if (rows == 0) return XP_OK;
+    if (!topk_w || !y) return XP_ERR_NULL;
+    st = xp_down_rows(dims, rows, act, experts, workspace, ws_bytes, out, stream);
+    if (st != XP_OK) return st;
+    return xp_combine(dims, rows, out, topk_w, y, stream);
 }

@@ -125,7 +125,7 @@ def xp_workspace_bytes(d: xp_dims, max_rows: int) -> int:
 
 
 def xp_workspace_layout(d: xp_dims, max_rows: int) -> list:
-    off = (ctypes.c_size_t * 7)()
+    off = (ctypes.c_size_t * 6)()
     _check(lib().xp_workspace_layout(ctypes.byref(d), int(max_rows), off), "xp_workspace_layout")
     return list(off)
 

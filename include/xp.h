@@ -112,9 +112,8 @@ size_t xp_workspace_bytes(const xp_dims* dims, int32_t max_rows);
  *   off[3] entry  int32 [R*k]        row*k + slot, experts ascending, rows ascending
  *   off[4] gate/up passes int32 [R*k][4] = (expert, first entry, real rows, pass size)
  *   off[5] down passes    int32 [R*k][4]
- *   off[6] combine counts int32 [R][hidden/64] (zero between launches)
  * Returns XP_OK or an error for bad dims. */
-int xp_workspace_layout(const xp_dims* dims, int32_t max_rows, size_t off[7]);
+int xp_workspace_layout(const xp_dims* dims, int32_t max_rows, size_t off[6]);
 
 /* ----------------------------------------------------------- the four calls */
 
@@ -154,22 +153,18 @@ int xp_combine(const xp_dims* dims, int32_t rows, const float* out, const float*
                void* stream);
 
 /* ------------------------------------------------------------ fused calls
- * The same path in two launches instead of four, with the same bits. */
+ * The same path in fewer calls, with the same bits. */
 
 /* xp_route_bucket followed by xp_gateup_rows. With rows <= 64 this is one
- * launch: every workgroup routes and plans the batch itself, so no launch
- * boundary separates routing from the weight stream; the plan, topk_id and
- * topk_w are still written to the workspace and outputs. More rows run the
- * two calls. */
+ * launch: every workgroup routes and plans the batch itself (the grid is two
+ * workgroups per CU), so no launch boundary separates routing from the weight
+ * stream; the plan, topk_id and topk_w are still written to the workspace and
+ * outputs. More rows run the two calls. */
 int xp_route_gateup(const xp_dims* dims, int32_t rows, const float* logits, const uint16_t* x,
                     const xp_expert* experts, int32_t* topk_id, float* topk_w, void* workspace,
                     size_t ws_bytes, float* act, void* stream);
 
-/* xp_down_rows followed by xp_combine in one launch: for each (row, 64-column
- * tile) the down workgroup that writes the last of the row's k slots sums
- * them in slot order (the combine's arithmetic) into y. Uses the workspace's
- * combine counts, which xp_route_bucket / xp_route_gateup clear and this call
- * leaves cleared; calls on one workspace must not overlap. */
+/* xp_down_rows followed by xp_combine (two launches on the stream). */
 int xp_down_combine(const xp_dims* dims, int32_t rows, const float* act, const xp_expert* experts,
                     const float* topk_w, void* workspace, size_t ws_bytes, float* out, float* y,
                     void* stream);
