@@ -28,6 +28,36 @@ if ROOT not in sys.path:
 METRIC = "MoE decode rows/s + expert-weight HBM GB/s (% of peak), 1–16 rows/layer"
 HBM_PEAK_GBPS = 8000.0
 CUS, LANES, CLOCK_GHZ = 256, 64, 2.4     # fp32 vector fma lanes per CU per clock, unpacked
+CSRC = os.path.join(ROOT, "fp4_routed_expert_xp_amd", "csrc")
+
+# HBM bytes per launch of the roofline kernel (gateup_kernel<false,true>, one-row
+# workload), from two rocprofv3 --pmc runs: FETCH_SIZE, then WRITE_SIZE, in KiB per
+# dispatch (mean over the dispatches of that workload). Each is scaled by what the
+# same counter read for a plain 2 GiB device-to-device copy: FETCH_SIZE read
+# 1,048,590 KiB for 2,097,152 KiB fetched, WRITE_SIZE read exactly 2,097,152 KiB.
+# The figure belongs to the kernel sources it was taken on (their digest below);
+# after any change under csrc/ the bench reports traffic as null.
+TRAFFIC = dict(sources="e96c2614", fetch_kib=35018.4, write_kib=66.4,
+               fetch_factor=2097152 / 1048590.0, write_factor=1.0)
+
+
+def csrc_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        p = os.path.join(CSRC, name)
+        if os.path.isfile(p) and name.endswith((".hip", ".h", ".py")):
+            h.update(name.encode())
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:8]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the roofline kernel, or None once the sources changed."""
+    if csrc_digest() != TRAFFIC["sources"]:
+        return None
+    kib = TRAFFIC["fetch_kib"] * TRAFFIC["fetch_factor"] + TRAFFIC["write_kib"] * TRAFFIC["write_factor"]
+    return int(round(kib * 1024))
 
 
 def log(msg: str) -> None:
@@ -347,7 +377,7 @@ def main():
                      "achieved": round(achieved, 1), "bytes_per_launch": head["gateup_bytes"],
                      "launch_us": head["kernel_us"]["route_gateup"],
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic()},
         "copy_gbps": round(copy_gbps, 1),
         "wall_s_timed": round(th["wall_s"], 4),
         "cells": reports,
