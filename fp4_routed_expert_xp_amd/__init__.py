@@ -6,6 +6,6 @@ a C ABI, ``include/xp.h``); :mod:`fp4_routed_expert_xp_amd.xp` binds it.
 from . import xp  # noqa: F401
 from .xp import (  # noqa: F401
     XPError, dims, xp_combine, xp_down_combine, xp_down_rows, xp_gateup_rows, xp_gateup_rows_split,
-    xp_get_tiers, xp_pack_matrix, xp_route_bucket, xp_route_gateup, xp_set_tiers, xp_status_string,
+    xp_get_tiers, xp_pack_matrix, xp_prefill_down, xp_prefill_gateup, xp_route_bucket, xp_route_gateup, xp_set_tiers, xp_status_string,
     xp_workspace_bytes, xp_workspace_layout,
 )

@@ -22,6 +22,7 @@ EXPORTS = (
     "xp_pack_matrix", "xp_workspace_bytes", "xp_workspace_layout", "xp_route_bucket",
     "xp_gateup_rows", "xp_gateup_rows_split", "xp_down_rows", "xp_combine",
     "xp_set_tiers", "xp_get_tiers", "xp_status_string", "xp_route_gateup", "xp_down_combine",
+    "xp_prefill_gateup", "xp_prefill_down",
 )
 
 
@@ -68,13 +69,15 @@ def lib():
         L.xp_combine.argtypes = [D, i32, P, P, P, P]
         L.xp_route_gateup.argtypes = [D, i32, P, P, P, P, P, P, sz, P, P]
         L.xp_down_combine.argtypes = [D, i32, P, P, P, P, sz, P, P, P]
+        L.xp_prefill_gateup.argtypes = [D, i32, P, P, P, sz, P, P]
+        L.xp_prefill_down.argtypes = [D, i32, P, P, P, sz, P, P]
         L.xp_set_tiers.argtypes = [P, i32, P, i32]
         L.xp_get_tiers.argtypes = [P, P, P, P]
         L.xp_status_string.argtypes = [ctypes.c_int]
         L.xp_status_string.restype = ctypes.c_char_p
         for name in ("xp_pack_matrix", "xp_workspace_layout", "xp_route_bucket", "xp_gateup_rows",
                      "xp_gateup_rows_split", "xp_down_rows", "xp_combine", "xp_set_tiers", "xp_get_tiers",
-                     "xp_route_gateup", "xp_down_combine"):
+                     "xp_route_gateup", "xp_down_combine", "xp_prefill_gateup", "xp_prefill_down"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -240,6 +243,26 @@ def xp_down_combine(d: xp_dims, rows: int, act, experts, topk_w, workspace, out,
     nbytes = workspace.numel() if workspace is not None else 0
     _check(lib().xp_down_combine(ctypes.byref(d), int(rows), _ptr(act), _ptr(experts), _ptr(topk_w),
                                  _ptr(workspace), nbytes, _ptr(out), _ptr(y), _stream(stream)), "xp_down_combine")
+
+
+def xp_prefill_gateup(d: xp_dims, rows: int, x, experts, workspace, act, stream=None) -> None:
+    if rows > 0:
+        _dev_bf16(x, "x", rows * d.hidden)
+        _dev(experts, torch.int64, "experts", d.n_experts * 6)
+        _dev(act, torch.float32, "act", rows * d.top_k * d.inter)
+    nbytes = workspace.numel() if workspace is not None else 0
+    _check(lib().xp_prefill_gateup(ctypes.byref(d), int(rows), _ptr(x), _ptr(experts), _ptr(workspace), nbytes,
+                                   _ptr(act), _stream(stream)), "xp_prefill_gateup")
+
+
+def xp_prefill_down(d: xp_dims, rows: int, act, experts, workspace, out, stream=None) -> None:
+    if rows > 0:
+        _dev(act, torch.float32, "act", rows * d.top_k * d.inter)
+        _dev(experts, torch.int64, "experts", d.n_experts * 6)
+        _dev(out, torch.float32, "out", rows * d.top_k * d.hidden)
+    nbytes = workspace.numel() if workspace is not None else 0
+    _check(lib().xp_prefill_down(ctypes.byref(d), int(rows), _ptr(act), _ptr(experts), _ptr(workspace), nbytes,
+                                 _ptr(out), _stream(stream)), "xp_prefill_down")
 
 
 # -------------------------------------------------------------- conveniences

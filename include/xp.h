@@ -169,6 +169,30 @@ int xp_down_combine(const xp_dims* dims, int32_t rows, const float* act, const x
                     const float* topk_w, void* workspace, size_t ws_bytes, float* out, float* y,
                     void* stream);
 
+/* ---------------------------------------------------------- prefill chunk
+ * The same layer for a prompt chunk (thousands of rows, about a hundred per
+ * expert): gate/up and down as grouped bf16 matrix-core contractions over the
+ * plan of xp_route_bucket. Each weight (e2m1 code times its E4M3 scale) is
+ * exact in bf16 and x is bf16, so gate/up products are exact with fp32
+ * accumulation; act enters down as two bf16 halves (top 16 bits, then the top
+ * 16 bits of the remainder), about 16 significant bits. The summation order is
+ * the matrix cores', not the decode chain's: results are NOT bit-equal to
+ * xp_gateup_rows / xp_down_rows, and meet the per-row tolerance (max |err| /
+ * max |ref| <= 1e-3 against the float64 definition) instead. act must be
+ * finite for xp_prefill_down (an infinite act gives NaN in out). Any row count
+ * is accepted; xp_combine finishes the layer. [#2983, "What this changes" for
+ * the layer math; the 4,096-row prompt chunk is the serving page's default] */
+
+/* act[row][slot][I] fp32 = silu(W_gate x_row) * (W_up x_row) for every entry of
+ * the plan. x: [rows][H] bf16 bit patterns. Same buffers as xp_gateup_rows. */
+int xp_prefill_gateup(const xp_dims* dims, int32_t rows, const uint16_t* x, const xp_expert* experts,
+                      const void* workspace, size_t ws_bytes, float* act, void* stream);
+
+/* out[row][slot][H] fp32 = W_down act[row][slot] for every entry of the plan.
+ * Same buffers as xp_down_rows. */
+int xp_prefill_down(const xp_dims* dims, int32_t rows, const float* act, const xp_expert* experts,
+                    const void* workspace, size_t ws_bytes, float* out, void* stream);
+
 /* ------------------------------------------------------------ pass sizes */
 
 /* Set the pass sizes used by later xp_route_bucket calls (host, process-wide,

@@ -70,6 +70,8 @@ def test_bad_dims_rejected_before_any_launch(dims, status):
     assert L.xp_gateup_rows(ctypes.byref(d), 4, P, P, P, 1 << 30, P, None) == status
     assert L.xp_down_rows(ctypes.byref(d), 4, P, P, P, 1 << 30, P, None) == status
     assert L.xp_combine(ctypes.byref(d), 4, P, P, P, None) == status
+    assert L.xp_prefill_gateup(ctypes.byref(d), 4, P, P, P, 1 << 30, P, None) == status
+    assert L.xp_prefill_down(ctypes.byref(d), 4, P, P, P, 1 << 30, P, None) == status
 
 
 def test_null_rows_and_workspace_checks():
@@ -92,6 +94,13 @@ def test_null_rows_and_workspace_checks():
     assert L.xp_route_gateup(ctypes.byref(d), 4, P, P, P, P, P, P, need - 1, P, None) == xp.XP_ERR_WORKSPACE
     assert L.xp_down_combine(ctypes.byref(d), 4, P, P, None, P, need, P, P, None) == xp.XP_ERR_NULL
     assert L.xp_down_combine(ctypes.byref(d), 0, None, None, None, None, 0, None, None, None) == xp.XP_OK
+    assert L.xp_prefill_gateup(ctypes.byref(d), 0, None, None, None, 0, None, None) == xp.XP_OK
+    assert L.xp_prefill_down(ctypes.byref(d), 0, None, None, None, 0, None, None) == xp.XP_OK
+    assert L.xp_prefill_gateup(ctypes.byref(d), -1, P, P, P, need, P, None) == xp.XP_ERR_SHAPE
+    assert L.xp_prefill_gateup(ctypes.byref(d), 4, None, P, P, need, P, None) == xp.XP_ERR_NULL
+    assert L.xp_prefill_down(ctypes.byref(d), 4, P, P, P, need, None, None) == xp.XP_ERR_NULL
+    assert L.xp_prefill_gateup(ctypes.byref(d), 4, P, P, P, need - 1, P, None) == xp.XP_ERR_WORKSPACE
+    assert L.xp_prefill_down(ctypes.byref(d), 4, P, P, P, need - 1, P, None) == xp.XP_ERR_WORKSPACE
     assert L.xp_pack_matrix(100, 64, P, P, P, P, None) == xp.XP_ERR_SHAPE
     assert L.xp_pack_matrix(64, 48, P, P, P, P, None) == xp.XP_ERR_SHAPE
     assert L.xp_pack_matrix(64, 64, None, P, P, P, None) == xp.XP_ERR_NULL

@@ -1,0 +1,165 @@
+"""GPU: the prefill-chunk contraction (xp_prefill_gateup, xp_prefill_down) against the oracle.
+
+The matrix-core path sums in another order than the decode chain, so it is held
+to the per-row tolerance against the float64 oracle (max |gpu - ref| / max |ref|
+<= 1e-3 over each row's entries of act, out and y) and not to bit equality.
+Small widths cover several 128-row blocks per expert with ragged tails, a
+column count that leaves half of the last 128-column block empty, and single
+rows; the 4,096-row chunk at release widths is checked on sampled rows (routing
+and the plan for every row) since the oracle cannot finish the whole chunk in
+seconds.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from fp4_routed_expert_xp_amd import xp
+
+from gpu_helpers import DeviceLayer, log, read_plan, rel_err_rows, to_dev
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+TINY = synth.CONFIGS["tiny"]
+# 384 intermediate columns: three 128-column blocks for gate/up, the last one half empty.
+MID = dataclasses.replace(TINY, name="mid", H=512, I=384, E=16, k=4, seed=1101, weight_seed=1101)
+PREFILL = synth.CONFIGS["prefill"]
+
+
+def run_prefill(layer: DeviceLayer, x_bits, logits) -> dict:
+    d = layer.d
+    R = x_bits.shape[0]
+    k, H, I = d.top_k, d.hidden, d.inter
+    x = to_dev(x_bits)
+    lg = to_dev(logits.astype(np.float32))
+    ws = torch.zeros(max(xp.xp_workspace_bytes(d, R), 256), dtype=torch.uint8, device="cuda")
+    nan = float("nan")
+    topk_id = torch.full((R, k), -1, dtype=torch.int32, device="cuda")
+    topk_w = torch.full((R, k), nan, dtype=torch.float32, device="cuda")
+    act = torch.full((R, k, I), nan, dtype=torch.float32, device="cuda")
+    out = torch.full((R, k, H), nan, dtype=torch.float32, device="cuda")
+    y = torch.full((R, H), nan, dtype=torch.float32, device="cuda")
+    xp.xp_route_bucket(d, R, lg, topk_id, topk_w, ws)
+    xp.xp_prefill_gateup(d, R, x, layer.table, ws, act)
+    xp.xp_prefill_down(d, R, act, layer.table, ws, out)
+    xp.xp_combine(d, R, out, topk_w, y)
+    torch.cuda.synchronize()
+    return dict(topk_id=topk_id.cpu().numpy(), topk_w=topk_w.cpu().numpy(), act=act.cpu().numpy(),
+                out=out.cpu().numpy(), y=y.cpu().numpy(), ws=ws.cpu().numpy())
+
+
+def oracle_rows(layer: DeviceLayer, x, lg):
+    ids, _ = oracle.route(lg, layer.cfg.k)
+    ex = {int(e): layer.host_expert(int(e)) for e in np.unique(ids)}
+    return oracle.layer(x, lg, ex, layer.cfg.H, layer.cfg.I, layer.cfg.E, layer.cfg.k)
+
+
+def check_rows(res, ref, rows=None):
+    sel = slice(None) if rows is None else rows
+    assert np.array_equal(res["topk_id"][sel], ref["topk_id"])
+    for name in ("act", "out", "y"):
+        got = res[name][sel]
+        assert np.all(np.isfinite(got)), name
+        err = rel_err_rows(got, ref[name])
+        assert np.all(err <= TOL), (name, float(err.max()), int(err.argmax()))
+    return max(float(rel_err_rows(res[n][sel], ref[n]).max()) for n in ("act", "out", "y"))
+
+
+@pytest.fixture(scope="module")
+def tiny_layer():
+    return DeviceLayer(TINY, 0)
+
+
+@pytest.fixture(scope="module")
+def mid_layer():
+    return DeviceLayer(MID, 0)
+
+
+@pytest.mark.parametrize("R", [1, 3, 64, 300, 1000])
+def test_tiny_prefill_matches_oracle(tiny_layer, R):
+    # 8 experts, top-2: R = 1000 puts about 250 rows on each expert (two full
+    # 128-row blocks and a ragged third).
+    log("prefill tiny R=%d" % R)
+    x = synth.activations(TINY.seed, 100 + R, R, TINY.H)
+    lg = synth.logits(TINY.seed, 100 + R, R, TINY.E)
+    res = run_prefill(tiny_layer, x, lg)
+    ref = oracle_rows(tiny_layer, x, lg)
+    worst = check_rows(res, ref)
+    log("  worst per-row relative error %.2e" % worst)
+
+
+@pytest.mark.parametrize("R", [2, 129, 517])
+def test_mid_prefill_matches_oracle(mid_layer, R):
+    log("prefill mid R=%d" % R)
+    x = synth.activations(MID.seed, R, R, MID.H)
+    lg = synth.logits(MID.seed, R, R, MID.E, bias_sigma=0.5)
+    res = run_prefill(mid_layer, x, lg)
+    ref = oracle_rows(mid_layer, x, lg)
+    worst = check_rows(res, ref)
+    log("  worst per-row relative error %.2e" % worst)
+
+
+def test_prefill_skewed_expert(tiny_layer):
+    # Every row on experts 0 and 1 (one expert with all R rows in slot 0):
+    # ten full blocks and a tail of 5.
+    R = 1285
+    log("prefill tiny skewed R=%d" % R)
+    x = synth.activations(TINY.seed, 7, R, TINY.H)
+    lg = np.full((R, TINY.E), -4.0, dtype=np.float32)
+    lg[:, 0] = 3.0
+    lg[:, 1] = 2.0 + 0.001 * np.arange(R, dtype=np.float32) / R
+    res = run_prefill(tiny_layer, x, lg)
+    ref = oracle_rows(tiny_layer, x, lg)
+    check_rows(res, ref)
+
+
+def test_prefill_empty_and_errors(tiny_layer):
+    d = tiny_layer.d
+    xp.xp_prefill_gateup(d, 0, None, tiny_layer.table, None, None)
+    xp.xp_prefill_down(d, 0, None, tiny_layer.table, None, None)
+    ws = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    x = torch.zeros((4, d.hidden), dtype=torch.int16, device="cuda")
+    act = torch.zeros((4, d.top_k, d.inter), dtype=torch.float32, device="cuda")
+    with pytest.raises(xp.XPError) as ei:
+        xp.xp_prefill_gateup(d, 4, x, tiny_layer.table, ws, act)
+    assert ei.value.status == xp.XP_ERR_WORKSPACE
+
+
+@pytest.fixture(scope="module")
+def prefill_layer():
+    log("materialising release-width layer 0 (256 experts) for the prefill chunk")
+    return DeviceLayer(PREFILL, 0)
+
+
+def test_prefill_chunk_release_width(prefill_layer):
+    """4,096 rows, 256 experts, top-8, logits with a per-expert bias (sigma 0.5).
+
+    Routing, counts, offsets and entries are bit-exact for every row; act, out
+    and y are compared with the float64 oracle on sampled rows, among them the
+    rows in the last (ragged) block of the most loaded expert.
+    """
+    cfg = PREFILL
+    x, lg = synth.layer_inputs(cfg, 0)
+    log("prefill chunk: R=%d" % cfg.R)
+    res = run_prefill(prefill_layer, x, lg)
+    ids, w = oracle.route(lg, cfg.k)
+    assert np.array_equal(res["topk_id"], ids)
+    count, offset, entry = oracle.bucket(ids, cfg.E)
+    plan = read_plan(prefill_layer.d, cfg.R, res["ws"])
+    assert np.array_equal(plan["count"], count)
+    assert np.array_equal(plan["offset"], offset)
+    assert np.array_equal(plan["entry"], entry)
+    for name in ("act", "out", "y"):
+        assert np.all(np.isfinite(res[name])), name
+    busiest = int(np.argmax(count))
+    log("  busiest expert %d with %d rows; %d experts routed" % (busiest, count[busiest], int((count > 0).sum())))
+    tail = entry[offset[busiest + 1] - 1] // cfg.k
+    rng = np.random.default_rng(5)
+    rows = sorted(set([0, cfg.R - 1, int(tail)] + [int(r) for r in rng.integers(0, cfg.R, 3)]))
+    ref = oracle_rows(prefill_layer, x[rows], lg[rows])
+    worst = check_rows(res, ref, rows)
+    log("  sampled rows %s: worst per-row relative error %.2e" % (rows, worst))
