@@ -70,7 +70,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--layers", type=int, default=40)
-    ap.add_argument("--cells", default="one_row,four_same,sixteen_random")
+    ap.add_argument("--cells", default="one_row,four_same,sixteen_random,prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU work budget of the oracle sample")
     return ap.parse_args()
@@ -168,6 +168,10 @@ class Cell:
             xp.xp_route_gateup(d, R, self.logits[l], self.x[l], tab, self.topk_id, self.topk_w, ws, self.act)
         elif kind == "down_combine":
             xp.xp_down_combine(d, R, self.act, tab, self.topk_w, ws, self.out, self.y)
+        elif kind == "prefill_gateup":
+            xp.xp_prefill_gateup(d, R, self.x[l], tab, ws, self.act)
+        elif kind == "prefill_down":
+            xp.xp_prefill_down(d, R, self.act, tab, ws, self.out)
         else:
             raise ValueError(kind)
 
@@ -195,7 +199,10 @@ class Cell:
         return dict(distinct=distinct, gu_rows=gu_rows, dn_rows=dn_rows)
 
 
-PATHS = {"four_calls": ("route", "gateup", "down", "combine"), "two_calls": ("route_gateup", "down_combine")}
+PATHS = {"four_calls": ("route", "gateup", "down", "combine"), "two_calls": ("route_gateup", "down_combine"),
+         "prefill": ("route", "prefill_gateup", "prefill_down", "combine")}
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PREFILL_LAYERS = 4               # prefill cells rotate over this many layers (3.4 GB of weights each)
 
 
 def _graph(fn):
@@ -290,6 +297,33 @@ def cell_report(cell: Cell, t: dict, copy_gbps: float) -> dict:
     )
 
 
+def prefill_report(cell: Cell, t: dict) -> dict:
+    """The prompt chunk on the matrix-core path: algorithmic flops are 6*H*I per
+    (row, slot) pair (gate and up 2*H*I each, down 2*H*I); the down contraction
+    runs twice (act as bf16 hi and lo), which the flop count does not include."""
+    cfg = cell.cfg
+    st = cell.plan_stats()
+    L = cell.layers
+    H, I, k, R = cfg.H, cfg.I, cfg.k, cfg.R
+    pairs = R * k
+    layer_ms = t["ms_per_round"] / L
+    flops = 6.0 * H * I * pairs
+    gu_us, dn_us = t["kernel_us"]["prefill_gateup"], t["kernel_us"]["prefill_down"]
+    gu_tf = 4.0 * H * I * pairs / (gu_us * 1e-6) / 1e12
+    dn_tf = 2.0 * H * I * pairs / (dn_us * 1e-6) / 1e12
+    tf = flops / (layer_ms * 1e-3) / 1e12
+    return dict(
+        workload=cfg.name, path=t["path"], rows=R, layers=L, round_ms=round(t["ms_per_round"], 4),
+        layer_ms=round(layer_ms, 4), rows_per_s=round(R / (layer_ms * 1e-3), 1),
+        distinct_experts=round(sum(st["distinct"]) / L, 2),
+        tflop_per_layer=round(flops / 1e12, 4), tflops=round(tf, 1),
+        pct_mfma_peak=round(100 * tf / MFMA_BF16_PEAK_TFLOPS, 2),
+        kernel_us={kk: round(v, 2) for kk, v in t["kernel_us"].items()},
+        gateup_tflops=round(gu_tf, 1), down_tflops=round(dn_tf, 1),
+        weight_gbps=round(sum(st["distinct"]) / L * cfg.expert_bytes / (layer_ms * 1e-3) / 1e9, 1),
+    )
+
+
 # ------------------------------------------------------------ CPU baseline
 def cpu_baseline(budget_s: float) -> dict:
     """The float64 oracle, untuned, on this host's cores: one-row layers of the
@@ -343,6 +377,15 @@ def main():
     reports, timings = {}, {}
     for name in cells:
         cfg = synth.CONFIGS[name]
+        if name == "prefill":
+            cell = Cell(model, cfg, min(args.layers, PREFILL_LAYERS))
+            t = time_cell(cell, "prefill", args.steps, args.warmup)
+            key = "prefill/prefill"
+            timings[key] = t
+            reports[key] = prefill_report(cell, t)
+            log("%s: %s" % (key, json.dumps(reports[key])))
+            del cell
+            continue
         cell = Cell(model, cfg, args.layers)
         for path in ("two_calls", "four_calls"):
             t = time_cell(cell, path, args.steps, args.warmup)
@@ -350,7 +393,11 @@ def main():
             timings[key] = t
             reports[key] = cell_report(cell, t, copy_gbps)
             log("%s: %s" % (key, json.dumps(reports[key])))
-    head_key = "%s/two_calls" % cells[0]
+    decode = [c for c in cells if c != "prefill"]
+    if not decode:
+        log("the headline is a decode workload: name one of one_row, four_same, sixteen_random in --cells")
+        sys.exit(2)
+    head_key = "%s/two_calls" % decode[0]
     head = reports[head_key]
     th = timings[head_key]
     achieved = head["gateup_gbps"]
@@ -369,7 +416,7 @@ def main():
         "data": "synthetic (seeded fp4 e2m1 codes, E4M3 2^U{-6..0} scales, bf16 N(0,1) x, N(0,1) logits)",
         "config": {"workload": "%s: %d-row decode through a %d-layer round of independent layers, hidden %d, "
                                "intermediate %d, %d experts, top-%d; two launches per layer "
-                               "(xp_route_gateup, xp_down_combine)" % (cells[0], head["rows"], args.layers,
+                               "(xp_route_gateup, xp_down_combine)" % (decode[0], head["rows"], args.layers,
                                                                         base.H, base.I, base.E, base.k),
                    "rows": head["rows"], "layers": args.layers, "hidden": base.H, "inter": base.I,
                    "experts": base.E, "top_k": base.k, "path": "two_calls"},
@@ -382,6 +429,14 @@ def main():
         "wall_s_timed": round(th["wall_s"], 4),
         "cells": reports,
     }
+    if "prefill/prefill" in reports:
+        pf = reports["prefill/prefill"]
+        cfg = synth.CONFIGS["prefill"]
+        line["prefill_roofline"] = {
+            "kernel": "prefill_gateup_kernel (xp_prefill_gateup)", "bound": "mfma",
+            "achieved": pf["gateup_tflops"], "flops_per_launch": 4 * cfg.H * cfg.I * cfg.R * cfg.k,
+            "launch_us": pf["kernel_us"]["prefill_gateup"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(pf["gateup_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

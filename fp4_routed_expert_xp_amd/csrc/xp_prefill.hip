@@ -135,9 +135,182 @@ __device__ __forceinline__ Deal deal(int total) {
 }
 
 // ------------------------------------------------------------------ gate/up
+// The K loop is software-pipelined over 32-wide groups: each wave keeps the
+// weight words and scale bytes of the next D groups in flight (a register
+// ring), each thread keeps the activations of the next kDA groups in flight and
+// stages one group ahead in LDS, and the weights of group g+1 are decoded while
+// group g's matrix instructions run. The loop body has no branches (D divides
+// the group count; refills past the end re-read the last group), so the
+// compiler's wait counts follow the ring exactly. NS = 16-row slabs computed:
+// the item's rows rounded up to 2, 4, 6 or 8 slabs.
+constexpr int kDA = 4;  // activation groups in flight per thread
+
+// Scheduling hint for one pipelined step: after the step's LDS reads, issue the
+// matrix instructions one at a time with VALU work (the next group's decode,
+// the activation split) slotted between them, so both units stay busy.
+template <int NMFMA, int NVALU>
+__device__ __forceinline__ void interleave_step() {
+    __builtin_amdgcn_sched_group_barrier(0x100, 32, 0);  // LDS reads
+#pragma unroll
+    for (int i = 0; i < NMFMA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                         // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, (NVALU + NMFMA - 1) / NMFMA, 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                         // a global load
+    }
+}
+
+struct GuArgs {
+    const uint16_t* x;
+    const xp_expert* experts;
+    float* act;
+    int k, H, I, G;
+};
+
+template <int NS, int D>
+__device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint16_t (*sA)[kPM * kAStride],
+                                        const int* sEntry) {
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int G = a.G, H = a.H, I = a.I;
+
+    // Activation rows staged by all threads: row t/2, 16 bf16 at k offset (t&1)*16.
+    const int arow = t >> 1, acol = (t & 1) * 16;
+    const u32x4v* xrow = (const u32x4v*)(a.x + (size_t)(sEntry[arow] / a.k) * H + acol);
+    u32x4v ra[kDA][2];
+
+    // This wave's columns: packed tile pt, columns c0 .. c0+31 of it. A wave past
+    // the last tile (I not a multiple of 128) reads tile 0 and stores nothing.
+    const int pt_raw = it.nt * 2 + (wave >> 1);
+    const bool live = pt_raw * 64 < I;
+    const int pt = live ? pt_raw : 0;
+    const int c0 = (wave & 1) * 32;
+    const xp_expert ex = a.experts[it.e];
+    const int col = c0 + (lane & 15);  // column of the first 16-column MFMA tile
+    const int word = lane >> 4;        // which 8 k of the 32-group this lane decodes
+    gwords_t gc = (gwords_t)(ex.gate_codes) + (size_t)pt * G * 256 + col * 4 + word;
+    gwords_t uc = (gwords_t)(ex.up_codes) + (size_t)pt * G * 256 + col * 4 + word;
+    gbytes1_t gs = (gbytes1_t)(ex.gate_scales) + (size_t)pt * G * 64 + col;
+    gbytes1_t us = (gbytes1_t)(ex.up_scales) + (size_t)pt * G * 64 + col;
+    uint32_t bc[D][4], bs[D][4];
+    auto load_b = [&](int slot, int g) {
+        g = min(g, G - 1);
+        bc[slot][0] = gc[g * 256];
+        bc[slot][1] = gc[g * 256 + 64];  // 16 columns on: +64 words, +16 scale bytes
+        bc[slot][2] = uc[g * 256];
+        bc[slot][3] = uc[g * 256 + 64];
+        bs[slot][0] = gs[g * 64];
+        bs[slot][1] = gs[g * 64 + 16];
+        bs[slot][2] = us[g * 64];
+        bs[slot][3] = us[g * 64 + 16];
+    };
+    auto load_a = [&](int slot, int g) {
+        g = min(g, G - 1);
+        ra[slot][0] = xrow[4 * g];
+        ra[slot][1] = xrow[4 * g + 1];
+    };
+    auto store_a = [&](int buf, int slot) {
+        u32x4v* q = (u32x4v*)(&sA[buf][arow * kAStride + acol]);
+        q[0] = ra[slot][0];
+        q[1] = ra[slot][1];
+    };
+    bf16x8 bf[2][4];
+    auto decode_b = [&](int buf, int slot) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) bf[buf][q] = decode8(bc[slot][q], e4m3f(bs[slot][q]));
+    };
+
+    f32x4 acc[NS][2][2];
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            acc[s][c][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+            acc[s][c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+
+#pragma unroll
+    for (int u = 0; u < D; ++u) load_b(u, u);
+#pragma unroll
+    for (int u = 0; u < kDA; ++u) load_a(u, u);
+    store_a(0, 0);
+    load_a(0, kDA);
+    decode_b(0, 0);
+    load_b(0, D);
+    __syncthreads();
+
+    for (int g0 = 0; g0 < G; g0 += D) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+            const int g = g0 + u;
+            const int cur = u & 1;
+            const uint16_t* a_lds = &sA[cur][(lane & 15) * kAStride + word * 8];
+            bf16x8 af[NS];
+#pragma unroll
+            for (int s = 0; s < NS; ++s) af[s] = *(const bf16x8*)(a_lds + s * 16 * kAStride);
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                acc[s][0][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s], bf[cur][0], acc[s][0][0], 0, 0, 0);
+                acc[s][1][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s], bf[cur][1], acc[s][1][0], 0, 0, 0);
+                acc[s][0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s], bf[cur][2], acc[s][0][1], 0, 0, 0);
+                acc[s][1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s], bf[cur][3], acc[s][1][1], 0, 0, 0);
+            }
+            // next group's weights: decode now (overlaps the matrix work), refill the ring
+            const int nslot = (u + 1) % D;
+            decode_b(cur ^ 1, nslot);
+            load_b(nslot, g + 1 + D);
+            // next group's activations into the other LDS buffer, refill the ring
+            const int aslot = (u + 1) % kDA;
+            store_a(cur ^ 1, aslot);
+            load_a(aslot, g + 1 + kDA);
+            __syncthreads();
+        }
+    }
+
+    if (live) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = s * 16 + (lane >> 4) * 4 + r;
+                    if (row < it.rows) {
+                        const float gv = acc[s][c][0][r], uv = acc[s][c][1][r];
+                        a.act[(size_t)sEntry[row] * I + pt * 64 + c0 + c * 16 + (lane & 15)] =
+                            (gv / (1.0f + expf(-gv))) * uv;
+                    }
+                }
+            }
+        }
+    }
+}
+
+// Slab count class (2, 4, 6 or 8) and ring depth (8, 4 or 1: the largest that
+// divides the group count), then the item.
+template <typename F>
+__device__ __forceinline__ void dispatch_item(int rows, int G, F&& f) {
+    const int slabs = (rows + 15) >> 4;
+    const int ns = slabs <= 2 ? 2 : slabs <= 4 ? 4 : slabs <= 6 ? 6 : 8;
+    const int d = (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : 1;
+#define XP_PF_CASE(NS_, D_) \
+    if (ns == NS_ && d == D_) { f.template run<NS_, D_>(); return; }
+    XP_PF_CASE(2, 8) XP_PF_CASE(4, 8) XP_PF_CASE(6, 8) XP_PF_CASE(8, 8)
+    XP_PF_CASE(2, 4) XP_PF_CASE(4, 4) XP_PF_CASE(6, 4) XP_PF_CASE(8, 4)
+    XP_PF_CASE(2, 1) XP_PF_CASE(4, 1) XP_PF_CASE(6, 1) XP_PF_CASE(8, 1)
+#undef XP_PF_CASE
+}
+
+struct GuRun {
+    const GuArgs& a;
+    const Item& it;
+    uint16_t (*sA)[kPM * kAStride];
+    const int* sEntry;
+    template <int NS, int D>
+    __device__ __forceinline__ void run() const { gu_item<NS, D>(a, it, sA, sEntry); }
+};
+
 // act[entry][n] = silu(g) * u for the item's rows and columns, where g and u
 // are the rows' products with gate and up (K = hidden).
-__global__ __launch_bounds__(kPThreads, 2) void prefill_gateup_kernel(
+__global__ __launch_bounds__(kPThreads, 1) void prefill_gateup_kernel(
     const xp_expert* __restrict__ experts, const uint16_t* __restrict__ x, const int32_t* __restrict__ count,
     const int32_t* __restrict__ offset, const int32_t* __restrict__ entry, int E, int k, int H, int I,
     float* __restrict__ act) {
@@ -146,107 +319,167 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_gateup_kernel(
     __shared__ int sP[kMaxExperts + 1];
     __shared__ int swave[4];
 
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int t = threadIdx.x;
     const int n_tiles = (I + kPN - 1) / kPN;
     const int total = block_prefix(count, E, sP, swave) * n_tiles;
-    const int G = H / 32;
+    const GuArgs a{x, experts, act, k, H, I, H / 32};
     const Deal dl = deal(total);
 
     for (int i = dl.first; i < dl.end; i += dl.step) {
         const Item it = item_at(i, n_tiles, sP, E, count);
         if (t < kPM) sEntry[t] = entry[offset[it.e] + it.m0 + min(t, it.rows - 1)];
         __syncthreads();
-
-        // Activation rows staged by all threads: row t/2, 16 bf16 at k offset (t&1)*16.
-        const int arow = t >> 1, acol = (t & 1) * 16;
-        const uint16_t* xrow = x + (size_t)(sEntry[arow] / k) * H + acol;
-        u32x4v ra0, ra1;
-        auto load_a = [&](int g) {
-            const u32x4v* p = (const u32x4v*)(xrow + 32 * g);
-            ra0 = p[0];
-            ra1 = p[1];
-        };
-        auto store_a = [&](int buf) {
-            u32x4v* q = (u32x4v*)(&sA[buf][arow * kAStride + acol]);
-            q[0] = ra0;
-            q[1] = ra1;
-        };
-
-        // This wave's columns: packed tile pt, columns c0 .. c0+31 of it.
-        const int pt = it.nt * 2 + (wave >> 1);
-        const int c0 = (wave & 1) * 32;
-        const bool live = pt * 64 < I;
-        const xp_expert ex = experts[it.e];
-        const int col = c0 + (lane & 15);  // column in the packed tile for the first 16-column MFMA tile
-        const int word = lane >> 4;        // which 8 k of the 32-group this lane decodes
-        gwords_t gc = (gwords_t)(ex.gate_codes) + (size_t)pt * G * 256 + col * 4 + word;
-        gwords_t uc = (gwords_t)(ex.up_codes) + (size_t)pt * G * 256 + col * 4 + word;
-        gbytes1_t gs = (gbytes1_t)(ex.gate_scales) + (size_t)pt * G * 64 + col;
-        gbytes1_t us = (gbytes1_t)(ex.up_scales) + (size_t)pt * G * 64 + col;
-
-        f32x4 acc[8][2][2];
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                acc[s][c][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-                acc[s][c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-        const int slabs = (it.rows + 15) >> 4;
-
-        load_a(0);
-        store_a(0);
-        __syncthreads();
-        for (int g = 0; g < G; ++g) {
-            if (g + 1 < G) load_a(g + 1);
-            if (live) {
-                // 16 columns apart: +64 words of codes, +16 scale bytes.
-                const uint32_t cg0 = gc[g * 256], cg1 = gc[g * 256 + 64];
-                const uint32_t cu0 = uc[g * 256], cu1 = uc[g * 256 + 64];
-                const float sg0 = e4m3f(gs[g * 64]), sg1 = e4m3f(gs[g * 64 + 16]);
-                const float su0 = e4m3f(us[g * 64]), su1 = e4m3f(us[g * 64 + 16]);
-                const bf16x8 bg0 = decode8(cg0, sg0), bg1 = decode8(cg1, sg1);
-                const bf16x8 bu0 = decode8(cu0, su0), bu1 = decode8(cu1, su1);
-                const uint16_t* a_lds = &sA[g & 1][(lane & 15) * kAStride + word * 8];
-#pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    if (s < slabs) {
-                        const bf16x8 a = *(const bf16x8*)(a_lds + s * 16 * kAStride);
-                        acc[s][0][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bg0, acc[s][0][0], 0, 0, 0);
-                        acc[s][1][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bg1, acc[s][1][0], 0, 0, 0);
-                        acc[s][0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bu0, acc[s][0][1], 0, 0, 0);
-                        acc[s][1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bu1, acc[s][1][1], 0, 0, 0);
-                    }
-                }
-            }
-            if (g + 1 < G) store_a((g + 1) & 1);
-            __syncthreads();
-        }
-
-        if (live) {
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int row = s * 16 + (lane >> 4) * 4 + r;
-                        if (row < it.rows) {
-                            const float gv = acc[s][c][0][r], uv = acc[s][c][1][r];
-                            act[(size_t)sEntry[row] * I + pt * 64 + c0 + c * 16 + (lane & 15)] =
-                                (gv / (1.0f + expf(-gv))) * uv;
-                        }
-                    }
-                }
-            }
-        }
+        dispatch_item(it.rows, a.G, GuRun{a, it, sA, sEntry});
         __syncthreads();  // sEntry and sA are rewritten by the next item
     }
 }
 
 // --------------------------------------------------------------------- down
+// act (fp32) split into bf16 hi (top half) and lo (top half of act - hi), two
+// values per word.
+__device__ __forceinline__ void split_pair(uint32_t a0, uint32_t a1, uint32_t& hi, uint32_t& lo) {
+    const float r0 = __uint_as_float(a0) - __uint_as_float(a0 & 0xFFFF0000u);
+    const float r1 = __uint_as_float(a1) - __uint_as_float(a1 & 0xFFFF0000u);
+    hi = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
+    lo = __builtin_amdgcn_perm(__float_as_uint(r1), __float_as_uint(r0), 0x07060302u);
+}
+
+struct DnArgs {
+    const float* act;
+    const xp_expert* experts;
+    float* out;
+    int H, I, G;
+};
+
+template <int NS, int D>
+__device__ __forceinline__ void dn_item(const DnArgs& a, const Item& it, uint16_t (*sHi)[kPM * kAStride],
+                                        uint16_t (*sLo)[kPM * kAStride], const int* sEntry) {
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int G = a.G, H = a.H, I = a.I;
+
+    // act rows staged by all threads: row t/2, 16 floats at k offset (t&1)*16.
+    const int arow = t >> 1, acol = (t & 1) * 16;
+    const u32x4v* arow_p = (const u32x4v*)(a.act + (size_t)sEntry[arow] * I + acol);
+    u32x4v ra[kDA][4];
+    auto load_a = [&](int slot, int g) {
+        g = min(g, G - 1);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) ra[slot][q] = arow_p[8 * g + q];
+    };
+    auto store_a = [&](int buf, int slot) {
+        uint32_t hi[8], lo[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            split_pair(ra[slot][q >> 1][(q & 1) * 2], ra[slot][q >> 1][(q & 1) * 2 + 1], hi[q], lo[q]);
+        u32x4v* qh = (u32x4v*)(&sHi[buf][arow * kAStride + acol]);
+        u32x4v* ql = (u32x4v*)(&sLo[buf][arow * kAStride + acol]);
+        qh[0] = u32x4v{hi[0], hi[1], hi[2], hi[3]};
+        qh[1] = u32x4v{hi[4], hi[5], hi[6], hi[7]};
+        ql[0] = u32x4v{lo[0], lo[1], lo[2], lo[3]};
+        ql[1] = u32x4v{lo[4], lo[5], lo[6], lo[7]};
+    };
+
+    const int pt_raw = it.nt * 2 + (wave >> 1);
+    const bool live = pt_raw * 64 < H;
+    const int pt = live ? pt_raw : 0;
+    const int c0 = (wave & 1) * 32;
+    const xp_expert ex = a.experts[it.e];
+    const int col = c0 + (lane & 15);
+    const int word = lane >> 4;
+    gwords_t dc = (gwords_t)(ex.down_codes) + (size_t)pt * G * 256 + col * 4 + word;
+    gbytes1_t ds = (gbytes1_t)(ex.down_scales) + (size_t)pt * G * 64 + col;
+    uint32_t bc[D][2], bs[D][2];
+    auto load_b = [&](int slot, int g) {
+        g = min(g, G - 1);
+        bc[slot][0] = dc[g * 256];
+        bc[slot][1] = dc[g * 256 + 64];
+        bs[slot][0] = ds[g * 64];
+        bs[slot][1] = ds[g * 64 + 16];
+    };
+    bf16x8 bf[2][2];
+    auto decode_b = [&](int buf, int slot) {
+        bf[buf][0] = decode8(bc[slot][0], e4m3f(bs[slot][0]));
+        bf[buf][1] = decode8(bc[slot][1], e4m3f(bs[slot][1]));
+    };
+
+    f32x4 acc[NS][2];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        acc[s][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc[s][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+#pragma unroll
+    for (int u = 0; u < D; ++u) load_b(u, u);
+#pragma unroll
+    for (int u = 0; u < kDA; ++u) load_a(u, u);
+    store_a(0, 0);
+    load_a(0, kDA);
+    decode_b(0, 0);
+    load_b(0, D);
+    __syncthreads();
+
+    for (int g0 = 0; g0 < G; g0 += D) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+            const int g = g0 + u;
+            const int cur = u & 1;
+            const int off = (lane & 15) * kAStride + word * 8;
+            bf16x8 ah[NS], al[NS];
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                ah[s] = *(const bf16x8*)(&sHi[cur][off + s * 16 * kAStride]);
+                al[s] = *(const bf16x8*)(&sLo[cur][off + s * 16 * kAStride]);
+            }
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                acc[s][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[s], bf[cur][0], acc[s][0], 0, 0, 0);
+                acc[s][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[s], bf[cur][1], acc[s][1], 0, 0, 0);
+            }
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                acc[s][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[s], bf[cur][0], acc[s][0], 0, 0, 0);
+                acc[s][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[s], bf[cur][1], acc[s][1], 0, 0, 0);
+            }
+            const int nslot = (u + 1) % D;
+            decode_b(cur ^ 1, nslot);
+            load_b(nslot, g + 1 + D);
+            const int aslot = (u + 1) % kDA;
+            store_a(cur ^ 1, aslot);
+            load_a(aslot, g + 1 + kDA);
+            interleave_step<4 * NS, 100>();
+            __syncthreads();
+        }
+    }
+
+    if (live) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = s * 16 + (lane >> 4) * 4 + r;
+                    if (row < it.rows)
+                        a.out[(size_t)sEntry[row] * H + pt * 64 + c0 + c * 16 + (lane & 15)] = acc[s][c][r];
+                }
+            }
+        }
+    }
+}
+
+struct DnRun {
+    const DnArgs& a;
+    const Item& it;
+    uint16_t (*sHi)[kPM * kAStride];
+    uint16_t (*sLo)[kPM * kAStride];
+    const int* sEntry;
+    template <int NS, int D>
+    __device__ __forceinline__ void run() const { dn_item<NS, D>(a, it, sHi, sLo, sEntry); }
+};
+
 // out[entry][n] = the rows' act (fp32, as bf16 hi + lo) times down (K = inter).
-__global__ __launch_bounds__(kPThreads, 2) void prefill_down_kernel(
+__global__ __launch_bounds__(kPThreads, 1) void prefill_down_kernel(
     const xp_expert* __restrict__ experts, const float* __restrict__ act, const int32_t* __restrict__ count,
     const int32_t* __restrict__ offset, const int32_t* __restrict__ entry, int E, int H, int I,
     float* __restrict__ out) {
@@ -256,107 +489,22 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_down_kernel(
     __shared__ int sP[kMaxExperts + 1];
     __shared__ int swave[4];
 
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int t = threadIdx.x;
     const int n_tiles = (H + kPN - 1) / kPN;
     const int total = block_prefix(count, E, sP, swave) * n_tiles;
-    const int G = I / 32;
+    const DnArgs a{act, experts, out, H, I, I / 32};
     const Deal dl = deal(total);
 
     for (int i = dl.first; i < dl.end; i += dl.step) {
         const Item it = item_at(i, n_tiles, sP, E, count);
         if (t < kPM) sEntry[t] = entry[offset[it.e] + it.m0 + min(t, it.rows - 1)];
         __syncthreads();
-
-        // act rows staged by all threads: row t/2, 16 floats at k offset (t&1)*16,
-        // split into bf16 hi (top half) and lo (top half of the remainder).
-        const int arow = t >> 1, acol = (t & 1) * 16;
-        const float* arow_p = act + (size_t)sEntry[arow] * I + acol;
-        u32x4v ra[4];
-        auto load_a = [&](int g) {
-            const u32x4v* p = (const u32x4v*)(arow_p + 32 * g);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) ra[q] = p[q];
-        };
-        auto store_a = [&](int buf) {
-            uint32_t hi[8], lo[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const uint32_t a0 = ra[q >> 1][(q & 1) * 2], a1 = ra[q >> 1][(q & 1) * 2 + 1];
-                const float r0 = __uint_as_float(a0) - __uint_as_float(a0 & 0xFFFF0000u);
-                const float r1 = __uint_as_float(a1) - __uint_as_float(a1 & 0xFFFF0000u);
-                hi[q] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
-                lo[q] = __builtin_amdgcn_perm(__float_as_uint(r1), __float_as_uint(r0), 0x07060302u);
-            }
-            u32x4v* qh = (u32x4v*)(&sHi[buf][arow * kAStride + acol]);
-            u32x4v* ql = (u32x4v*)(&sLo[buf][arow * kAStride + acol]);
-            qh[0] = u32x4v{hi[0], hi[1], hi[2], hi[3]};
-            qh[1] = u32x4v{hi[4], hi[5], hi[6], hi[7]};
-            ql[0] = u32x4v{lo[0], lo[1], lo[2], lo[3]};
-            ql[1] = u32x4v{lo[4], lo[5], lo[6], lo[7]};
-        };
-
-        const int pt = it.nt * 2 + (wave >> 1);
-        const int c0 = (wave & 1) * 32;
-        const bool live = pt * 64 < H;
-        const xp_expert ex = experts[it.e];
-        const int col = c0 + (lane & 15);
-        const int word = lane >> 4;
-        gwords_t dc = (gwords_t)(ex.down_codes) + (size_t)pt * G * 256 + col * 4 + word;
-        gbytes1_t ds = (gbytes1_t)(ex.down_scales) + (size_t)pt * G * 64 + col;
-
-        f32x4 acc[8][2];
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            acc[s][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-            acc[s][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        const int slabs = (it.rows + 15) >> 4;
-
-        load_a(0);
-        store_a(0);
-        __syncthreads();
-        for (int g = 0; g < G; ++g) {
-            if (g + 1 < G) load_a(g + 1);
-            if (live) {
-                const uint32_t c0w = dc[g * 256], c1w = dc[g * 256 + 64];
-                const float s0 = e4m3f(ds[g * 64]), s1 = e4m3f(ds[g * 64 + 16]);
-                const bf16x8 b0 = decode8(c0w, s0), b1 = decode8(c1w, s1);
-                const int off = (lane & 15) * kAStride + word * 8;
-#pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    if (s < slabs) {
-                        const bf16x8 ah = *(const bf16x8*)(&sHi[g & 1][off + s * 16 * kAStride]);
-                        const bf16x8 al = *(const bf16x8*)(&sLo[g & 1][off + s * 16 * kAStride]);
-                        acc[s][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b0, acc[s][0], 0, 0, 0);
-                        acc[s][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b1, acc[s][1], 0, 0, 0);
-                        acc[s][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b0, acc[s][0], 0, 0, 0);
-                        acc[s][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b1, acc[s][1], 0, 0, 0);
-                    }
-                }
-            }
-            if (g + 1 < G) store_a((g + 1) & 1);
-            __syncthreads();
-        }
-
-        if (live) {
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int row = s * 16 + (lane >> 4) * 4 + r;
-                        if (row < it.rows)
-                            out[(size_t)sEntry[row] * H + pt * 64 + c0 + c * 16 + (lane & 15)] = acc[s][c][r];
-                    }
-                }
-            }
-        }
+        dispatch_item(it.rows, a.G, DnRun{a, it, sHi, sLo, sEntry});
         __syncthreads();
     }
 }
 
-// Persistent grid: two workgroups per CU, a multiple of 8 (one share per XCD),
+// Persistent grid: one workgroup per CU, a multiple of 8 (one share per XCD),
 // never more than an upper bound on the items.
 static int prefill_grid(int rows, int k, int E, int n_tiles) {
     static int cap = 0;
@@ -365,7 +513,7 @@ static int prefill_grid(int rows, int k, int E, int n_tiles) {
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;
-        cap = ((2 * cus + 7) / 8) * 8;
+        cap = ((cus + 7) / 8) * 8;
     }
     const long long nk = (long long)rows * k;
     const long long blocks = (nk + kPM - 1) / kPM + std::min<long long>(E, nk);  // >= sum of ceil(n_e / 128)
