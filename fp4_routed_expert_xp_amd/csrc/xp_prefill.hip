@@ -145,20 +145,6 @@ __device__ __forceinline__ Deal deal(int total) {
 // the item's rows rounded up to 2, 4, 6 or 8 slabs.
 constexpr int kDA = 4;  // activation groups in flight per thread
 
-// Scheduling hint for one pipelined step: after the step's LDS reads, issue the
-// matrix instructions one at a time with VALU work (the next group's decode,
-// the activation split) slotted between them, so both units stay busy.
-template <int NMFMA, int NVALU>
-__device__ __forceinline__ void interleave_step() {
-    __builtin_amdgcn_sched_group_barrier(0x100, 32, 0);  // LDS reads
-#pragma unroll
-    for (int i = 0; i < NMFMA; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                         // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, (NVALU + NMFMA - 1) / NMFMA, 0);  // VALU
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                         // a global load
-    }
-}
-
 struct GuArgs {
     const uint16_t* x;
     const xp_expert* experts;
@@ -447,7 +433,6 @@ __device__ __forceinline__ void dn_item(const DnArgs& a, const Item& it, uint16_
             const int aslot = (u + 1) % kDA;
             store_a(cur ^ 1, aslot);
             load_a(aslot, g + 1 + kDA);
-            interleave_step<4 * NS, 100>();
             __syncthreads();
         }
     }

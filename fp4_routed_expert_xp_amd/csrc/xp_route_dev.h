@@ -29,19 +29,15 @@ __device__ __forceinline__ float order_logit(uint32_t o) {
     return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 
-// One wave selects row r's top-k: k rounds, each taking the largest order over
-// the wave and, among the lanes holding it, the smallest expert id (so equal
-// logits go to the lower id and NaN comes last). Lane j keeps round j's pick.
-// Writes ids and softmax weights (fp32: exp of each chosen logit minus the
-// largest, summed in slot order, one division) to global memory when topk_id is
-// given, ids to sid[0..k) in LDS, and sets bit r_local of each chosen expert's mask.
-// CPL = candidates per lane (E <= 64 * CPL).
+// One wave selects the first kk picks of a logit row: kk rounds, each taking
+// the largest order over the wave and, among the lanes holding it, the smallest
+// expert id (so equal logits go to the lower id and NaN comes last). Lane j
+// (j < kk) gets round j's order key and id. CPL = candidates per lane
+// (E <= 64 * CPL).
 template <int CPL>
-__device__ void topk_row_n(const float* __restrict__ logits, int E, int k, int r, int r_local,
-                           int32_t* __restrict__ topk_id, float* __restrict__ topk_w, int32_t* sid,
-                           unsigned long long* smask) {
+__device__ __forceinline__ void topk_picks(const float* __restrict__ lr, int E, int kk, uint32_t& mine_ord,
+                                           uint32_t& mine_id) {
     const int lane = threadIdx.x & 63;
-    const float* lr = logits + (size_t)r * E;
     float v[CPL];
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
@@ -55,8 +51,9 @@ __device__ void topk_row_n(const float* __restrict__ logits, int E, int k, int r
         live[i] = lane + 64 * i < E;
         ord[i] = logit_order(v[i]);
     }
-    uint32_t mine_ord = 0u, mine_id = 0u;
-    for (int j = 0; j < k; ++j) {
+    mine_ord = 0u;
+    mine_id = 0u;
+    for (int j = 0; j < kk; ++j) {
         // this lane's best live candidate: larger order, then smaller id
         uint32_t bo = 0u, bi = 0xFFFFFFFFu;
         bool any = false;
@@ -72,17 +69,45 @@ __device__ void topk_row_n(const float* __restrict__ logits, int E, int k, int r
             if ((uint32_t)(lane + 64 * i) == wi) live[i] = false;
         if (lane == j) { mine_ord = wo; mine_id = wi; }
     }
-    // lane 0 holds the largest chosen logit; every lane j < k its own exp term
+}
+
+// topk_picks for E <= 1024.
+__device__ __forceinline__ void topk_picks_any(const float* __restrict__ lr, int E, int kk, uint32_t& mo,
+                                               uint32_t& mi) {
+    if (E <= 64) topk_picks<1>(lr, E, kk, mo, mi);
+    else if (E <= 128) topk_picks<2>(lr, E, kk, mo, mi);
+    else if (E <= 256) topk_picks<4>(lr, E, kk, mo, mi);
+    else if (E <= 512) topk_picks<8>(lr, E, kk, mo, mi);
+    else topk_picks<16>(lr, E, kk, mo, mi);
+}
+
+// Softmax weight of lane j's pick over the k picks (fp32): exp of its logit
+// minus the largest (lane 0's), divided by the sum of those terms taken in
+// slot order. Every lane of the wave must call this.
+__device__ __forceinline__ float topk_weight(uint32_t mine_ord, int k) {
     const float top = order_logit((uint32_t)__builtin_amdgcn_readfirstlane((int)mine_ord));
     const float ex = expf(order_logit(mine_ord) - top);
     float s = 0.0f;
     for (int j = 0; j < k; ++j) s = s + __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(ex), j));
+    return ex / s;
+}
+
+// One wave routes row r: ids and softmax weights to global memory when topk_id
+// is given, ids to sid[0..k) in LDS, and bit r_local of each chosen expert's mask.
+template <int CPL>
+__device__ void topk_row_n(const float* __restrict__ logits, int E, int k, int r, int r_local,
+                           int32_t* __restrict__ topk_id, float* __restrict__ topk_w, int32_t* sid,
+                           unsigned long long* smask) {
+    const int lane = threadIdx.x & 63;
+    uint32_t mine_ord, mine_id;
+    topk_picks<CPL>(logits + (size_t)r * E, E, k, mine_ord, mine_id);
+    const float w = topk_weight(mine_ord, k);
     if (lane < k) {
         const int id = (int)mine_id;
         sid[lane] = id;
         if (topk_id) {
             topk_id[(size_t)r * k + lane] = id;
-            topk_w[(size_t)r * k + lane] = ex / s;
+            topk_w[(size_t)r * k + lane] = w;
         }
         atomicOr(&smask[id], 1ull << r_local);
     }

@@ -61,66 +61,80 @@ typedef const u32x4 __attribute__((address_space(1)))* gcodes_t;
 typedef const uint8_t __attribute__((address_space(1)))* gbytes_t;
 
 // Weight codes are read once: non-temporal loads keep them out of the caches' way.
-__device__ __forceinline__ u32x4 load_codes(gcodes_t p) { return __builtin_nontemporal_load(p); }
+#ifndef XP_NT_CODES
+#define XP_NT_CODES 1
+#endif
+__device__ __forceinline__ u32x4 load_codes(gcodes_t p) {
+#if XP_NT_CODES
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
 
 // Groups kept in flight per wave: deep for small passes, shallower as rows add
 // registers (gate/up keeps within 128 VGPRs for 16-wave workgroups; down within
 // 128 so that two 8-wave workgroups share a CU).
+#ifndef XP_GU_DEPTH_1
+#define XP_GU_DEPTH_1 2
+#endif
+#ifndef XP_DN_DEPTH_1
+#define XP_DN_DEPTH_1 2
+#endif
 template <int P>
 struct GuDepth {
-    static constexpr int value = P <= 2 ? 8 : (P <= 4 ? 4 : 2);
+    static constexpr int value = P <= 2 ? XP_GU_DEPTH_1 : (P <= 4 ? 4 : 2);
 };
 template <int P>
 struct DnDepth {
-    static constexpr int value = P == 1 ? 8 : (P <= 4 ? 4 : 1);
+    static constexpr int value = P == 1 ? XP_DN_DEPTH_1 : (P <= 4 ? 4 : 1);
 };
 
 // ------------------------------------------------------------------ gate/up
 
 // One leaf of one matrix (gate or up) for one (pass, tile): returns the P leaf
-// values of this lane's column.
+// values of this lane's column. The leaf's groups are g = leaf, leaf+8, ...;
+// every leaf walks ceil(G/8) of them so the loop body has no branches (the
+// ring's wait counts then follow it exactly): a group past the end re-reads
+// group G-1 and its product is discarded by a select.
 template <int P>
-__device__ __forceinline__ void gu_leaf(gcodes_t cc, gbytes_t ss, const uint32_t* const (&xr)[P], int leaf, int ng,
+__device__ __forceinline__ void gu_leaf(gcodes_t cc, gbytes_t ss, const uint32_t* const (&xr)[P], int leaf, int G,
                                         int lane, float (&acc)[P]) {
     constexpr int D = GuDepth<P>::value;
     const int xl = lane & 15;
+    const int ng = (G + 7) >> 3;
 #pragma unroll
     for (int r = 0; r < P; ++r) acc[r] = 0.0f;
     u32x4 bc[D];
     uint32_t bs[D];
     uint32_t bx[D][P];
+    auto load = [&](int s, int i) {
+        const int g = min(leaf + 8 * i, G - 1);
+        bc[s] = load_codes(cc + (size_t)g * kTile);
+        bs[s] = ss[(size_t)g * kTile];
 #pragma unroll
-    for (int s = 0; s < D; ++s) {
-        if (s < ng) {
-            const int g = leaf + 8 * s;
-            bc[s] = load_codes(cc + (size_t)g * kTile);
-            bs[s] = ss[(size_t)g * kTile];
+        for (int r = 0; r < P; ++r) bx[s][r] = xr[r][16 * g + xl];
+    };
 #pragma unroll
-            for (int r = 0; r < P; ++r) bx[s][r] = xr[r][16 * g + xl];
-        }
-    }
+    for (int s = 0; s < D; ++s) load(s, s);
     for (int i0 = 0; i0 < ng; i0 += D) {
 #pragma unroll
         for (int s = 0; s < D; ++s) {
             const int i = i0 + s;
-            if (i < ng) {
-                float w[32];
-                decode32(bc[s], w);
-                const float sc = e4m3(bs[s]);
-                uint32_t xc[P];
+            float w[32];
+            decode32(bc[s], w);
+            const float sc = e4m3(bs[s]);
+            uint32_t xc[P];
 #pragma unroll
-                for (int r = 0; r < P; ++r) xc[r] = bx[s][r];
-                if (i + D < ng) {
-                    const int g = leaf + 8 * (i + D);
-                    bc[s] = load_codes(cc + (size_t)g * kTile);
-                    bs[s] = ss[(size_t)g * kTile];
+            for (int r = 0; r < P; ++r) xc[r] = bx[s][r];
+            load(s, i + D);
+            float p[P];
+            Chain<P>::bf16(w, xc, p);
+            const bool valid = leaf + 8 * i < G;
 #pragma unroll
-                    for (int r = 0; r < P; ++r) bx[s][r] = xr[r][16 * g + xl];
-                }
-                float p[P];
-                Chain<P>::bf16(w, xc, p);
-#pragma unroll
-                for (int r = 0; r < P; ++r) acc[r] = __builtin_fmaf(p[r], sc, acc[r]);
+            for (int r = 0; r < P; ++r) {
+                const float v = __builtin_fmaf(p[r], sc, acc[r]);
+                acc[r] = valid ? v : acc[r];
             }
         }
     }
@@ -135,7 +149,6 @@ __device__ __forceinline__ void gu_item(const xp_expert* __restrict__ experts, c
     const int leaf = wave & 7, up = wave >> 3;
     const int e = ps.x, first = ps.y, real = ps.z;
     const int G = H >> 5;
-    const int ng = (G > leaf) ? (G - leaf + 7) >> 3 : 0;
 
     const xp_expert ex = experts[e];
     const size_t tile_chunks = (size_t)tile * G * kTile;
@@ -149,7 +162,7 @@ __device__ __forceinline__ void gu_item(const xp_expert* __restrict__ experts, c
         xr[r] = (const uint32_t*)(x + (size_t)(ent / k) * H);
     }
     float acc[P];
-    gu_leaf<P>(cc, ss, xr, leaf, ng, lane, acc);
+    gu_leaf<P>(cc, ss, xr, leaf, G, lane, acc);
 
     // leaves -> LDS: red[wave][row][lane], gate leaves in waves 0-7, up in 8-15
 #pragma unroll
@@ -265,6 +278,65 @@ __global__ __launch_bounds__(1024) void gateup_kernel(const xp_expert* __restric
 
 // --------------------------------------------------------------------- down
 
+// ---------------------------------------------------------- one-row decode
+// Routing, plan and gate/up for a batch of one row in one launch. With one row
+// every chosen expert has a one-row pass, so item (slot j, tile) needs only the
+// row's j-th pick: the workgroup's first wave runs top-k rounds 0..j and the
+// workgroup starts its weight stream without the full plan. The workgroup of
+// (slot k-1, tile 0) runs all k rounds and publishes what xp_route_bucket
+// writes for this row: top-k ids and weights, counts, offsets, entries and both
+// pass lists (one P=1 pass per chosen expert, experts ascending).
+__device__ void publish_one_row(const RouteIn& ri, int k, uint32_t mo, uint32_t mi) {
+    const int lane = threadIdx.x & 63;
+    const float w = topk_weight(mo, k);
+    int rank = 0;  // position of this lane's pick among the picks by expert id
+    for (int i = 0; i < k; ++i) rank += ((uint32_t)__builtin_amdgcn_readlane((int)mi, i) < mi) ? 1 : 0;
+    if (lane < k) {
+        ri.topk_id[lane] = (int32_t)mi;
+        ri.topk_w[lane] = w;
+        ri.w.gu_pass[rank] = make_int4((int)mi, rank, 1, 1);
+        ri.w.dn_pass[rank] = make_int4((int)mi, rank, 1, 1);
+        ri.w.entry[rank] = lane;  // row 0, slot lane
+    }
+    for (int e0 = 0; e0 <= ri.E; e0 += 64) {
+        const int e = e0 + lane;
+        int below = 0, hit = 0;
+        for (int i = 0; i < k; ++i) {
+            const int o = __builtin_amdgcn_readlane((int)mi, i);
+            below += o < e ? 1 : 0;
+            hit |= o == e ? 1 : 0;
+        }
+        if (e <= ri.E) ri.w.offset[e] = below;
+        if (e < ri.E) ri.w.count[e] = hit;
+    }
+    if (lane == 0) {
+        ri.w.hdr[0] = k;
+        ri.w.hdr[1] = k;
+    }
+}
+
+__global__ __launch_bounds__(1024) void gateup_one_row_kernel(const xp_expert* __restrict__ experts,
+                                                              const uint16_t* __restrict__ x, RouteIn ri, int H,
+                                                              int I, int k, float* __restrict__ act) {
+    __shared__ float red[2 * kLeaves * kTile];
+    __shared__ int32_t s_entry[1];
+    __shared__ int s_pick;
+    const int n_tiles = I / kTile;
+    const int j = blockIdx.x / n_tiles, tile = blockIdx.x - j * n_tiles;
+    const bool publish = (j == k - 1) && (tile == 0);
+    if (threadIdx.x < 64) {
+        uint32_t mo, mi;
+        topk_picks_any(ri.logits, ri.E, publish ? k : j + 1, mo, mi);
+        if ((int)threadIdx.x == j) {
+            s_pick = (int)mi;
+            s_entry[0] = j;
+        }
+        if (publish) publish_one_row(ri, k, mo, mi);
+    }
+    __syncthreads();
+    gu_item<1, false>(experts, x, s_entry, make_int4(s_pick, 0, 1, 1), tile, H, I, k, act, nullptr, red);
+}
+
 template <int P>
 __device__ __forceinline__ void dn_item(const xp_expert* __restrict__ experts, const float* __restrict__ act,
                         const int32_t* __restrict__ entry, int4 ps, int tile, int H, int I,
@@ -274,7 +346,6 @@ __device__ __forceinline__ void dn_item(const xp_expert* __restrict__ experts, c
     const int lane = threadIdx.x & 63;
     const int e = ps.x, first = ps.y, real = ps.z;
     const int G = I >> 5;
-    const int ng = (G > leaf) ? (G - leaf + 7) >> 3 : 0;
     const int xl = 2 * (lane & 15);
 
     const xp_expert ex = experts[e];
@@ -286,44 +357,41 @@ __device__ __forceinline__ void dn_item(const xp_expert* __restrict__ experts, c
 #pragma unroll
     for (int r = 0; r < P; ++r) ar[r] = act + (size_t)entry[first + (r < real ? r : real - 1)] * I;
 
+    // Branch-free ring over ceil(G/8) groups per leaf, as in gu_leaf.
+    const int ng = (G + 7) >> 3;
     float acc[P];
 #pragma unroll
     for (int r = 0; r < P; ++r) acc[r] = 0.0f;
     u32x4 bc[D];
     uint32_t bs[D];
     float2 bx[D][P];
+    auto load = [&](int s, int i) {
+        const int g = min(leaf + 8 * i, G - 1);
+        bc[s] = load_codes(cc + (size_t)g * kTile);
+        bs[s] = ss[(size_t)g * kTile];
 #pragma unroll
-    for (int s = 0; s < D; ++s) {
-        if (s < ng) {
-            const int g = leaf + 8 * s;
-            bc[s] = load_codes(cc + (size_t)g * kTile);
-            bs[s] = ss[(size_t)g * kTile];
+        for (int r = 0; r < P; ++r) bx[s][r] = *(const float2*)(ar[r] + 32 * g + xl);
+    };
 #pragma unroll
-            for (int r = 0; r < P; ++r) bx[s][r] = *(const float2*)(ar[r] + 32 * g + xl);
-        }
-    }
+    for (int s = 0; s < D; ++s) load(s, s);
     for (int i0 = 0; i0 < ng; i0 += D) {
 #pragma unroll
         for (int s = 0; s < D; ++s) {
             const int i = i0 + s;
-            if (i < ng) {
-                float w[32];
-                decode32(bc[s], w);
-                const float sc = e4m3(bs[s]);
-                float xa[P], xb[P];
+            float w[32];
+            decode32(bc[s], w);
+            const float sc = e4m3(bs[s]);
+            float xa[P], xb[P];
 #pragma unroll
-                for (int r = 0; r < P; ++r) { xa[r] = bx[s][r].x; xb[r] = bx[s][r].y; }
-                if (i + D < ng) {
-                    const int g = leaf + 8 * (i + D);
-                    bc[s] = load_codes(cc + (size_t)g * kTile);
-                    bs[s] = ss[(size_t)g * kTile];
+            for (int r = 0; r < P; ++r) { xa[r] = bx[s][r].x; xb[r] = bx[s][r].y; }
+            load(s, i + D);
+            float p[P];
+            Chain<P>::f32(w, xa, xb, p);
+            const bool valid = leaf + 8 * i < G;
 #pragma unroll
-                    for (int r = 0; r < P; ++r) bx[s][r] = *(const float2*)(ar[r] + 32 * g + xl);
-                }
-                float p[P];
-                Chain<P>::f32(w, xa, xb, p);
-#pragma unroll
-                for (int r = 0; r < P; ++r) acc[r] = __builtin_fmaf(p[r], sc, acc[r]);
+            for (int r = 0; r < P; ++r) {
+                const float v = __builtin_fmaf(p[r], sc, acc[r]);
+                acc[r] = valid ? v : acc[r];
             }
         }
     }
@@ -453,6 +521,12 @@ XP_API int xp_route_gateup(const xp_dims* dims, int32_t rows, const float* logit
     }
     WsPtrs w = ws_ptrs(workspace, dims, rows);
     RouteIn ri{logits, rows, dims->n_experts, topk_id, topk_w, w, current_tiers()};
+    if (rows == 1) {
+        const int grid = dims->top_k * (dims->inter / kTile);
+        hipLaunchKernelGGL(gateup_one_row_kernel, dim3(grid), dim3(1024), 0, (hipStream_t)stream, experts, x, ri,
+                           dims->hidden, dims->inter, dims->top_k, act);
+        return launch_status();
+    }
     const int grid = std::min(grid_for(rows, dims->top_k, dims->inter / kTile), fused_grid_cap());
     hipLaunchKernelGGL((gateup_kernel<false, true>), dim3(grid), dim3(1024), 0, (hipStream_t)stream, experts, x,
                        (const int32_t*)nullptr, (const int32_t*)nullptr, (const int4*)nullptr, ri, dims->hidden,
