@@ -187,7 +187,7 @@ __device__ __forceinline__ void gu_item(const xp_expert* __restrict__ experts, c
     __syncthreads();
 }
 
-// Routing inputs for the fused route + gate/up launch (unused otherwise).
+// Routing inputs of the one-row route + gate/up launch.
 struct RouteIn {
     const float* logits;
     int R, E;
@@ -197,86 +197,35 @@ struct RouteIn {
     Tiers T;
 };
 
-// Without ROUTE the plan comes from the workspace. With ROUTE (at most 64 rows)
-// every workgroup routes and plans the batch itself into LDS, so no separate
-// routing launch precedes this one; workgroup 0 also publishes the plan
-// (top-k, weights, entries, both pass lists, header) for the down launch that
-// follows. The grid is capped at two workgroups per CU, so each workgroup plans
-// once and then walks several items.
-template <bool SPLIT, bool ROUTE>
+// Gate/up passes over the plan in the workspace: work item = (pass, tile).
+template <bool SPLIT>
 __global__ __launch_bounds__(1024) void gateup_kernel(const xp_expert* __restrict__ experts,
                                                       const uint16_t* __restrict__ x,
                                                       const int32_t* __restrict__ hdr,
-                                                      const int32_t* __restrict__ entry_g,
-                                                      const int4* __restrict__ passes_g, RouteIn ri, int H, int I,
+                                                      const int32_t* __restrict__ entry,
+                                                      const int4* __restrict__ passes, int E, int H, int I,
                                                       int k, float* __restrict__ out0, float* __restrict__ out1) {
     __shared__ float red[2 * kLeaves * kMaxPass * kTile];
+    const xp_expert* tab = experts;
     const int n_tiles = I / kTile;
-    int n_pass;
-    const int32_t* entry;
-    const int4* passes;
-    if (ROUTE) {
-        __shared__ unsigned long long smask[kMaxExperts];
-        __shared__ int32_t sid[kSmallRows][kMaxTopK];
-        __shared__ int32_t scnt[kMaxExperts];
-        __shared__ int32_t soff[kMaxExperts + 1];
-        __shared__ int32_t sentry[kSmallRows * kMaxTopK];
-        __shared__ int4 sgu[kSmallRows * kMaxTopK];
-        __shared__ int32_t sn_gu;
-        __shared__ int wsum[48];
-        const bool lead = blockIdx.x == 0;
-        const int E = ri.E, R = ri.R;
-        for (int e = threadIdx.x; e < E; e += blockDim.x) smask[e] = 0ull;
-        __syncthreads();
-        const int wave = threadIdx.x >> 6;
-        for (int r = wave; r < R; r += 16)
-            topk_row(ri.logits, E, k, r, r, lead ? ri.topk_id : nullptr, ri.topk_w, sid[r], smask);
-        __syncthreads();
-        for (int e = threadIdx.x; e < E; e += blockDim.x) scnt[e] = __popcll(smask[e]);
-        __syncthreads();
-        plan_block(E, scnt, ri.T, soff, sgu, lead ? ri.w.dn_pass : nullptr, lead ? ri.w.count : nullptr,
-                   lead ? ri.w.offset : nullptr, lead ? ri.w.hdr : nullptr, &sn_gu, wsum);
-        __syncthreads();
-        const int t = threadIdx.x;
-        if (t < R * k) {
-            const int r = t / k, j = t - r * k;
-            const int e = sid[r][j];
-            const unsigned long long below = (r == 0) ? 0ull : (smask[e] & ((1ull << r) - 1ull));
-            const int pos = soff[e] + __popcll(below);
-            sentry[pos] = t;
-            if (lead) ri.w.entry[pos] = t;
-        }
-        __syncthreads();
-        n_pass = sn_gu;
-        if (lead)
-            for (int i = t; i < n_pass; i += blockDim.x) ri.w.gu_pass[i] = sgu[i];
-        entry = sentry;
-        passes = sgu;
-    } else {
-        n_pass = hdr[0];
-        entry = entry_g;
-        passes = passes_g;
-    }
-    const int n_items = n_pass * n_tiles;
+    const int n_items = hdr[0] * n_tiles;
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
         const int pass = item / n_tiles;
         const int tile = item - pass * n_tiles;
         const int4 ps = passes[pass];
         switch (ps.w) {
-            case 1: gu_item<1, SPLIT>(experts, x, entry, ps, tile, H, I, k, out0, out1, red); break;
-            case 2: gu_item<2, SPLIT>(experts, x, entry, ps, tile, H, I, k, out0, out1, red); break;
-            case 3: gu_item<3, SPLIT>(experts, x, entry, ps, tile, H, I, k, out0, out1, red); break;
-            case 4: gu_item<4, SPLIT>(experts, x, entry, ps, tile, H, I, k, out0, out1, red); break;
-            case 5: gu_item<5, SPLIT>(experts, x, entry, ps, tile, H, I, k, out0, out1, red); break;
-            case 6: gu_item<6, SPLIT>(experts, x, entry, ps, tile, H, I, k, out0, out1, red); break;
-            case 7: gu_item<7, SPLIT>(experts, x, entry, ps, tile, H, I, k, out0, out1, red); break;
-            case 8: gu_item<8, SPLIT>(experts, x, entry, ps, tile, H, I, k, out0, out1, red); break;
+            case 1: gu_item<1, SPLIT>(tab, x, entry, ps, tile, H, I, k, out0, out1, red); break;
+            case 2: gu_item<2, SPLIT>(tab, x, entry, ps, tile, H, I, k, out0, out1, red); break;
+            case 3: gu_item<3, SPLIT>(tab, x, entry, ps, tile, H, I, k, out0, out1, red); break;
+            case 4: gu_item<4, SPLIT>(tab, x, entry, ps, tile, H, I, k, out0, out1, red); break;
+            case 5: gu_item<5, SPLIT>(tab, x, entry, ps, tile, H, I, k, out0, out1, red); break;
+            case 6: gu_item<6, SPLIT>(tab, x, entry, ps, tile, H, I, k, out0, out1, red); break;
+            case 7: gu_item<7, SPLIT>(tab, x, entry, ps, tile, H, I, k, out0, out1, red); break;
+            case 8: gu_item<8, SPLIT>(tab, x, entry, ps, tile, H, I, k, out0, out1, red); break;
             default: break;
         }
     }
 }
-
-// --------------------------------------------------------------------- down
 
 // ---------------------------------------------------------- one-row decode
 // Routing, plan and gate/up for a batch of one row in one launch. With one row
@@ -414,9 +363,10 @@ __global__ __launch_bounds__(512, 4) void down_kernel(const xp_expert* __restric
                                                       const float* __restrict__ act,
                                                       const int32_t* __restrict__ hdr,
                                                       const int32_t* __restrict__ entry,
-                                                      const int4* __restrict__ passes, int H, int I,
+                                                      const int4* __restrict__ passes, int E, int H, int I,
                                                       float* __restrict__ out) {
     __shared__ float red[kLeaves * kMaxPass * kTile];
+    const xp_expert* tab = experts;
     const int n_tiles = H / kTile;
     const int n_items = hdr[1] * n_tiles;
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
@@ -424,14 +374,14 @@ __global__ __launch_bounds__(512, 4) void down_kernel(const xp_expert* __restric
         const int tile = item - pass * n_tiles;
         const int4 ps = passes[pass];
         switch (ps.w) {
-            case 1: dn_item<1>(experts, act, entry, ps, tile, H, I, out, red); break;
-            case 2: dn_item<2>(experts, act, entry, ps, tile, H, I, out, red); break;
-            case 3: dn_item<3>(experts, act, entry, ps, tile, H, I, out, red); break;
-            case 4: dn_item<4>(experts, act, entry, ps, tile, H, I, out, red); break;
-            case 5: dn_item<5>(experts, act, entry, ps, tile, H, I, out, red); break;
-            case 6: dn_item<6>(experts, act, entry, ps, tile, H, I, out, red); break;
-            case 7: dn_item<7>(experts, act, entry, ps, tile, H, I, out, red); break;
-            case 8: dn_item<8>(experts, act, entry, ps, tile, H, I, out, red); break;
+            case 1: dn_item<1>(tab, act, entry, ps, tile, H, I, out, red); break;
+            case 2: dn_item<2>(tab, act, entry, ps, tile, H, I, out, red); break;
+            case 3: dn_item<3>(tab, act, entry, ps, tile, H, I, out, red); break;
+            case 4: dn_item<4>(tab, act, entry, ps, tile, H, I, out, red); break;
+            case 5: dn_item<5>(tab, act, entry, ps, tile, H, I, out, red); break;
+            case 6: dn_item<6>(tab, act, entry, ps, tile, H, I, out, red); break;
+            case 7: dn_item<7>(tab, act, entry, ps, tile, H, I, out, red); break;
+            case 8: dn_item<8>(tab, act, entry, ps, tile, H, I, out, red); break;
             default: break;
         }
     }
@@ -453,26 +403,14 @@ static int gateup_common(const xp_dims* dims, int32_t rows, const uint16_t* x, c
     Plan pl = plan_view(ws, dims, rows);
     const int grid = grid_for(rows, dims->top_k, dims->inter / kTile);
     hipStream_t s = (hipStream_t)stream;
-    RouteIn none{};
     if (split)
-        hipLaunchKernelGGL((gateup_kernel<true, false>), dim3(grid), dim3(1024), 0, s, experts, x, pl.hdr, pl.entry,
-                           pl.gu_pass, none, dims->hidden, dims->inter, dims->top_k, o0, o1);
+        hipLaunchKernelGGL((gateup_kernel<true>), dim3(grid), dim3(1024), 0, s, experts, x, pl.hdr, pl.entry,
+                           pl.gu_pass, dims->n_experts, dims->hidden, dims->inter, dims->top_k, o0, o1);
     else
-        hipLaunchKernelGGL((gateup_kernel<false, false>), dim3(grid), dim3(1024), 0, s, experts, x, pl.hdr, pl.entry,
-                           pl.gu_pass, none, dims->hidden, dims->inter, dims->top_k, o0, (float*)nullptr);
+        hipLaunchKernelGGL((gateup_kernel<false>), dim3(grid), dim3(1024), 0, s, experts, x, pl.hdr, pl.entry,
+                           pl.gu_pass, dims->n_experts, dims->hidden, dims->inter, dims->top_k, o0,
+                           (float*)nullptr);
     return launch_status();
-}
-
-static int fused_grid_cap() {
-    static int cap = 0;
-    if (cap == 0) {
-        int dev = 0, cus = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-            cus = 256;
-        cap = 2 * cus;
-    }
-    return cap;
 }
 
 }  // namespace xp
@@ -500,7 +438,7 @@ XP_API int xp_down_rows(const xp_dims* dims, int32_t rows, const float* act, con
     Plan pl = plan_view(workspace, dims, rows);
     const int grid = grid_for(rows, dims->top_k, dims->hidden / kTile);
     hipLaunchKernelGGL(down_kernel, dim3(grid), dim3(512), 0, (hipStream_t)stream, experts, act, pl.hdr, pl.entry,
-                       pl.dn_pass, dims->hidden, dims->inter, out);
+                       pl.dn_pass, dims->n_experts, dims->hidden, dims->inter, out);
     return launch_status();
 }
 
@@ -513,24 +451,17 @@ XP_API int xp_route_gateup(const xp_dims* dims, int32_t rows, const float* logit
     if (rows == 0) return XP_OK;
     if (!logits || !x || !experts || !topk_id || !topk_w || !workspace || !act) return XP_ERR_NULL;
     if (ws_bytes < ws_layout(dims, rows).total) return XP_ERR_WORKSPACE;
-    if (rows > kSmallRows) {
-        // larger batches: the separate routing launch, then gate/up
+    if (rows > 1) {
+        // the routing launch, then gate/up over the published plan
         st = xp_route_bucket(dims, rows, logits, topk_id, topk_w, workspace, ws_bytes, stream);
         if (st != XP_OK) return st;
         return xp_gateup_rows(dims, rows, x, experts, workspace, ws_bytes, act, stream);
     }
     WsPtrs w = ws_ptrs(workspace, dims, rows);
     RouteIn ri{logits, rows, dims->n_experts, topk_id, topk_w, w, current_tiers()};
-    if (rows == 1) {
-        const int grid = dims->top_k * (dims->inter / kTile);
-        hipLaunchKernelGGL(gateup_one_row_kernel, dim3(grid), dim3(1024), 0, (hipStream_t)stream, experts, x, ri,
-                           dims->hidden, dims->inter, dims->top_k, act);
-        return launch_status();
-    }
-    const int grid = std::min(grid_for(rows, dims->top_k, dims->inter / kTile), fused_grid_cap());
-    hipLaunchKernelGGL((gateup_kernel<false, true>), dim3(grid), dim3(1024), 0, (hipStream_t)stream, experts, x,
-                       (const int32_t*)nullptr, (const int32_t*)nullptr, (const int4*)nullptr, ri, dims->hidden,
-                       dims->inter, dims->top_k, act, (float*)nullptr);
+    const int grid = dims->top_k * (dims->inter / kTile);
+    hipLaunchKernelGGL(gateup_one_row_kernel, dim3(grid), dim3(1024), 0, (hipStream_t)stream, experts, x, ri,
+                       dims->hidden, dims->inter, dims->top_k, act);
     return launch_status();
 }
 

@@ -155,11 +155,11 @@ int xp_combine(const xp_dims* dims, int32_t rows, const float* out, const float*
 /* ------------------------------------------------------------ fused calls
  * The same path in fewer calls, with the same bits. */
 
-/* xp_route_bucket followed by xp_gateup_rows. With rows <= 64 this is one
- * launch: every workgroup routes and plans the batch itself (the grid is two
- * workgroups per CU), so no launch boundary separates routing from the weight
- * stream; the plan, topk_id and topk_w are still written to the workspace and
- * outputs. More rows run the two calls. */
+/* xp_route_bucket followed by xp_gateup_rows. With one row this is one
+ * launch: every workgroup finds the row's expert for its own slot (top-k rounds
+ * up to that slot) and starts its weight stream without waiting for a full
+ * plan, while one workgroup publishes topk_id, topk_w and the plan exactly as
+ * xp_route_bucket writes them. More rows run the two calls. */
 int xp_route_gateup(const xp_dims* dims, int32_t rows, const float* logits, const uint16_t* x,
                     const xp_expert* experts, int32_t* topk_id, float* topk_w, void* workspace,
                     size_t ws_bytes, float* act, void* stream);
