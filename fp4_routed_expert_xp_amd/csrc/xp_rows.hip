@@ -271,7 +271,10 @@ __global__ __launch_bounds__(1024) void gateup_one_row_kernel(const xp_expert* _
     __shared__ int32_t s_entry[1];
     __shared__ int s_pick;
     const int n_tiles = I / kTile;
-    const int j = blockIdx.x / n_tiles, tile = blockIdx.x - j * n_tiles;
+    // Workgroups start in blockIdx order over a few microseconds; the slots that
+    // need the most top-k rounds go first, so late starters route quickly.
+    const int jb = blockIdx.x / n_tiles, tile = blockIdx.x - jb * n_tiles;
+    const int j = k - 1 - jb;
     const bool publish = (j == k - 1) && (tile == 0);
     if (threadIdx.x < 64) {
         uint32_t mo, mi;
