@@ -72,6 +72,7 @@ def parse():
     ap.add_argument("--layers", type=int, default=40)
     ap.add_argument("--cells", default="one_row,four_same,sixteen_random,prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-tier-sweep", action="store_true", help="skip the pass-size sweep cells")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU work budget of the oracle sample")
     return ap.parse_args()
 
@@ -203,6 +204,10 @@ PATHS = {"four_calls": ("route", "gateup", "down", "combine"), "two_calls": ("ro
          "prefill": ("route", "prefill_gateup", "prefill_down", "combine")}
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PREFILL_LAYERS = 4               # prefill cells rotate over this many layers (3.4 GB of weights each)
+# Pass-size sets timed against the default ({2,4,6,8} gate/up, {2,4} down):
+# the padded passes of four the pages replaced, one size only, and powers of two.
+TIER_SWEEP = [((4,), (4,)), ((8,), (4,)), ((2, 4, 8), (2, 4)), ((2,), (2,)), ((2, 4, 6, 8), (2, 4, 8))]
+SWEEP_CELLS = ("four_same", "sixteen_random")
 
 
 def _graph(fn):
@@ -393,6 +398,20 @@ def main():
             timings[key] = t
             reports[key] = cell_report(cell, t, copy_gbps)
             log("%s: %s" % (key, json.dumps(reports[key])))
+        if name in SWEEP_CELLS and not args.no_tier_sweep:
+            # same rows, other pass sizes: the bits are unchanged (the probe
+            # tests check it), only the time moves
+            for gu, dn in TIER_SWEEP:
+                xp.xp_set_tiers(list(gu), list(dn))
+                try:
+                    t = time_cell(cell, "two_calls", args.steps, args.warmup)
+                finally:
+                    xp.xp_set_tiers(None, None)
+                key = "%s/two_calls/tiers_gu%s_dn%s" % (name, "-".join(map(str, gu)), "-".join(map(str, dn)))
+                rep = cell_report(cell, t, copy_gbps)
+                rep["tiers"] = {"gate_up": list(gu), "down": list(dn)}
+                reports[key] = rep
+                log("%s: %s" % (key, json.dumps(rep)))
     decode = [c for c in cells if c != "prefill"]
     if not decode:
         log("the headline is a decode workload: name one of one_row, four_same, sixteen_random in --cells")
