@@ -19,9 +19,9 @@
 // (two 16-column MFMA tiles) for all 128 rows (eight 16-row slabs), so each wave
 // decodes only its own columns' weights, and the rows' activations are staged
 // once per workgroup in LDS (double-buffered along K, one 32-wide group per
-// step). The grid is persistent; items are laid out expert-major and dealt to
-// the eight XCDs in contiguous ranges so the workgroups sharing an expert's rows
-// and weights share one L2.
+// step). The grid is persistent (two workgroups per CU); items are laid out
+// expert-major and dealt to the eight XCDs in contiguous ranges so the
+// workgroups sharing an expert's rows and weights share one L2.
 #include "xp_common.h"
 
 #include <algorithm>
@@ -143,7 +143,30 @@ __device__ __forceinline__ Deal deal(int total) {
 // the group count; refills past the end re-read the last group), so the
 // compiler's wait counts follow the ring exactly. NS = 16-row slabs computed:
 // the item's rows rounded up to 2, 4, 6 or 8 slabs.
-constexpr int kDA = 4;  // activation groups in flight per thread
+//
+// Per kernel: waves per SIMD (= resident workgroups per CU), the deepest weight
+// ring and the activation ring. Two resident workgroups per CU let one's
+// decode, LDS and barrier time overlap the other's matrix work (measured: both
+// kernels faster than with one workgroup and deeper rings); the rings are sized
+// so the 128 (gate/up) or 64 (down) accumulators per lane still fit.
+#ifndef XP_PF_GU_WAVES
+#define XP_PF_GU_WAVES 2
+#endif
+#ifndef XP_PF_GU_DMAX
+#define XP_PF_GU_DMAX 2
+#endif
+#ifndef XP_PF_GU_DA
+#define XP_PF_GU_DA 2
+#endif
+#ifndef XP_PF_DN_WAVES
+#define XP_PF_DN_WAVES 2
+#endif
+#ifndef XP_PF_DN_DMAX
+#define XP_PF_DN_DMAX 4
+#endif
+#ifndef XP_PF_DN_DA
+#define XP_PF_DN_DA 2
+#endif
 
 struct GuArgs {
     const uint16_t* x;
@@ -152,7 +175,7 @@ struct GuArgs {
     int k, H, I, G;
 };
 
-template <int NS, int D>
+template <int NS, int D, int kDA>
 __device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint16_t (*sA)[kPM * kAStride],
                                         const int* sEntry) {
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -272,15 +295,16 @@ __device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint16_
 
 // Slab count class (2, 4, 6 or 8) and ring depth (8, 4 or 1: the largest that
 // divides the group count), then the item.
-template <typename F>
+template <int kDMax, typename F>
 __device__ __forceinline__ void dispatch_item(int rows, int G, F&& f) {
     const int slabs = (rows + 15) >> 4;
     const int ns = slabs <= 2 ? 2 : slabs <= 4 ? 4 : slabs <= 6 ? 6 : 8;
-    const int d = (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : 1;
+    constexpr int dh = kDMax, dl = kDMax / 2;
+    const int d = (G % dh == 0) ? dh : (G % dl == 0) ? dl : 1;
 #define XP_PF_CASE(NS_, D_) \
     if (ns == NS_ && d == D_) { f.template run<NS_, D_>(); return; }
-    XP_PF_CASE(2, 8) XP_PF_CASE(4, 8) XP_PF_CASE(6, 8) XP_PF_CASE(8, 8)
-    XP_PF_CASE(2, 4) XP_PF_CASE(4, 4) XP_PF_CASE(6, 4) XP_PF_CASE(8, 4)
+    XP_PF_CASE(2, dh) XP_PF_CASE(4, dh) XP_PF_CASE(6, dh) XP_PF_CASE(8, dh)
+    XP_PF_CASE(2, dl) XP_PF_CASE(4, dl) XP_PF_CASE(6, dl) XP_PF_CASE(8, dl)
     XP_PF_CASE(2, 1) XP_PF_CASE(4, 1) XP_PF_CASE(6, 1) XP_PF_CASE(8, 1)
 #undef XP_PF_CASE
 }
@@ -291,12 +315,12 @@ struct GuRun {
     uint16_t (*sA)[kPM * kAStride];
     const int* sEntry;
     template <int NS, int D>
-    __device__ __forceinline__ void run() const { gu_item<NS, D>(a, it, sA, sEntry); }
+    __device__ __forceinline__ void run() const { gu_item<NS, D, XP_PF_GU_DA>(a, it, sA, sEntry); }
 };
 
 // act[entry][n] = silu(g) * u for the item's rows and columns, where g and u
 // are the rows' products with gate and up (K = hidden).
-__global__ __launch_bounds__(kPThreads, 1) void prefill_gateup_kernel(
+__global__ __launch_bounds__(kPThreads, XP_PF_GU_WAVES) void prefill_gateup_kernel(
     const xp_expert* __restrict__ experts, const uint16_t* __restrict__ x, const int32_t* __restrict__ count,
     const int32_t* __restrict__ offset, const int32_t* __restrict__ entry, int E, int k, int H, int I,
     float* __restrict__ act) {
@@ -315,7 +339,7 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_gateup_kernel(
         const Item it = item_at(i, n_tiles, sP, E, count);
         if (t < kPM) sEntry[t] = entry[offset[it.e] + it.m0 + min(t, it.rows - 1)];
         __syncthreads();
-        dispatch_item(it.rows, a.G, GuRun{a, it, sA, sEntry});
+        dispatch_item<XP_PF_GU_DMAX>(it.rows, a.G, GuRun{a, it, sA, sEntry});
         __syncthreads();  // sEntry and sA are rewritten by the next item
     }
 }
@@ -337,7 +361,7 @@ struct DnArgs {
     int H, I, G;
 };
 
-template <int NS, int D>
+template <int NS, int D, int kDA>
 __device__ __forceinline__ void dn_item(const DnArgs& a, const Item& it, uint16_t (*sHi)[kPM * kAStride],
                                         uint16_t (*sLo)[kPM * kAStride], const int* sEntry) {
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -460,11 +484,11 @@ struct DnRun {
     uint16_t (*sLo)[kPM * kAStride];
     const int* sEntry;
     template <int NS, int D>
-    __device__ __forceinline__ void run() const { dn_item<NS, D>(a, it, sHi, sLo, sEntry); }
+    __device__ __forceinline__ void run() const { dn_item<NS, D, XP_PF_DN_DA>(a, it, sHi, sLo, sEntry); }
 };
 
 // out[entry][n] = the rows' act (fp32, as bf16 hi + lo) times down (K = inter).
-__global__ __launch_bounds__(kPThreads, 1) void prefill_down_kernel(
+__global__ __launch_bounds__(kPThreads, XP_PF_DN_WAVES) void prefill_down_kernel(
     const xp_expert* __restrict__ experts, const float* __restrict__ act, const int32_t* __restrict__ count,
     const int32_t* __restrict__ offset, const int32_t* __restrict__ entry, int E, int H, int I,
     float* __restrict__ out) {
@@ -484,22 +508,23 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_down_kernel(
         const Item it = item_at(i, n_tiles, sP, E, count);
         if (t < kPM) sEntry[t] = entry[offset[it.e] + it.m0 + min(t, it.rows - 1)];
         __syncthreads();
-        dispatch_item(it.rows, a.G, DnRun{a, it, sHi, sLo, sEntry});
+        dispatch_item<XP_PF_DN_DMAX>(it.rows, a.G, DnRun{a, it, sHi, sLo, sEntry});
         __syncthreads();
     }
 }
 
-// Persistent grid: one workgroup per CU, a multiple of 8 (one share per XCD),
+// Persistent grid: per_cu workgroups per CU, a multiple of 8 (one share per XCD),
 // never more than an upper bound on the items.
-static int prefill_grid(int rows, int k, int E, int n_tiles) {
-    static int cap = 0;
-    if (cap == 0) {
-        int dev = 0, cus = 0;
+static int prefill_grid(int rows, int k, int E, int n_tiles, int per_cu) {
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, n = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-            cus = 256;
-        cap = ((cus + 7) / 8) * 8;
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cus = n;
     }
+    const int cap = ((per_cu * cus + 7) / 8) * 8;
     const long long nk = (long long)rows * k;
     const long long blocks = (nk + kPM - 1) / kPM + std::min<long long>(E, nk);  // >= sum of ceil(n_e / 128)
     const long long items = blocks * n_tiles;
@@ -521,7 +546,7 @@ XP_API int xp_prefill_gateup(const xp_dims* dims, int32_t rows, const uint16_t* 
     if (ws_bytes < ws_layout(dims, rows).total) return XP_ERR_WORKSPACE;
     WsPtrs w = ws_ptrs(const_cast<void*>(workspace), dims, rows);
     const int n_tiles = (dims->inter + kPN - 1) / kPN;
-    const int grid = prefill_grid(rows, dims->top_k, dims->n_experts, n_tiles);
+    const int grid = prefill_grid(rows, dims->top_k, dims->n_experts, n_tiles, XP_PF_GU_WAVES);
     hipLaunchKernelGGL(prefill_gateup_kernel, dim3(grid), dim3(kPThreads), 0, (hipStream_t)stream, experts, x,
                        w.count, w.offset, w.entry, dims->n_experts, dims->top_k, dims->hidden, dims->inter, act);
     return launch_status();
@@ -537,7 +562,7 @@ XP_API int xp_prefill_down(const xp_dims* dims, int32_t rows, const float* act, 
     if (ws_bytes < ws_layout(dims, rows).total) return XP_ERR_WORKSPACE;
     WsPtrs w = ws_ptrs(const_cast<void*>(workspace), dims, rows);
     const int n_tiles = (dims->hidden + kPN - 1) / kPN;
-    const int grid = prefill_grid(rows, dims->top_k, dims->n_experts, n_tiles);
+    const int grid = prefill_grid(rows, dims->top_k, dims->n_experts, n_tiles, XP_PF_DN_WAVES);
     hipLaunchKernelGGL(prefill_down_kernel, dim3(grid), dim3(kPThreads), 0, (hipStream_t)stream, experts, act,
                        w.count, w.offset, w.entry, dims->n_experts, dims->hidden, dims->inter, out);
     return launch_status();
