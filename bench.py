@@ -30,14 +30,14 @@ HBM_PEAK_GBPS = 8000.0
 CUS, LANES, CLOCK_GHZ = 256, 64, 2.4     # fp32 vector fma lanes per CU per clock, unpacked
 CSRC = os.path.join(ROOT, "fp4_routed_expert_xp_amd", "csrc")
 
-# HBM bytes per launch of the roofline kernel (gateup_kernel<false,true>, one-row
+# HBM bytes per launch of the roofline kernel (gateup_one_row_kernel, one-row
 # workload), from two rocprofv3 --pmc runs: FETCH_SIZE, then WRITE_SIZE, in KiB per
 # dispatch (mean over the dispatches of that workload). Each is scaled by what the
 # same counter read for a plain 2 GiB device-to-device copy: FETCH_SIZE read
 # 1,048,590 KiB for 2,097,152 KiB fetched, WRITE_SIZE read exactly 2,097,152 KiB.
 # The figure belongs to the kernel sources it was taken on (their digest below);
 # after any change under csrc/ the bench reports traffic as null.
-TRAFFIC = dict(sources="e96c2614", fetch_kib=35018.4, write_kib=66.4,
+TRAFFIC = dict(sources="241d2a3c", fetch_kib=34990.5, write_kib=66.4,
                fetch_factor=2097152 / 1048590.0, write_factor=1.0)
 
 
@@ -439,7 +439,8 @@ def main():
                                                                         base.H, base.I, base.E, base.k),
                    "rows": head["rows"], "layers": args.layers, "hidden": base.H, "inter": base.I,
                    "experts": base.E, "top_k": base.k, "path": "two_calls"},
-        "roofline": {"kernel": "gateup_kernel<false,true> (xp_route_gateup)", "bound": "hbm",
+        "roofline": {"kernel": "gateup_one_row_kernel (xp_route_gateup)" if head["rows"] == 1
+                     else "route_*_kernel + gateup_kernel<false> (xp_route_gateup)", "bound": "hbm",
                      "achieved": round(achieved, 1), "bytes_per_launch": head["gateup_bytes"],
                      "launch_us": head["kernel_us"]["route_gateup"],
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
