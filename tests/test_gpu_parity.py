@@ -9,6 +9,8 @@
 - On exact inputs (integer activations, power-of-two scales) every fp32 sum
   is exact, so the projections equal float64 bit for bit.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -17,7 +19,7 @@ import oracle
 import synth
 from fp4_routed_expert_xp_amd import xp
 
-from gpu_helpers import DeviceLayer, bits, log, rel_err_rows, run_path, same_class, to_dev
+from gpu_helpers import DeviceLayer, bits, log, rel_err_rows, run_fused, run_path, same_class, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -213,3 +215,30 @@ def test_release_planted_rows_keep_class(release_layer):
     ref = oracle.layer(x[rows], lg[rows], ex, cfg.H, cfg.I, cfg.E, cfg.k)
     for name in ("act", "out", "y"):
         assert same_class(res[name][rows], ref[name]), name
+
+
+# ---------------------------------------------------------- largest E and k
+MAXED = dataclasses.replace(TINY, name="maxed", H=128, I=64, E=1024, k=16, seed=1201, weight_seed=1201)
+
+
+@pytest.fixture(scope="module")
+def maxed_layer():
+    log("materialising 1024 small experts")
+    return DeviceLayer(MAXED, 0)
+
+
+@pytest.mark.parametrize("R", [1, 5, 70])
+def test_largest_experts_and_topk(maxed_layer, R):
+    """E = 1024 and k = 16 (the ABI's limits), H = 128 (leaves 4-7 of gate/up hold
+    no group and contribute +0), through both the single-workgroup (R <= 64) and
+    the block routing (R > 64); the two-call path gives the same bits."""
+    log("maxed R=%d" % R)
+    x = synth.activations(MAXED.seed, R, R, MAXED.H)
+    lg = synth.logits(MAXED.seed, R, R, MAXED.E)
+    res = run_path(maxed_layer, x, lg, split=True, canary=True)
+    ref = _oracle_layer(maxed_layer, x, lg)
+    _check_values(res, ref, R)
+    _check_chains(maxed_layer, x, res, range(min(R, 3)))
+    fused = run_fused(maxed_layer, x, lg)
+    for n in ("topk_w", "act", "out", "y"):
+        assert np.array_equal(bits(res[n]), bits(fused[n])), n
