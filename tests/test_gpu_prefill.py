@@ -163,3 +163,14 @@ def test_prefill_chunk_release_width(prefill_layer):
     ref = oracle_rows(prefill_layer, x[rows], lg[rows])
     worst = check_rows(res, ref, rows)
     log("  sampled rows %s: worst per-row relative error %.2e" % (rows, worst))
+
+
+def test_prefill_largest_experts_and_topk():
+    """1024 experts and top-16 (four experts per thread in the workgroups' block scan)."""
+    cfg = dataclasses.replace(TINY, name="maxed", H=128, I=64, E=1024, k=16, seed=1202, weight_seed=1202)
+    layer = DeviceLayer(cfg, 0)
+    R = 300
+    x = synth.activations(cfg.seed, R, R, cfg.H)
+    lg = synth.logits(cfg.seed, R, R, cfg.E, bias_sigma=0.5)
+    res = run_prefill(layer, x, lg)
+    check_rows(res, oracle_rows(layer, x, lg))
