@@ -112,36 +112,17 @@ inline Plan plan_view(const void* ws, const xp_dims* d, int32_t rows) {
 }  // namespace xp
 
 // ---------------------------------------------------------------- wave helpers
-// Cross-lane steps by DPP (no LDS traffic). Lanes whose DPP source is outside
-// their row, or whose row is masked off, receive `old` = the identity (0).
+// Cross-lane steps by DPP (no LDS traffic).
 namespace xp {
 
+// v from the DPP source lane; lanes whose source is outside their row, or whose
+// row is masked off, get 0 (the identity of a sum).
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ uint32_t dpp_or0(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
 }
 
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ uint64_t dpp_max_step(uint64_t x) {
-    const uint32_t lo = dpp_or0<CTRL, ROW_MASK>((uint32_t)x);
-    const uint32_t hi = dpp_or0<CTRL, ROW_MASK>((uint32_t)(x >> 32));
-    const uint64_t y = ((uint64_t)hi << 32) | lo;
-    return y > x ? y : x;
-}
-
-// Largest unsigned 64-bit value over the wave (identity 0), returned to every lane.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
-    x = dpp_max_step<0x111, 0xF>(x);  // row_shr:1
-    x = dpp_max_step<0x112, 0xF>(x);  // row_shr:2
-    x = dpp_max_step<0x114, 0xF>(x);  // row_shr:4
-    x = dpp_max_step<0x118, 0xF>(x);  // row_shr:8  -> lane 15 of each row holds the row's max
-    x = dpp_max_step<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
-    x = dpp_max_step<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3 -> lane 63 holds the max
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, 63);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), 63);
-    return ((uint64_t)hi << 32) | lo;
-}
-
+// v from the DPP source lane; lanes without a source keep their own v.
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ uint32_t dpp_self(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xF, false);

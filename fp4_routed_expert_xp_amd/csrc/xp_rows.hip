@@ -190,11 +190,10 @@ __device__ __forceinline__ void gu_item(const xp_expert* __restrict__ experts, c
 // Routing inputs of the one-row route + gate/up launch.
 struct RouteIn {
     const float* logits;
-    int R, E;
+    int E;
     int32_t* topk_id;
     float* topk_w;
     WsPtrs w;
-    Tiers T;
 };
 
 // Gate/up passes over the plan in the workspace: work item = (pass, tile).
@@ -461,7 +460,7 @@ XP_API int xp_route_gateup(const xp_dims* dims, int32_t rows, const float* logit
         return xp_gateup_rows(dims, rows, x, experts, workspace, ws_bytes, act, stream);
     }
     WsPtrs w = ws_ptrs(workspace, dims, rows);
-    RouteIn ri{logits, rows, dims->n_experts, topk_id, topk_w, w, current_tiers()};
+    RouteIn ri{logits, dims->n_experts, topk_id, topk_w, w};
     const int grid = dims->top_k * (dims->inter / kTile);
     hipLaunchKernelGGL(gateup_one_row_kernel, dim3(grid), dim3(1024), 0, (hipStream_t)stream, experts, x, ri,
                        dims->hidden, dims->inter, dims->top_k, act);
