@@ -18,9 +18,9 @@
 // columns). A workgroup of four waves takes one item: wave w owns 32 columns
 // (two 16-column MFMA tiles) for all 128 rows (eight 16-row slabs), so each wave
 // decodes only its own columns' weights, and the rows' activations are staged
-// once per workgroup in LDS (double-buffered along K, one 32-wide group per
-// step). The grid is persistent (two workgroups per CU); items are laid out
-// expert-major and dealt to the eight XCDs in contiguous ranges so the
+// once per workgroup in LDS (double-buffered along K, two 32-wide groups per
+// step and barrier). The grid is persistent (two workgroups per CU); items are
+// laid out expert-major and dealt to the eight XCDs in contiguous ranges so the
 // workgroups sharing an expert's rows and weights share one L2.
 #include "xp_common.h"
 
@@ -31,7 +31,7 @@ namespace xp {
 constexpr int kPM = 128;        // rows per item
 constexpr int kPN = 128;        // output columns per item (two packed 64-column tiles)
 constexpr int kPThreads = 256;  // four waves
-constexpr int kAStride = 40;    // bf16 per LDS activation row: 32 + 8 padding (conflict-free 16-byte reads)
+constexpr int kAStride = 72;    // bf16 per LDS activation row: two groups (64) + 8 padding (conflict-free 16-byte reads)
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
@@ -138,8 +138,9 @@ __device__ __forceinline__ Deal deal(int total) {
 // The K loop is software-pipelined over 32-wide groups: each wave keeps the
 // weight words and scale bytes of the next D groups in flight (a register
 // ring), each thread keeps the activations of the next kDA groups in flight and
-// stages one group ahead in LDS, and the weights of group g+1 are decoded while
-// group g's matrix instructions run. The loop body has no branches (D divides
+// stages the next two groups in LDS at every other group (one barrier per two
+// groups), and the weights of group g+1 are decoded while group g's matrix
+// instructions run. The loop body has no branches (D divides
 // the group count; refills past the end re-read the last group), so the
 // compiler's wait counts follow the ring exactly. NS = 16-row slabs computed:
 // the item's rows rounded up to 2, 4, 6 or 8 slabs.
@@ -178,6 +179,7 @@ struct GuArgs {
 template <int NS, int D, int kDA>
 __device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint16_t (*sA)[kPM * kAStride],
                                         const int* sEntry) {
+    static_assert(kDA % 2 == 0 && D % kDA == 0, "rings hold whole steps of two groups");
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int G = a.G, H = a.H, I = a.I;
 
@@ -216,8 +218,8 @@ __device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint16_
         ra[slot][0] = xrow[4 * g];
         ra[slot][1] = xrow[4 * g + 1];
     };
-    auto store_a = [&](int buf, int slot) {
-        u32x4v* q = (u32x4v*)(&sA[buf][arow * kAStride + acol]);
+    auto store_a = [&](int buf, int slot, int half) {  // half: which group of the buffer's two
+        u32x4v* q = (u32x4v*)(&sA[buf][arow * kAStride + half * 32 + acol]);
         q[0] = ra[slot][0];
         q[1] = ra[slot][1];
     };
@@ -240,8 +242,10 @@ __device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint16_
     for (int u = 0; u < D; ++u) load_b(u, u);
 #pragma unroll
     for (int u = 0; u < kDA; ++u) load_a(u, u);
-    store_a(0, 0);
+    store_a(0, 0, 0);
+    store_a(0, 1, 1);
     load_a(0, kDA);
+    load_a(1, kDA + 1);
     decode_b(0, 0);
     load_b(0, D);
     __syncthreads();
@@ -251,7 +255,8 @@ __device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint16_
         for (int u = 0; u < D; ++u) {
             const int g = g0 + u;
             const int cur = u & 1;
-            const uint16_t* a_lds = &sA[cur][(lane & 15) * kAStride + word * 8];
+            const int buf = (g >> 1) & 1;  // LDS buffers hold two groups each
+            const uint16_t* a_lds = &sA[buf][(lane & 15) * kAStride + cur * 32 + word * 8];
             bf16x8 af[NS];
 #pragma unroll
             for (int s = 0; s < NS; ++s) af[s] = *(const bf16x8*)(a_lds + s * 16 * kAStride);
@@ -266,11 +271,15 @@ __device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint16_
             const int nslot = (u + 1) % D;
             decode_b(cur ^ 1, nslot);
             load_b(nslot, g + 1 + D);
-            // next group's activations into the other LDS buffer, refill the ring
-            const int aslot = (u + 1) % kDA;
-            store_a(cur ^ 1, aslot);
-            load_a(aslot, g + 1 + kDA);
-            __syncthreads();
+            if (u & 1) {
+                // the next two groups' activations into the other LDS buffer, refill the ring
+                const int s0 = (u + 1) % kDA, s1 = (u + 2) % kDA;
+                store_a(buf ^ 1, s0, 0);
+                store_a(buf ^ 1, s1, 1);
+                load_a(s0, g + 1 + kDA);
+                load_a(s1, g + 2 + kDA);
+                __syncthreads();
+            }
         }
     }
 
@@ -299,13 +308,20 @@ template <int kDMax, typename F>
 __device__ __forceinline__ void dispatch_item(int rows, int G, F&& f) {
     const int slabs = (rows + 15) >> 4;
     const int ns = slabs <= 2 ? 2 : slabs <= 4 ? 4 : slabs <= 6 ? 6 : 8;
-    constexpr int dh = kDMax, dl = kDMax / 2;
-    const int d = (G % dh == 0) ? dh : (G % dl == 0) ? dl : 1;
+    // ring depths are even (a step is two groups) and G is even (H and I are
+    // multiples of 64): the deepest that divides G, else half of it, else 2
+    static_assert(kDMax % 2 == 0, "weight ring depth must be even");
+    constexpr int dh = kDMax, dl = (kDMax / 2) % 2 == 0 ? kDMax / 2 : 2;
+    const int d = (G % dh == 0) ? dh : (G % dl == 0) ? dl : 2;
 #define XP_PF_CASE(NS_, D_) \
     if (ns == NS_ && d == D_) { f.template run<NS_, D_>(); return; }
     XP_PF_CASE(2, dh) XP_PF_CASE(4, dh) XP_PF_CASE(6, dh) XP_PF_CASE(8, dh)
-    XP_PF_CASE(2, dl) XP_PF_CASE(4, dl) XP_PF_CASE(6, dl) XP_PF_CASE(8, dl)
-    XP_PF_CASE(2, 1) XP_PF_CASE(4, 1) XP_PF_CASE(6, 1) XP_PF_CASE(8, 1)
+    if constexpr (dl != dh) {
+        XP_PF_CASE(2, dl) XP_PF_CASE(4, dl) XP_PF_CASE(6, dl) XP_PF_CASE(8, dl)
+    }
+    if constexpr (dl != 2 && dh != 2) {
+        XP_PF_CASE(2, 2) XP_PF_CASE(4, 2) XP_PF_CASE(6, 2) XP_PF_CASE(8, 2)
+    }
 #undef XP_PF_CASE
 }
 
@@ -364,6 +380,7 @@ struct DnArgs {
 template <int NS, int D, int kDA>
 __device__ __forceinline__ void dn_item(const DnArgs& a, const Item& it, uint16_t (*sHi)[kPM * kAStride],
                                         uint16_t (*sLo)[kPM * kAStride], const int* sEntry) {
+    static_assert(kDA % 2 == 0 && D % kDA == 0, "rings hold whole steps of two groups");
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int G = a.G, H = a.H, I = a.I;
 
@@ -376,13 +393,13 @@ __device__ __forceinline__ void dn_item(const DnArgs& a, const Item& it, uint16_
 #pragma unroll
         for (int q = 0; q < 4; ++q) ra[slot][q] = arow_p[8 * g + q];
     };
-    auto store_a = [&](int buf, int slot) {
+    auto store_a = [&](int buf, int slot, int half) {
         uint32_t hi[8], lo[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q)
             split_pair(ra[slot][q >> 1][(q & 1) * 2], ra[slot][q >> 1][(q & 1) * 2 + 1], hi[q], lo[q]);
-        u32x4v* qh = (u32x4v*)(&sHi[buf][arow * kAStride + acol]);
-        u32x4v* ql = (u32x4v*)(&sLo[buf][arow * kAStride + acol]);
+        u32x4v* qh = (u32x4v*)(&sHi[buf][arow * kAStride + half * 32 + acol]);
+        u32x4v* ql = (u32x4v*)(&sLo[buf][arow * kAStride + half * 32 + acol]);
         qh[0] = u32x4v{hi[0], hi[1], hi[2], hi[3]};
         qh[1] = u32x4v{hi[4], hi[5], hi[6], hi[7]};
         ql[0] = u32x4v{lo[0], lo[1], lo[2], lo[3]};
@@ -423,8 +440,10 @@ __device__ __forceinline__ void dn_item(const DnArgs& a, const Item& it, uint16_
     for (int u = 0; u < D; ++u) load_b(u, u);
 #pragma unroll
     for (int u = 0; u < kDA; ++u) load_a(u, u);
-    store_a(0, 0);
+    store_a(0, 0, 0);
+    store_a(0, 1, 1);
     load_a(0, kDA);
+    load_a(1, kDA + 1);
     decode_b(0, 0);
     load_b(0, D);
     __syncthreads();
@@ -434,12 +453,13 @@ __device__ __forceinline__ void dn_item(const DnArgs& a, const Item& it, uint16_
         for (int u = 0; u < D; ++u) {
             const int g = g0 + u;
             const int cur = u & 1;
-            const int off = (lane & 15) * kAStride + word * 8;
+            const int buf = (g >> 1) & 1;  // LDS buffers hold two groups each
+            const int off = (lane & 15) * kAStride + cur * 32 + word * 8;
             bf16x8 ah[NS], al[NS];
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-                ah[s] = *(const bf16x8*)(&sHi[cur][off + s * 16 * kAStride]);
-                al[s] = *(const bf16x8*)(&sLo[cur][off + s * 16 * kAStride]);
+                ah[s] = *(const bf16x8*)(&sHi[buf][off + s * 16 * kAStride]);
+                al[s] = *(const bf16x8*)(&sLo[buf][off + s * 16 * kAStride]);
             }
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
@@ -454,10 +474,14 @@ __device__ __forceinline__ void dn_item(const DnArgs& a, const Item& it, uint16_
             const int nslot = (u + 1) % D;
             decode_b(cur ^ 1, nslot);
             load_b(nslot, g + 1 + D);
-            const int aslot = (u + 1) % kDA;
-            store_a(cur ^ 1, aslot);
-            load_a(aslot, g + 1 + kDA);
-            __syncthreads();
+            if (u & 1) {
+                const int s0 = (u + 1) % kDA, s1 = (u + 2) % kDA;
+                store_a(buf ^ 1, s0, 0);
+                store_a(buf ^ 1, s1, 1);
+                load_a(s0, g + 1 + kDA);
+                load_a(s1, g + 2 + kDA);
+                __syncthreads();
+            }
         }
     }
 
