@@ -122,32 +122,34 @@ __device__ __forceinline__ uint32_t dpp_or0(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
 }
 
-// v from the DPP source lane; lanes without a source keep their own v.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ uint32_t dpp_self(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xF, false);
-}
-
 // Largest / smallest unsigned 32-bit value over the wave, returned to every
-// lane. Lanes whose DPP source is outside the row keep their own value, which
-// max and min leave unchanged.
+// lane: six max (min) steps with a DPP source (row shifts 1, 2, 4, 8, then the
+// row broadcasts 15 and 31); lanes without a source in a step keep their own
+// value, and lane 63 ends with the wave's result. One instruction per step; the
+// s_nop pads cover the DPP read-after-VALU-write and EXEC hazards.
+#define XP_WAVE_REDUCE_U32(OP)                                              \
+    asm volatile("s_nop 4\n\t"                                             \
+                 "v_" OP "_u32_dpp %0, %0, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\t" \
+                 "s_nop 1\n\t"                                             \
+                 "v_" OP "_u32_dpp %0, %0, %0 row_shr:2 row_mask:0xf bank_mask:0xf\n\t" \
+                 "s_nop 1\n\t"                                             \
+                 "v_" OP "_u32_dpp %0, %0, %0 row_shr:4 row_mask:0xf bank_mask:0xf\n\t" \
+                 "s_nop 1\n\t"                                             \
+                 "v_" OP "_u32_dpp %0, %0, %0 row_shr:8 row_mask:0xf bank_mask:0xf\n\t" \
+                 "s_nop 1\n\t"                                             \
+                 "v_" OP "_u32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t" \
+                 "s_nop 1\n\t"                                             \
+                 "v_" OP "_u32_dpp %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf\n\t" \
+                 "s_nop 1"                                                   \
+                 : "+v"(x))
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
-    x = max(x, dpp_self<0x111, 0xF>(x));
-    x = max(x, dpp_self<0x112, 0xF>(x));
-    x = max(x, dpp_self<0x114, 0xF>(x));
-    x = max(x, dpp_self<0x118, 0xF>(x));
-    x = max(x, dpp_self<0x142, 0xA>(x));
-    x = max(x, dpp_self<0x143, 0xC>(x));
+    XP_WAVE_REDUCE_U32("max");
     return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
-    x = min(x, dpp_self<0x111, 0xF>(x));
-    x = min(x, dpp_self<0x112, 0xF>(x));
-    x = min(x, dpp_self<0x114, 0xF>(x));
-    x = min(x, dpp_self<0x118, 0xF>(x));
-    x = min(x, dpp_self<0x142, 0xA>(x));
-    x = min(x, dpp_self<0x143, 0xC>(x));
+    XP_WAVE_REDUCE_U32("min");
     return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
