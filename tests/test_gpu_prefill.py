@@ -174,3 +174,37 @@ def test_prefill_largest_experts_and_topk():
     lg = synth.logits(cfg.seed, R, R, cfg.E, bias_sigma=0.5)
     res = run_prefill(layer, x, lg)
     check_rows(res, oracle_rows(layer, x, lg))
+
+
+@pytest.mark.parametrize("pieces", [(1, 7, 100, 300), (64, 64, 64, 64, 64)])
+def test_prefill_rows_do_not_depend_on_the_chunk(mid_layer, pieces):
+    """A row's act, out and y bits are the same whether it runs in a 700-row
+    chunk or in a piece of 1, 7, 64, 100 or 300 rows: each output element is
+    one row of A against one column of B, accumulated over K in a fixed group
+    order, whatever else shares the 128-row block."""
+    R = 700
+    x = synth.activations(MID.seed + 3, R, R, MID.H)
+    lg = synth.logits(MID.seed + 3, R, R, MID.E, bias_sigma=0.5)
+    full = run_prefill(mid_layer, x, lg)
+    r0 = 0
+    for n in pieces:
+        part = run_prefill(mid_layer, x[r0:r0 + n], lg[r0:r0 + n])
+        for name in ("act", "out", "y"):
+            a = np.ascontiguousarray(full[name][r0:r0 + n]).view(np.uint32)
+            b = np.ascontiguousarray(part[name]).view(np.uint32)
+            assert np.array_equal(a, b), (pieces, r0, n, name)
+        r0 += n
+
+
+def test_prefill_chunk_invariance_release_width(prefill_layer):
+    """The same at release widths: rows of the 4,096-row chunk against pieces
+    of 1, 7 and 100 rows cut from it (busiest-expert rows included)."""
+    cfg = PREFILL
+    x, lg = synth.layer_inputs(cfg, 0)
+    full = run_prefill(prefill_layer, x, lg)
+    for r0, n in ((0, 1), (1, 7), (3996, 100)):
+        part = run_prefill(prefill_layer, x[r0:r0 + n], lg[r0:r0 + n])
+        for name in ("act", "out", "y"):
+            a = np.ascontiguousarray(full[name][r0:r0 + n]).view(np.uint32)
+            b = np.ascontiguousarray(part[name]).view(np.uint32)
+            assert np.array_equal(a, b), (r0, n, name)
