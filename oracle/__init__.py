@@ -52,6 +52,8 @@ def lib():
         L.or_bf16.restype = f64
         L.or_route.argtypes = [i32, i32, i32, P, P, P]
         L.or_route.restype = None
+        L.or_fp8_proj.argtypes = [i32, i32, i32, P, P, P, P]
+        L.or_fp8_proj.restype = None
         L.or_bucket.argtypes = [i32, i32, i32, P, P, P, P]
         L.or_bucket.restype = None
         L.or_passes.argtypes = [i32, P, i32, P, P, i32]
@@ -247,3 +249,17 @@ def combine32(w_f32, out_f32) -> np.ndarray:
 
 def omp_threads() -> int:
     return lib().or_omp_threads()
+
+
+def fp8_proj(x_bits: np.ndarray, w: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """float64 y [R][N] of the dense FP8 projection (see or_fp8_proj)."""
+    x_bits = _c(x_bits, np.uint16)
+    w = _c(w, np.uint8)
+    s = _c(s, np.float32)
+    R, K = x_bits.shape
+    N = w.shape[0]
+    assert w.shape == (N, K) and K % 128 == 0
+    assert s.shape == ((N + 127) // 128, K // 128)
+    y = np.zeros((R, N), dtype=np.float64)
+    lib().or_fp8_proj(R, N, K, _p(x_bits), _p(w), _p(s), _p(y))
+    return y

@@ -306,3 +306,25 @@ void or_combine32(int k, int H, const float* w, const float* out, float* y) {
         y[n] = s;
     }
 }
+
+/* ------------------------------------------------- dense FP8 projections */
+
+/* y[r][n] = sum over k of bf16(x[r][k]) * e4m3fn(w[n][k]) * s[n/128][k/128],
+ * in float64 with k ascending; R rows of x [R][K] (bf16 bits), w [N][K] E4M3FN
+ * bytes, s [ceil(N/128)][K/128] float. The dense FP8 projections are the
+ * other weight stream of a decode layer (the 6-16-row matrix-tile commit,
+ * #2973, in [#2983]'s commit list); the pages give no scale layout, so the
+ * reading is the released FP8 checkpoints' one: one scale per 128 x 128 block
+ * of the weight matrix, multiplying the decoded bytes. */
+void or_fp8_proj(int R, int N, int K, const uint16_t* x, const uint8_t* w, const float* s, double* y) {
+    const int KB = K / 128;
+    for (int r = 0; r < R; ++r)
+        for (int n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int k = 0; k < K; ++k) {
+                double wv = or_e4m3fn(w[(size_t)n * K + k]) * (double)s[(size_t)(n / 128) * KB + k / 128];
+                acc += or_bf16(x[(size_t)r * K + k]) * wv;
+            }
+            y[(size_t)r * N + n] = acc;
+        }
+}

@@ -29,6 +29,7 @@ M2 = 0x94D049BB133111EB
 # stream (tensor) ids
 GATE_CODES, GATE_SCALES, UP_CODES, UP_SCALES, DOWN_CODES, DOWN_SCALES = 1, 2, 3, 4, 5, 6
 X, LOGITS, BIAS, PLANT = 7, 8, 9, 10
+FP8_WEIGHTS, FP8_SCALES = 11, 12
 MATRICES = {
     "gate": (GATE_CODES, GATE_SCALES),
     "up": (UP_CODES, UP_SCALES),
@@ -92,6 +93,26 @@ def expert(seed: int, layer: int, e: int, H: int, I: int, emin: int, emax: int) 
         down_codes=codes(seed, layer, e, DOWN_CODES, H, I),
         down_scales=scales(seed, layer, e, DOWN_SCALES, H, I, emin, emax),
     )
+
+
+# ------------------------------------------------ dense FP8 projections
+def fp8_weights(seed: int, layer: int, N: int, K: int) -> np.ndarray:
+    """E4M3FN bytes [N][K], uniform over the 254 non-NaN codes (0x7F and 0xFF
+    are skipped): output i of the stream gives byte i from its high 32 bits."""
+    w = stream(stream_key(seed, layer, FP8_WEIGHTS), 0, N * K)
+    b = ((w >> np.uint64(32)) * np.uint64(254)) >> np.uint64(32)
+    b = np.where(b >= np.uint64(0x7F), b + np.uint64(1), b)
+    return b.astype(np.uint8).reshape(N, K)
+
+
+def fp8_scales(seed: int, layer: int, N: int, K: int, emin: int = -10, emax: int = -6) -> np.ndarray:
+    """fp32 scales 2^e, e uniform on {emin..emax}, one per 128 x 128 block:
+    [ceil(N/128)][K/128]."""
+    nb, kb = (N + 127) // 128, K // 128
+    n = np.uint64(emax - emin + 1)
+    w = stream(stream_key(seed, layer, FP8_SCALES), 0, nb * kb)
+    e = (((w >> np.uint64(32)) * n) >> np.uint64(32)).astype(np.int64) + emin
+    return np.ldexp(np.ones(nb * kb, dtype=np.float32), e.astype(np.int32)).reshape(nb, kb)
 
 
 # --------------------------------------------------------- float streams

@@ -55,3 +55,16 @@ def test_plant_positions():
     f = synth.bf16_bits_to_f32(xp)
     assert np.isnan(f[nr, nc]) and f[ir, ic] == np.inf
     assert int(np.sum(~np.isfinite(f))) == 2
+
+
+def test_fp8_generators():
+    w = synth.fp8_weights(5, 1, 64, 512)
+    assert w.shape == (64, 512) and w.dtype == np.uint8
+    assert not np.any((w == 0x7F) | (w == 0xFF))          # no NaN codes
+    assert np.unique(w).size == 254
+    assert np.array_equal(w, synth.fp8_weights(5, 1, 64, 512))
+    assert not np.array_equal(w, synth.fp8_weights(5, 2, 64, 512))
+    s = synth.fp8_scales(5, 1, 300, 512, -10, -6)
+    assert s.shape == (3, 4) and s.dtype == np.float32
+    e = np.log2(s)
+    assert np.all(e == np.round(e)) and e.min() >= -10 and e.max() <= -6
