@@ -1,0 +1,230 @@
+// xp_fp8.hip — dense FP8 projections for decode rows: y = x W^T with W stored
+// as E4M3FN bytes and one fp32 scale per 128 x 128 block, x bf16, y fp32.
+//
+// Source: the matrix-tile commit for the FP8 projections (#2973) listed on the
+// TensorFold page "dsv41 metal: decode experts decode an expert's weights once
+// for all of its rows" (#2983), commit list: a row's bits do not depend on how
+// many rows share the launch or on how K is split across the workgroup, because
+// every K-piece's partial result starts from zero and the pieces meet in one
+// fixed, zero-padded pair tree.
+//
+// Arithmetic of one output y[r][n] (every launch form computes exactly this):
+//   block root  q_j = four v_mfma_f32_16x16x32_bf16 steps from +0 over the 128 k
+//                     of block j, in k order (32 k per step);
+//   leaf        c_j = q_j * s[n / 128][j]          (one fp32 multiply);
+//   y          = pair tree over j = 0 .. P-1, P the power of two >= K/128, with
+//                c_j = +0 for j >= K/128; level by level, node = left + right.
+// A row's matrix-core result depends only on its own row of x and the weights,
+// so rows never interact; padding rows of a 16-row tile are zero and unstored.
+//
+// Launch: one workgroup per 16 output columns; its S waves ("slices") each own
+// an aligned run of P/S blocks, hold that run's weights in registers for all
+// row tiles, reduce their leaves by the low levels of the tree, and meet in LDS
+// for the top log2(S) levels. S is a free choice (1..16): the bits are the same.
+#include "xp_common.h"
+
+namespace xp {
+namespace fp8 {
+
+constexpr int kCols = 16;        // output columns per workgroup (one MFMA tile)
+constexpr int kBlock = 128;      // k per scale block
+constexpr int kBlockBytes = 2048;  // packed bytes of one (16-column tile, block)
+constexpr int kMaxSlices = 16;
+constexpr int kMaxRun = 4;       // blocks per slice held in registers
+constexpr int kMaxBlocks = kMaxSlices * kMaxRun;  // K <= 8192
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4v;
+
+// Eight E4M3FN bytes (two dwords, k order from the low byte) to eight bf16:
+// exact, every E4M3FN value is a bf16 value.
+__device__ __forceinline__ bf16x8 group_bf16(uint32_t d0, uint32_t d1) {
+    const u32x4v r = u32x4v{
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, true)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true))};
+    return __builtin_bit_cast(bf16x8, r);
+}
+
+// The operands one slice works on: its weights (32 bytes per lane per block:
+// groups 0..3, 8 k each) and scales, and its lane's row of x.
+template <int RUN>
+struct Slice {
+    u32x4v w[RUN][2];
+    float sc[RUN];
+    const uint16_t* xr;  // row of x for this lane's A operand, at k = 8q
+    bool row_ok;
+    int j0, KB;
+};
+
+// Leaf j0 + b: four matrix-core steps from +0 over the block's 128 k in k
+// order, then the block scale; +0 for a padding block.
+template <int RUN>
+__device__ __forceinline__ f32x4 leaf(const Slice<RUN>& sl, int b) {
+    const int j = sl.j0 + b;
+    if (j >= sl.KB) return f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 a[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const u32x4v av = sl.row_ok ? *(const u32x4v*)(sl.xr + (size_t)j * kBlock + 32 * g) : u32x4v{0, 0, 0, 0};
+        a[g] = __builtin_bit_cast(bf16x8, av);
+    }
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], group_bf16(sl.w[b][0].x, sl.w[b][0].y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], group_bf16(sl.w[b][0].z, sl.w[b][0].w), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2], group_bf16(sl.w[b][1].x, sl.w[b][1].y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[3], group_bf16(sl.w[b][1].z, sl.w[b][1].w), acc, 0, 0, 0);
+    return acc * sl.sc[b];
+}
+
+// Root of the aligned run of LEN leaves starting at b0: (left subtree) + (right subtree).
+template <int RUN, int LEN>
+struct Run {
+    static __device__ __forceinline__ f32x4 root(const Slice<RUN>& sl, int b0) {
+        const f32x4 l = Run<RUN, LEN / 2>::root(sl, b0);
+        const f32x4 r = Run<RUN, LEN / 2>::root(sl, b0 + LEN / 2);
+        return l + r;
+    }
+};
+template <int RUN>
+struct Run<RUN, 1> {
+    static __device__ __forceinline__ f32x4 root(const Slice<RUN>& sl, int b0) { return leaf<RUN>(sl, b0); }
+};
+
+// One workgroup: 16 columns [16t, 16t + 16), all rows. RUN = blocks per slice.
+template <int RUN>
+__global__ __launch_bounds__(1024) void fp8_rows_kernel(int R, int N, int KB, const uint16_t* __restrict__ x,
+                                                        const uint8_t* __restrict__ pw,
+                                                        const float* __restrict__ scale, float* __restrict__ y) {
+    __shared__ float red[kMaxSlices * 4 * 64];
+    const int S = blockDim.x >> 6;
+    const int slice = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int c = lane & 15, q = lane >> 4;
+    const int t = blockIdx.x;
+    const int K = KB * kBlock;
+
+    Slice<RUN> sl;
+    sl.j0 = slice * RUN;
+    sl.KB = KB;
+    const float* srow = scale + (size_t)(t >> 3) * KB;
+#pragma unroll
+    for (int b = 0; b < RUN; ++b) {
+        const int j = sl.j0 + b;
+        if (j < KB) {
+            const u32x4v* p = (const u32x4v*)(pw + ((size_t)t * KB + j) * kBlockBytes + lane * 32);
+            sl.w[b][0] = __builtin_nontemporal_load(p);
+            sl.w[b][1] = __builtin_nontemporal_load(p + 1);
+            sl.sc[b] = srow[j];
+        } else {
+            sl.w[b][0] = u32x4v{0, 0, 0, 0};
+            sl.w[b][1] = u32x4v{0, 0, 0, 0};
+            sl.sc[b] = 0.0f;
+        }
+    }
+
+    for (int m0 = 0; m0 < R; m0 += 16) {
+        const int ra = m0 + c;  // this lane's row of the A operand
+        sl.row_ok = ra < R;
+        sl.xr = x + (size_t)(sl.row_ok ? ra : 0) * K + 8 * q;
+        // low levels of the pair tree: the slice's run
+        const f32x4 v = Run<RUN, RUN>::root(sl, 0);
+        if (S == 1) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = m0 + 4 * q + i;  // C row 4q + i, column c
+                if (r < R) y[(size_t)r * N + (size_t)t * kCols + c] = v[i];
+            }
+            continue;
+        }
+        // top levels across slices, through LDS; wave i finishes C rows 4q + i
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[(slice * 4 + i) * 64 + lane] = v[i];
+        __syncthreads();
+        for (int i = slice; i < 4; i += S) {
+            float u[kMaxSlices];
+#pragma unroll
+            for (int s = 0; s < kMaxSlices; ++s) u[s] = s < S ? red[(s * 4 + i) * 64 + lane] : 0.0f;
+#pragma unroll
+            for (int st = 1; st < kMaxSlices; st *= 2)
+#pragma unroll
+                for (int s = 0; s < kMaxSlices; s += 2 * st)
+                    if (s + st < S) u[s] = u[s] + u[s + st];
+            const int r = m0 + 4 * q + i;
+            if (r < R) y[(size_t)r * N + (size_t)t * kCols + c] = u[0];
+        }
+        __syncthreads();
+    }
+}
+
+// Plain [N][K] bytes -> the kernel's tiles: per (16-column tile t, block j)
+// 2,048 bytes, lane l's 32 at l * 32: for groups g = 0..3, the 8 bytes of
+// column 16t + l % 16 at k = 128j + 32g + 8(l / 16) .. +7.
+__global__ __launch_bounds__(256) void fp8_pack_kernel(int N, int K, const uint8_t* __restrict__ w,
+                                                       uint8_t* __restrict__ pw) {
+    const int KB = K / kBlock;
+    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (size_t)(N / kCols) * KB * 64) return;
+    const int lane = (int)(idx & 63);
+    const size_t tj = idx >> 6;
+    const int t = (int)(tj / KB), j = (int)(tj - (size_t)t * KB);
+    const int n = t * kCols + (lane & 15);
+    const uint8_t* src = w + (size_t)n * K + (size_t)j * kBlock + 8 * (lane >> 4);
+    uint2* dst = (uint2*)(pw + tj * kBlockBytes + lane * 32);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) dst[g] = *(const uint2*)(src + 32 * g);
+}
+
+static int next_pow2(int v) {
+    int p = 1;
+    while (p < v) p *= 2;
+    return p;
+}
+
+}  // namespace fp8
+}  // namespace xp
+
+using namespace xp;
+using namespace xp::fp8;
+
+static bool fp8_shape_ok(int32_t n, int32_t k) {
+    return n > 0 && k > 0 && n % kCols == 0 && k % kBlock == 0 && k / kBlock <= kMaxBlocks;
+}
+
+XP_API size_t xp_fp8_packed_bytes(int32_t n, int32_t k) {
+    return fp8_shape_ok(n, k) ? (size_t)n * (size_t)k : 0;
+}
+
+XP_API int xp_fp8_pack(int32_t n, int32_t k, const uint8_t* w, uint8_t* packed, void* stream) {
+    if (!fp8_shape_ok(n, k)) return XP_ERR_SHAPE;
+    if (!w || !packed) return XP_ERR_NULL;
+    const size_t threads = (size_t)(n / kCols) * (k / kBlock) * 64;
+    const unsigned grid = (unsigned)((threads + 255) / 256);
+    hipLaunchKernelGGL(fp8_pack_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, n, k, w, packed);
+    return launch_status();
+}
+
+XP_API int xp_fp8_rows(int32_t rows, int32_t n, int32_t k, const uint16_t* x, const uint8_t* packed,
+                       const float* scales, float* y, int32_t slices, void* stream) {
+    if (!fp8_shape_ok(n, k) || rows < 0) return XP_ERR_SHAPE;
+    if (rows == 0) return XP_OK;
+    if (!x || !packed || !scales || !y) return XP_ERR_NULL;
+    const int KB = k / kBlock;
+    const int P = next_pow2(KB);
+    int S = slices;
+    if (S == 0) S = P < kMaxSlices ? P : kMaxSlices;
+    if (S < 1 || S > kMaxSlices || (S & (S - 1)) != 0 || S > P) return XP_ERR_SHAPE;
+    const int run = P / S;
+    if (run > kMaxRun) return XP_ERR_SHAPE;
+    hipStream_t s = (hipStream_t)stream;
+    const dim3 grid(n / kCols), block(64 * S);
+    switch (run) {
+        case 1: hipLaunchKernelGGL(fp8_rows_kernel<1>, grid, block, 0, s, rows, n, KB, x, packed, scales, y); break;
+        case 2: hipLaunchKernelGGL(fp8_rows_kernel<2>, grid, block, 0, s, rows, n, KB, x, packed, scales, y); break;
+        case 4: hipLaunchKernelGGL(fp8_rows_kernel<4>, grid, block, 0, s, rows, n, KB, x, packed, scales, y); break;
+        default: return XP_ERR_SHAPE;
+    }
+    return launch_status();
+}

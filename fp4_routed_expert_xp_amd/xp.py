@@ -22,7 +22,7 @@ EXPORTS = (
     "xp_pack_matrix", "xp_workspace_bytes", "xp_workspace_layout", "xp_route_bucket",
     "xp_gateup_rows", "xp_gateup_rows_split", "xp_down_rows", "xp_combine",
     "xp_set_tiers", "xp_get_tiers", "xp_status_string", "xp_route_gateup", "xp_down_combine",
-    "xp_prefill_gateup", "xp_prefill_down",
+    "xp_prefill_gateup", "xp_prefill_down", "xp_fp8_packed_bytes", "xp_fp8_pack", "xp_fp8_rows",
 )
 
 
@@ -71,13 +71,18 @@ def lib():
         L.xp_down_combine.argtypes = [D, i32, P, P, P, P, sz, P, P, P]
         L.xp_prefill_gateup.argtypes = [D, i32, P, P, P, sz, P, P]
         L.xp_prefill_down.argtypes = [D, i32, P, P, P, sz, P, P]
+        L.xp_fp8_packed_bytes.argtypes = [i32, i32]
+        L.xp_fp8_packed_bytes.restype = sz
+        L.xp_fp8_pack.argtypes = [i32, i32, P, P, P]
+        L.xp_fp8_rows.argtypes = [i32, i32, i32, P, P, P, P, i32, P]
         L.xp_set_tiers.argtypes = [P, i32, P, i32]
         L.xp_get_tiers.argtypes = [P, P, P, P]
         L.xp_status_string.argtypes = [ctypes.c_int]
         L.xp_status_string.restype = ctypes.c_char_p
         for name in ("xp_pack_matrix", "xp_workspace_layout", "xp_route_bucket", "xp_gateup_rows",
                      "xp_gateup_rows_split", "xp_down_rows", "xp_combine", "xp_set_tiers", "xp_get_tiers",
-                     "xp_route_gateup", "xp_down_combine", "xp_prefill_gateup", "xp_prefill_down"):
+                     "xp_route_gateup", "xp_down_combine", "xp_prefill_gateup", "xp_prefill_down",
+                     "xp_fp8_pack", "xp_fp8_rows"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -263,6 +268,29 @@ def xp_prefill_down(d: xp_dims, rows: int, act, experts, workspace, out, stream=
     nbytes = workspace.numel() if workspace is not None else 0
     _check(lib().xp_prefill_down(ctypes.byref(d), int(rows), _ptr(act), _ptr(experts), _ptr(workspace), nbytes,
                                  _ptr(out), _stream(stream)), "xp_prefill_down")
+
+
+def xp_fp8_packed_bytes(n: int, k: int) -> int:
+    return int(lib().xp_fp8_packed_bytes(int(n), int(k)))
+
+
+def xp_fp8_pack(w, packed, stream=None) -> None:
+    """Repack a [n][k] E4M3FN byte matrix (uint8 device tensor) into ``packed``."""
+    n, k = (w.shape[0], w.shape[1]) if isinstance(w, torch.Tensor) and w.dim() == 2 else (0, 0)
+    _dev(w, torch.uint8, "w")
+    _dev(packed, torch.uint8, "packed", n * k)
+    _check(lib().xp_fp8_pack(int(n), int(k), _ptr(w), _ptr(packed), _stream(stream)), "xp_fp8_pack")
+
+
+def xp_fp8_rows(rows: int, n: int, k: int, x, packed, scales, y, slices: int = 0, stream=None) -> None:
+    """y[rows][n] fp32 = x[rows][k] (bf16) times the packed FP8 matrix (see xp_fp8_rows in xp.h)."""
+    if rows > 0:
+        _dev_bf16(x, "x", rows * k)
+        _dev(packed, torch.uint8, "packed", n * k)
+        _dev(scales, torch.float32, "scales", ((n + 127) // 128) * (k // 128))
+        _dev(y, torch.float32, "y", rows * n)
+    _check(lib().xp_fp8_rows(int(rows), int(n), int(k), _ptr(x), _ptr(packed), _ptr(scales), _ptr(y),
+                             int(slices), _stream(stream)), "xp_fp8_rows")
 
 
 # -------------------------------------------------------------- conveniences

@@ -193,6 +193,45 @@ int xp_prefill_gateup(const xp_dims* dims, int32_t rows, const uint16_t* x, cons
 int xp_prefill_down(const xp_dims* dims, int32_t rows, const float* act, const xp_expert* experts,
                     const void* workspace, size_t ws_bytes, float* out, void* stream);
 
+/* ------------------------------------------------- dense FP8 projections
+ * The decode layer's other weight stream: y = x W^T for a dense projection
+ * whose weights are E4M3FN bytes with one fp32 scale per 128 x 128 block
+ * (value = byte * scale), x bf16 rows, y fp32. A row's result never depends on
+ * how many rows share the launch, nor on the `slices` form chosen: [#2983,
+ * commit list: the matrix-tile commit for the FP8 projections (#2973), which
+ * keeps a row's bits equal to its one-row launch].
+ *
+ * Arithmetic of y[r][n] (the same in every form and at every row count):
+ *   q_j = four v_mfma_f32_16x16x32_bf16 steps from +0 over block j's 128 k, in k order;
+ *   c_j = q_j * s[n / 128][j];
+ *   y   = pair tree over j in [0, P), P = the power of two >= K/128, with c_j = +0
+ *         for j >= K/128, combined level by level as left + right.
+ * The products are exact (E4M3FN values are bf16 values) and the sums are the
+ * matrix cores' fp32 sums, so y meets the per-row tolerance against the float64
+ * definition (max |err| / max |ref| <= 1e-3) and is bit-equal across row counts
+ * and forms, not to a sequential fma chain.
+ *
+ * Shapes: n a positive multiple of 16; k a positive multiple of 128 with
+ * k / 128 <= 128. Scales: fp32 [ceil(n/128)][k/128], row-major (a partial last
+ * block of columns uses its block's scale). */
+
+/* Bytes of the packed layout of an n x k matrix (n * k), or 0 for a shape the
+ * kernels do not take. */
+size_t xp_fp8_packed_bytes(int32_t n, int32_t k);
+
+/* Repack w [n][k] (row n = output column n, E4M3FN bytes, k contiguous) into
+ * the kernel's layout: per 16-column tile and 128-k block, 2,048 bytes, lane
+ * l's 32 bytes at l*32 holding, for g = 0..3, the 8 bytes of column
+ * 16*tile + l%16 at k = 128*block + 32g + 8*(l/16) .. +7. One-time setup. */
+int xp_fp8_pack(int32_t n, int32_t k, const uint8_t* w, uint8_t* packed, void* stream);
+
+/* y[rows][n] fp32 = x[rows][k] (bf16 bit patterns, 16-byte aligned) times the
+ * packed matrix, scaled per block. slices: 0 picks the form (min(16, P) waves
+ * per 16 columns); 1, 2, 4, 8 or 16 forces that many (at most P, and P/slices
+ * <= 8), else XP_ERR_SHAPE. Any row count >= 0. */
+int xp_fp8_rows(int32_t rows, int32_t n, int32_t k, const uint16_t* x, const uint8_t* packed,
+                const float* scales, float* y, int32_t slices, void* stream);
+
 /* ------------------------------------------------------------ pass sizes */
 
 /* Set the pass sizes used by later xp_route_bucket calls (host, process-wide,

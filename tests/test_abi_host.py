@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "xp.h")
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(xp_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(xp_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_declares_the_binding_exports():
@@ -121,3 +121,21 @@ def test_tiers_set_get_and_refusals():
     finally:
         xp.xp_set_tiers(None, None)
     assert xp.xp_get_tiers() == ([2, 4, 6, 8], [2, 4])
+
+
+def test_fp8_argument_checks():
+    L = xp.lib()
+    P = ctypes.c_void_p(16)
+    assert xp.xp_fp8_packed_bytes(576, 4096) == 576 * 4096
+    for n, k in ((100, 4096), (576, 4000), (0, 128), (16, 0), (16, 128 * 65)):
+        assert xp.xp_fp8_packed_bytes(n, k) == 0, (n, k)
+        assert L.xp_fp8_pack(n, k, P, P, None) == xp.XP_ERR_SHAPE
+        assert L.xp_fp8_rows(1, n, k, P, P, P, P, 0, None) == xp.XP_ERR_SHAPE
+    assert L.xp_fp8_pack(16, 128, None, P, None) == xp.XP_ERR_NULL
+    assert L.xp_fp8_rows(1, 16, 128, P, None, P, P, 0, None) == xp.XP_ERR_NULL
+    assert L.xp_fp8_rows(-1, 16, 128, P, P, P, P, 0, None) == xp.XP_ERR_SHAPE
+    assert L.xp_fp8_rows(0, 16, 128, None, None, None, None, 0, None) == xp.XP_OK
+    # forms: a power of two up to 16, at most P = next power of two of k/128, P/slices <= 4
+    for slices in (3, 32, -1, 8):
+        assert L.xp_fp8_rows(1, 16, 512, P, P, P, P, slices, None) == xp.XP_ERR_SHAPE, slices
+    assert L.xp_fp8_rows(1, 16, 128 * 40, P, P, P, P, 4, None) == xp.XP_ERR_SHAPE  # P = 64: 16 blocks a slice
