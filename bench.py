@@ -71,7 +71,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--layers", type=int, default=40)
-    ap.add_argument("--cells", default="one_row,four_same,sixteen_random,prefill")
+    ap.add_argument("--cells", default="one_row,four_same,sixteen_random,prefill,fp8_rows")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-tier-sweep", action="store_true", help="skip the pass-size sweep cells")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU work budget of the oracle sample")
@@ -330,6 +330,87 @@ def prefill_report(cell: Cell, t: dict) -> dict:
     )
 
 
+# ------------------------------------------------- dense FP8 projections
+# A decode layer's dense FP8 projections at the layer's hidden width (synthetic
+# shapes, N x K): a narrow one with a ragged last 128-column block, a medium, a
+# square and one with K = 2048. E4M3FN weights, one fp32 scale per 128 x 128.
+FP8_SHAPES = ((576, 4096), (1536, 4096), (4096, 4096), (4096, 2048))
+FP8_ROWS = (1, 8, 16)
+FP8_SEEDED_SETS = 4     # distinct seeded weight sets; the 40 layers hold copies in their own buffers
+
+
+class Fp8Cell:
+    """40 layers of the FP8 projection set, each in its own device buffers."""
+
+    def __init__(self, layers: int):
+        import numpy as np
+        import torch
+        import synth
+        from fp4_routed_expert_xp_amd import xp
+        self.layers = layers
+        seeded = []
+        for l in range(min(layers, FP8_SEEDED_SETS)):
+            mats = []
+            for i, (N, K) in enumerate(FP8_SHAPES):
+                w = torch.from_numpy(synth.fp8_weights(5001, 16 * l + i, N, K)).cuda()
+                packed = torch.empty(N * K, dtype=torch.uint8, device="cuda")
+                xp.xp_fp8_pack(w, packed)
+                sc = torch.from_numpy(synth.fp8_scales(5001, 16 * l + i, N, K)).cuda()
+                mats.append((packed, sc))
+            seeded.append(mats)
+        self.mats = [[(p.clone(), sc.clone()) for p, sc in seeded[l % len(seeded)]] for l in range(layers)]
+        del seeded
+        rmax = max(FP8_ROWS)
+        kmax = max(K for _, K in FP8_SHAPES)
+        nmax = max(N for N, _ in FP8_SHAPES)
+        xb = synth.activations(5002, 0, rmax, kmax)
+        self.x = torch.from_numpy(xb.view(np.int16).copy()).cuda()
+        self.y = torch.empty((rmax, nmax), dtype=torch.float32, device="cuda")
+        self.set_bytes = sum(N * K + ((N + 127) // 128) * (K // 128) * 4 for N, K in FP8_SHAPES)
+        torch.cuda.synchronize()
+
+
+def time_fp8(cell: Fp8Cell, steps: int, warmup: int) -> dict:
+    """Per row count: the round (every projection of every layer, one graph) and
+    each shape alone (a graph of that shape over the layers)."""
+    import torch
+    out = {}
+    for R in FP8_ROWS:
+        xs = {K: cell.x[:R, :K].contiguous() for _, K in FP8_SHAPES}
+
+        def run(i, l):
+            from fp4_routed_expert_xp_amd import xp
+            N, K = FP8_SHAPES[i]
+            packed, sc = cell.mats[l][i]
+            xp.xp_fp8_rows(R, N, K, xs[K], packed, sc, cell.y, 0)
+
+        def rnd():
+            for l in range(cell.layers):
+                for i in range(len(FP8_SHAPES)):
+                    run(i, l)
+        rnd()
+        torch.cuda.synchronize()
+        g = _graph(rnd)
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        ms = _replay_ms(g, steps)
+        del g
+        per = {}
+        for i, (N, K) in enumerate(FP8_SHAPES):
+            gk = _graph(lambda: [run(i, l) for l in range(cell.layers)])
+            gk.replay()
+            torch.cuda.synchronize()
+            per["%dx%d" % (N, K)] = round(_replay_ms(gk, 5) * 1e3 / cell.layers, 3)
+            del gk
+        layer_us = ms * 1e3 / cell.layers
+        out[R] = dict(rows=R, round_ms=round(ms, 4), layer_us=round(layer_us, 3),
+                      weight_gbps=round(cell.set_bytes / (layer_us * 1e-6) / 1e9, 1),
+                      pct_hbm_peak=round(100 * cell.set_bytes / (layer_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 2),
+                      kernel_us=per)
+    return out
+
+
 # ------------------------------------------------------------ CPU baseline
 def cpu_baseline(budget_s: float) -> dict:
     """The float64 oracle, untuned, on this host's cores: one-row layers of the
@@ -382,6 +463,15 @@ def main():
     log("plain copy bandwidth %.0f GB/s" % copy_gbps)
     reports, timings = {}, {}
     for name in cells:
+        if name == "fp8_rows":
+            fcell = Fp8Cell(args.layers)
+            for R, rep in time_fp8(fcell, args.steps, args.warmup).items():
+                rep["bytes_per_layer"] = fcell.set_bytes
+                rep["shapes"] = ["%dx%d" % s for s in FP8_SHAPES]
+                reports["fp8_rows/%d" % R] = rep
+                log("fp8_rows/%d: %s" % (R, json.dumps(rep)))
+            del fcell
+            continue
         cfg = synth.CONFIGS[name]
         if name == "prefill":
             cell = Cell(model, cfg, min(args.layers, PREFILL_LAYERS))
@@ -413,7 +503,7 @@ def main():
                 rep["tiers"] = {"gate_up": list(gu), "down": list(dn)}
                 reports[key] = rep
                 log("%s: %s" % (key, json.dumps(rep)))
-    decode = [c for c in cells if c != "prefill"]
+    decode = [c for c in cells if c not in ("prefill", "fp8_rows")]
     if not decode:
         log("the headline is a decode workload: name one of one_row, four_same, sixteen_random in --cells")
         sys.exit(2)
@@ -458,6 +548,16 @@ def main():
             "achieved": pf["gateup_tflops"], "flops_per_launch": 4 * cfg.H * cfg.I * cfg.R * cfg.k,
             "launch_us": pf["kernel_us"]["prefill_gateup"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(pf["gateup_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+    fp8 = [reports[k] for k in ("fp8_rows/1", "fp8_rows/16") if k in reports]
+    if fp8:
+        N, K = 4096, 4096
+        us = fp8[0]["kernel_us"]["%dx%d" % (N, K)]
+        nbytes = N * K + (N // 128) * (K // 128) * 4 + 2 * K + 4 * N
+        line["fp8_roofline"] = {
+            "kernel": "fp8_rows_kernel (xp_fp8_rows, %dx%d, %d row)" % (N, K, fp8[0]["rows"]), "bound": "hbm",
+            "achieved": round(nbytes / (us * 1e-6) / 1e9, 1), "bytes_per_launch": nbytes, "launch_us": us,
+            "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "traffic": None}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

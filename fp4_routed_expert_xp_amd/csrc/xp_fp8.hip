@@ -49,40 +49,58 @@ __device__ __forceinline__ bf16x8 group_bf16(uint32_t d0, uint32_t d1) {
 }
 
 // The operands one slice works on: its weights (32 bytes per lane per block:
-// groups 0..3, 8 k each) and scales, and its lane's row of x.
+// groups 0..3, 8 k each) and scales, and, for the current 16-row tile, its
+// lane's row of x (zeroed for rows past the end) for up to two blocks at a time.
+constexpr int kXBlocks = 2;
+
 template <int RUN>
 struct Slice {
     u32x4v w[RUN][2];
     float sc[RUN];
-    const uint16_t* xr;  // row of x for this lane's A operand, at k = 8q
+    u32x4v a[kXBlocks][4];
+    const uint16_t* xr;  // lane (c, q): row m0 + c (clamped) of x, at k = 8q
     bool row_ok;
     int j0, KB;
 };
 
-// Leaf j0 + b: four matrix-core steps from +0 over the block's 128 k in k
-// order, then the block scale; +0 for a padding block.
+// x of blocks b0 .. b0+n-1 of the run (n <= 2): k = 128j + 32g + 8q .. +7.
 template <int RUN>
-__device__ __forceinline__ f32x4 leaf(const Slice<RUN>& sl, int b) {
-    const int j = sl.j0 + b;
-    if (j >= sl.KB) return f32x4{0.f, 0.f, 0.f, 0.f};
-    bf16x8 a[4];
+__device__ __forceinline__ void load_x(Slice<RUN>& sl, int b0, int n) {
+    for (int i = 0; i < n; ++i) {
+        const int j = min(sl.j0 + b0 + i, sl.KB - 1);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const u32x4v av = sl.row_ok ? *(const u32x4v*)(sl.xr + (size_t)j * kBlock + 32 * g) : u32x4v{0, 0, 0, 0};
-        a[g] = __builtin_bit_cast(bf16x8, av);
+        for (int g = 0; g < 4; ++g) {
+            const u32x4v v = *(const u32x4v*)(sl.xr + (size_t)j * kBlock + 32 * g);
+            sl.a[i][g] = sl.row_ok ? v : u32x4v{0, 0, 0, 0};
+        }
     }
+}
+
+// Leaf j0 + b: four matrix-core steps from +0 over the block's 128 k in k
+// order, then the block scale; +0 for a padding block. ai: its slot in a[].
+template <int RUN>
+__device__ __forceinline__ f32x4 leaf(Slice<RUN>& sl, int b, int ai) {
+    if (sl.j0 + b >= sl.KB) return f32x4{0.f, 0.f, 0.f, 0.f};
+    // decode here, per row tile, so the x loads above are not held behind the weights
+    asm volatile("" : "+v"(sl.w[b][0]), "+v"(sl.w[b][1]));
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], group_bf16(sl.w[b][0].x, sl.w[b][0].y), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], group_bf16(sl.w[b][0].z, sl.w[b][0].w), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2], group_bf16(sl.w[b][1].x, sl.w[b][1].y), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[3], group_bf16(sl.w[b][1].z, sl.w[b][1].w), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, sl.a[ai][0]),
+                                                  group_bf16(sl.w[b][0].x, sl.w[b][0].y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, sl.a[ai][1]),
+                                                  group_bf16(sl.w[b][0].z, sl.w[b][0].w), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, sl.a[ai][2]),
+                                                  group_bf16(sl.w[b][1].x, sl.w[b][1].y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, sl.a[ai][3]),
+                                                  group_bf16(sl.w[b][1].z, sl.w[b][1].w), acc, 0, 0, 0);
     return acc * sl.sc[b];
 }
 
-// Root of the aligned run of LEN leaves starting at b0: (left subtree) + (right subtree).
+// Root of the aligned run of LEN leaves starting at b0: (left subtree) + (right
+// subtree). The x of a subtree of up to two blocks is loaded on entering it.
 template <int RUN, int LEN>
 struct Run {
-    static __device__ __forceinline__ f32x4 root(const Slice<RUN>& sl, int b0) {
+    static __device__ __forceinline__ f32x4 root(Slice<RUN>& sl, int b0) {
+        if constexpr (LEN == kXBlocks) load_x(sl, b0, LEN);
         const f32x4 l = Run<RUN, LEN / 2>::root(sl, b0);
         const f32x4 r = Run<RUN, LEN / 2>::root(sl, b0 + LEN / 2);
         return l + r;
@@ -90,7 +108,10 @@ struct Run {
 };
 template <int RUN>
 struct Run<RUN, 1> {
-    static __device__ __forceinline__ f32x4 root(const Slice<RUN>& sl, int b0) { return leaf<RUN>(sl, b0); }
+    static __device__ __forceinline__ f32x4 root(Slice<RUN>& sl, int b0) {
+        if constexpr (RUN == 1) load_x(sl, b0, 1);
+        return leaf<RUN>(sl, b0, b0 % kXBlocks);
+    }
 };
 
 // One workgroup: 16 columns [16t, 16t + 16), all rows. RUN = blocks per slice.
@@ -126,9 +147,9 @@ __global__ __launch_bounds__(1024) void fp8_rows_kernel(int R, int N, int KB, co
     }
 
     for (int m0 = 0; m0 < R; m0 += 16) {
-        const int ra = m0 + c;  // this lane's row of the A operand
+        const int ra = m0 + c;
         sl.row_ok = ra < R;
-        sl.xr = x + (size_t)(sl.row_ok ? ra : 0) * K + 8 * q;
+        sl.xr = x + (size_t)(sl.row_ok ? ra : R - 1) * K + 8 * q;
         // low levels of the pair tree: the slice's run
         const f32x4 v = Run<RUN, RUN>::root(sl, 0);
         if (S == 1) {
