@@ -21,6 +21,9 @@
 // an aligned run of P/S blocks, hold that run's weights in registers for all
 // row tiles, reduce their leaves by the low levels of the tree, and meet in LDS
 // for the top log2(S) levels. S is a free choice (1..16): the bits are the same.
+// Each wave stages its rows of x for two blocks at a time in its own LDS chunk
+// with whole-row loads (reading the matrix-core fragments straight from global
+// memory touches sixteen rows per instruction and cost about 2.5 us at 16 rows).
 #include "xp_common.h"
 
 namespace xp {
@@ -49,54 +52,63 @@ __device__ __forceinline__ bf16x8 group_bf16(uint32_t d0, uint32_t d1) {
 }
 
 // The operands one slice works on: its weights (32 bytes per lane per block:
-// groups 0..3, 8 k each) and scales, and, for the current 16-row tile, its
-// lane's row of x (zeroed for rows past the end) for up to two blocks at a time.
+// groups 0..3, 8 k each) and scales, and its LDS chunk of x for the current
+// 16-row tile (two blocks at a time).
 constexpr int kXBlocks = 2;
+constexpr int kXRow = 33;   // LDS row of a wave's x chunk: 256 k (512 B) + 16 B pad, in 16-B units
 
 template <int RUN>
 struct Slice {
     u32x4v w[RUN][2];
     float sc[RUN];
-    u32x4v a[kXBlocks][4];
-    const uint16_t* xr;  // lane (c, q): row m0 + c (clamped) of x, at k = 8q
-    bool row_ok;
+    u32x4v* xs;          // this wave's LDS x chunk: 16 rows x kXRow
+    const uint16_t* x;
+    int R, K, m0;
+    bool row_ok;         // row m0 + (lane % 16) exists
+    int lane;
     int j0, KB;
 };
 
-// x of blocks b0 .. b0+n-1 of the run (n <= 2): k = 128j + 32g + 8q .. +7.
+// Stage x of blocks b0 .. b0+n-1 (n <= 2) for rows m0 .. m0+15 in this wave's
+// LDS chunk, with whole-row coalesced loads (16 lanes per 256 B of a row).
 template <int RUN>
 __device__ __forceinline__ void load_x(Slice<RUN>& sl, int b0, int n) {
-    for (int i = 0; i < n; ++i) {
-        const int j = min(sl.j0 + b0 + i, sl.KB - 1);
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const u32x4v v = *(const u32x4v*)(sl.xr + (size_t)j * kBlock + 32 * g);
-            sl.a[i][g] = sl.row_ok ? v : u32x4v{0, 0, 0, 0};
-        }
+    const int lpr = 16 * n, rpi = 64 / lpr;
+    const int sub = sl.lane % lpr, rr = sl.lane / lpr;
+    const int jb = sl.j0 + b0;
+    for (int i = 0; i < 16 / rpi; ++i) {
+        const int rl = i * rpi + rr;
+        const int r = sl.m0 + rl;
+        if (r < sl.R && jb + (sub >> 4) < sl.KB)
+            sl.xs[rl * kXRow + sub] = *(const u32x4v*)(sl.x + (size_t)r * sl.K + (size_t)jb * kBlock + 8 * sub);
     }
 }
 
 // Leaf j0 + b: four matrix-core steps from +0 over the block's 128 k in k
-// order, then the block scale; +0 for a padding block. ai: its slot in a[].
+// order, then the block scale; +0 for a padding block. ai: the block's place in
+// the LDS chunk. A fragment: lane (c, q) holds row c at k = 32g + 8q .. +7.
 template <int RUN>
 __device__ __forceinline__ f32x4 leaf(Slice<RUN>& sl, int b, int ai) {
     if (sl.j0 + b >= sl.KB) return f32x4{0.f, 0.f, 0.f, 0.f};
-    // decode here, per row tile, so the x loads above are not held behind the weights
+    // decode here, per row tile, so the x loads are not held behind the weights
     asm volatile("" : "+v"(sl.w[b][0]), "+v"(sl.w[b][1]));
+    const int c = sl.lane & 15, q = sl.lane >> 4;
+    bf16x8 a[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const u32x4v v = sl.xs[c * kXRow + 16 * ai + 4 * g + q];
+        a[g] = __builtin_bit_cast(bf16x8, sl.row_ok ? v : u32x4v{0, 0, 0, 0});
+    }
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, sl.a[ai][0]),
-                                                  group_bf16(sl.w[b][0].x, sl.w[b][0].y), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, sl.a[ai][1]),
-                                                  group_bf16(sl.w[b][0].z, sl.w[b][0].w), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, sl.a[ai][2]),
-                                                  group_bf16(sl.w[b][1].x, sl.w[b][1].y), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, sl.a[ai][3]),
-                                                  group_bf16(sl.w[b][1].z, sl.w[b][1].w), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], group_bf16(sl.w[b][0].x, sl.w[b][0].y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], group_bf16(sl.w[b][0].z, sl.w[b][0].w), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2], group_bf16(sl.w[b][1].x, sl.w[b][1].y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[3], group_bf16(sl.w[b][1].z, sl.w[b][1].w), acc, 0, 0, 0);
     return acc * sl.sc[b];
 }
 
 // Root of the aligned run of LEN leaves starting at b0: (left subtree) + (right
-// subtree). The x of a subtree of up to two blocks is loaded on entering it.
+// subtree). The x of a two-block subtree (one block when RUN = 1) is staged on entering it.
 template <int RUN, int LEN>
 struct Run {
     static __device__ __forceinline__ f32x4 root(Slice<RUN>& sl, int b0) {
@@ -120,6 +132,7 @@ __global__ __launch_bounds__(1024) void fp8_rows_kernel(int R, int N, int KB, co
                                                         const uint8_t* __restrict__ pw,
                                                         const float* __restrict__ scale, float* __restrict__ y) {
     __shared__ float red[kMaxSlices * 4 * 64];
+    __shared__ u32x4v xsh[kMaxSlices * 16 * kXRow];
     const int S = blockDim.x >> 6;
     const int slice = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -128,6 +141,11 @@ __global__ __launch_bounds__(1024) void fp8_rows_kernel(int R, int N, int KB, co
     const int K = KB * kBlock;
 
     Slice<RUN> sl;
+    sl.xs = xsh + slice * 16 * kXRow;
+    sl.x = x;
+    sl.R = R;
+    sl.K = K;
+    sl.lane = lane;
     sl.j0 = slice * RUN;
     sl.KB = KB;
     const float* srow = scale + (size_t)(t >> 3) * KB;
@@ -147,9 +165,8 @@ __global__ __launch_bounds__(1024) void fp8_rows_kernel(int R, int N, int KB, co
     }
 
     for (int m0 = 0; m0 < R; m0 += 16) {
-        const int ra = m0 + c;
-        sl.row_ok = ra < R;
-        sl.xr = x + (size_t)(sl.row_ok ? ra : R - 1) * K + 8 * q;
+        sl.m0 = m0;
+        sl.row_ok = m0 + c < R;
         // low levels of the pair tree: the slice's run
         const f32x4 v = Run<RUN, RUN>::root(sl, 0);
         if (S == 1) {
