@@ -50,6 +50,8 @@ def lib():
         L.or_e4m3fn.restype = f64
         L.or_bf16.argtypes = [ctypes.c_uint16]
         L.or_bf16.restype = f64
+        L.or_round_bf16.argtypes = [f64]
+        L.or_round_bf16.restype = f64
         L.or_route.argtypes = [i32, i32, i32, P, P, P]
         L.or_route.restype = None
         L.or_fp8_proj.argtypes = [i32, i32, i32, P, P, P, P]
@@ -66,7 +68,7 @@ def lib():
         L.or_swiglu.restype = None
         L.or_combine.argtypes = [i32, i32, P, P, P]
         L.or_combine.restype = None
-        L.or_layer.argtypes = [i32] * 5 + [P] * 13
+        L.or_layer.argtypes = [i32] * 5 + [P] * 13 + [i32]
         L.or_layer.restype = i32
         L.or_chain32.argtypes = [i32, i32, P, P, P, P]
         L.or_chain32.restype = None
@@ -184,16 +186,26 @@ def combine(w, out) -> np.ndarray:
     return y
 
 
+def round_bf16(v) -> np.ndarray:
+    """Each float64 value rounded once to the nearest bf16 value (ties to even)."""
+    a = np.asarray(v, dtype=np.float64)
+    f = lib().or_round_bf16
+    return np.array([f(float(t)) for t in a.reshape(-1)], dtype=np.float64).reshape(a.shape)
+
+
 def bf16_to_f64(x_bits: np.ndarray) -> np.ndarray:
     b = _c(x_bits, np.uint16).astype(np.uint32) << 16
     return b.view(np.float32).astype(np.float64)
 
 
-def layer(x_bf16: np.ndarray, logits: np.ndarray, experts: dict, H: int, I: int, E: int, k: int):
+def layer(x_bf16: np.ndarray, logits: np.ndarray, experts: dict, H: int, I: int, E: int, k: int,
+          act_bf16: bool = False):
     """float64 layer over R rows.
 
     ``experts`` maps expert id -> dict with the six plain-layout arrays
     (gate_codes, gate_scales, up_codes, up_scales, down_codes, down_scales).
+    act_bf16: act is rounded to bf16 (round_bf16) before down, as in the
+    bf16-storage variant; the returned act holds the rounded values.
     Returns dict(topk_id, topk_w, act[R][k][I], out[R][k][H], y[R][H], threads).
     """
     x_bf16 = _c(x_bf16, np.uint16)
@@ -221,7 +233,7 @@ def layer(x_bf16: np.ndarray, logits: np.ndarray, experts: dict, H: int, I: int,
     if missing:
         raise KeyError("oracle.layer: experts %s are routed but not given" % sorted(missing))
     threads = lib().or_layer(H, I, E, k, R, _p(x_bf16), _p(logits), *tables,
-                             _p(topk_id), _p(topk_w), _p(act), _p(out), _p(y))
+                             _p(topk_id), _p(topk_w), _p(act), _p(out), _p(y), 1 if act_bf16 else 0)
     return dict(topk_id=topk_id, topk_w=topk_w, act=act, out=out, y=y, threads=threads)
 
 

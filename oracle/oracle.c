@@ -61,6 +61,27 @@ double or_bf16(uint16_t bits) {
     return (double)f;
 }
 
+/* Round to bf16 precision, to nearest with ties to even, once, from the exact
+ * float64 value: 8 significant bits; the exponent range of binary32, so below
+ * 2^-126 the step is 2^-133 (bf16 subnormals); a result at or above 2^128
+ * becomes infinity. NaN stays NaN, -0 stays -0. Used for the bf16 storage of
+ * act and y (reading: the stored value is the float64 definition rounded). */
+double or_round_bf16(double v) {
+    if (isnan(v) || isinf(v) || v == 0.0) return v;
+    double a = fabs(v);
+    int e;
+    frexp(a, &e);                          /* a = f * 2^e, f in [0.5, 1) */
+    int q = e - 8;                         /* step: 2^(e-8) gives 8 significant bits */
+    if (q < -133) q = -133;                /* bf16 subnormal step */
+    double m = ldexp(a, -q);               /* exact: a power-of-two scaling */
+    double r = floor(m);
+    double frac = m - r;                   /* exact */
+    if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+    double out = ldexp(r, q);
+    if (out >= ldexp(1.0, 128)) out = INFINITY;
+    return v < 0 ? -out : out;
+}
+
 static unsigned code_at(const uint8_t* codes, int K, int n, int k) {
     uint8_t b = codes[(size_t)n * (K / 2) + k / 2];
     return (k & 1) ? (b >> 4) : (b & 15u);
@@ -230,7 +251,7 @@ int or_layer(int H, int I, int E, int k, int R, const uint16_t* x_bf16, const fl
              const uint8_t* const* gate_codes, const uint8_t* const* gate_scales,
              const uint8_t* const* up_codes, const uint8_t* const* up_scales,
              const uint8_t* const* down_codes, const uint8_t* const* down_scales,
-             int32_t* topk_id, double* topk_w, double* act, double* out, double* y) {
+             int32_t* topk_id, double* topk_w, double* act, double* out, double* y, int act_bf16) {
     (void)E;
     or_route(R, E, k, logits, topk_id, topk_w);
     int used = 1;
@@ -255,6 +276,8 @@ int or_layer(int H, int I, int E, int k, int R, const uint16_t* x_bf16, const fl
         or_matvec(I, H, gate_codes[e], gate_scales[e], x, g);
         or_matvec(I, H, up_codes[e], up_scales[e], x, u);
         or_swiglu(I, g, u, act + (size_t)p * I);
+        if (act_bf16)
+            for (int i = 0; i < I; ++i) act[(size_t)p * I + i] = or_round_bf16(act[(size_t)p * I + i]);
         or_matvec(H, I, down_codes[e], down_scales[e], act + (size_t)p * I, out + (size_t)p * H);
         free(x);
         free(g);

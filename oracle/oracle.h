@@ -27,6 +27,8 @@ extern "C" {
 double or_e2m1(unsigned code);
 double or_e4m3fn(unsigned byte);
 double or_bf16(uint16_t bits);
+/* float64 -> nearest bf16 value (ties to even, one rounding), as a double */
+double or_round_bf16(double v);
 
 /* routing: top-k by (logit descending, expert id ascending; NaN ranks last),
  * combine weights = softmax over the k chosen logits, in float64. */
@@ -52,12 +54,14 @@ void or_combine(int k, int H, const double* w, const double* out, double* y);
 
 /* float64 layer for R rows. experts_* are host arrays of E pointers (NULL allowed
  * for experts no row selects). act [R][k][I], out [R][k][H], y [R][H].
+ * act_bf16: act is stored as bf16 (or_round_bf16) before down, as the
+ * bf16-storage variant does; act then holds the rounded values.
  * Runs rows x slots over OpenMP threads; returns the thread count used. */
 int or_layer(int H, int I, int E, int k, int R, const uint16_t* x_bf16, const float* logits,
              const uint8_t* const* gate_codes, const uint8_t* const* gate_scales,
              const uint8_t* const* up_codes, const uint8_t* const* up_scales,
              const uint8_t* const* down_codes, const uint8_t* const* down_scales,
-             int32_t* topk_id, double* topk_w, double* act, double* out, double* y);
+             int32_t* topk_id, double* topk_w, double* act, double* out, double* y, int act_bf16);
 
 /* fp32 replay of the per-row arithmetic (chain, scaled fma, eight-leaf tree),
  * for x given as float: y[n] for n in [0, N). */
