@@ -153,6 +153,14 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
     return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
+// fp32 -> bf16 bits, round to nearest, ties to even; a NaN stays a NaN (its
+// top half with the quiet bit set).
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
 // Inclusive prefix sum over the wave's lanes.
 __device__ __forceinline__ int wave_incl_sum(int x) {
     x += (int)dpp_or0<0x111, 0xF>((uint32_t)x);

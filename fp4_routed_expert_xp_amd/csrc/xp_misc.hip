@@ -4,10 +4,12 @@
 
 namespace xp {
 
-// y[r][n] = fma chain from +0 over slots j = 0..k-1 of w[r][j] * out[r][j][n].
+// y[r][n] = fma chain from +0 over slots j = 0..k-1 of w[r][j] * out[r][j][n];
+// Y16 stores it as bf16 (round to nearest even) instead of fp32.
 // [#2983, "Receipt": the combine output is the third tensor the probe holds equal]
+template <bool Y16>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ out, const float* __restrict__ w,
-                                                      int R, int H, int k, float* __restrict__ y) {
+                                                      int R, int H, int k, void* __restrict__ y) {
     const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= (size_t)R * H) return;
     const int r = (int)(idx / H);
@@ -16,7 +18,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     const float* wr = w + (size_t)r * k;
     float s = 0.0f;
     for (int j = 0; j < k; ++j) s = __builtin_fmaf(wr[j], o[(size_t)j * H], s);
-    y[idx] = s;
+    if (Y16)
+        ((uint16_t*)y)[idx] = bf16_rne(s);
+    else
+        ((float*)y)[idx] = s;
 }
 
 // Plain [N][K/2] codes / [N][K/32] scales -> tiles of 64 columns, group-major
@@ -40,8 +45,8 @@ __global__ __launch_bounds__(256) void pack_kernel(int N, int K, const uint8_t* 
 
 using namespace xp;
 
-XP_API int xp_combine(const xp_dims* dims, int32_t rows, const float* out, const float* topk_w, float* y,
-                      void* stream) {
+static int combine_common(const xp_dims* dims, int32_t rows, const float* out, const float* topk_w, void* y,
+                          bool y16, void* stream) {
     int st = check_dims(dims);
     if (st != XP_OK) return st;
     if (rows < 0) return XP_ERR_SHAPE;
@@ -49,9 +54,23 @@ XP_API int xp_combine(const xp_dims* dims, int32_t rows, const float* out, const
     if (!out || !topk_w || !y) return XP_ERR_NULL;
     const size_t n = (size_t)rows * dims->hidden;
     const unsigned grid = (unsigned)((n + 255) / 256);
-    hipLaunchKernelGGL(combine_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, out, topk_w, rows,
-                       dims->hidden, dims->top_k, y);
+    if (y16)
+        hipLaunchKernelGGL(combine_kernel<true>, dim3(grid), dim3(256), 0, (hipStream_t)stream, out, topk_w, rows,
+                           dims->hidden, dims->top_k, y);
+    else
+        hipLaunchKernelGGL(combine_kernel<false>, dim3(grid), dim3(256), 0, (hipStream_t)stream, out, topk_w, rows,
+                           dims->hidden, dims->top_k, y);
     return launch_status();
+}
+
+XP_API int xp_combine(const xp_dims* dims, int32_t rows, const float* out, const float* topk_w, float* y,
+                      void* stream) {
+    return combine_common(dims, rows, out, topk_w, y, false, stream);
+}
+
+XP_API int xp_combine_y16(const xp_dims* dims, int32_t rows, const float* out, const float* topk_w, uint16_t* y16,
+                          void* stream) {
+    return combine_common(dims, rows, out, topk_w, y16, true, stream);
 }
 
 XP_API int xp_pack_matrix(int32_t n, int32_t k, const uint8_t* codes, const uint8_t* scales, uint8_t* packed_codes,

@@ -140,7 +140,10 @@ __device__ __forceinline__ void gu_leaf(gcodes_t cc, gbytes_t ss, const uint32_t
     }
 }
 
-template <int P, bool SPLIT>
+// Gate/up outputs: act in fp32, g and u in fp32 (split), or act stored as bf16.
+enum GuOut { kActF32 = 0, kSplit = 1, kActBf16 = 2 };
+
+template <int P, int OUT>
 __device__ __forceinline__ void gu_item(const xp_expert* __restrict__ experts, const uint16_t* __restrict__ x,
                         const int32_t* __restrict__ entry, int4 ps, int tile, int H, int I, int k,
                         float* __restrict__ out0, float* __restrict__ out1, float* red) {
@@ -176,11 +179,15 @@ __device__ __forceinline__ void gu_item(const xp_expert* __restrict__ experts, c
             const float g = tree8(red + r * kTile + c, stride);
             const float u = tree8(red + 8 * stride + r * kTile + c, stride);
             const size_t o = (size_t)entry[first + r] * I + (size_t)tile * kTile + c;
-            if (SPLIT) {
+            if (OUT == kSplit) {
                 out0[o] = g;
                 out1[o] = u;
             } else {
-                out0[o] = (g / (1.0f + expf(-g))) * u;
+                const float a = (g / (1.0f + expf(-g))) * u;
+                if (OUT == kActBf16)
+                    ((uint16_t*)out0)[o] = bf16_rne(a);
+                else
+                    out0[o] = a;
             }
         }
     }
@@ -197,7 +204,7 @@ struct RouteIn {
 };
 
 // Gate/up passes over the plan in the workspace: work item = (pass, tile).
-template <bool SPLIT>
+template <int OUT>
 __global__ __launch_bounds__(1024) void gateup_kernel(const xp_expert* __restrict__ experts,
                                                       const uint16_t* __restrict__ x,
                                                       const int32_t* __restrict__ hdr,
@@ -213,14 +220,14 @@ __global__ __launch_bounds__(1024) void gateup_kernel(const xp_expert* __restric
         const int tile = item - pass * n_tiles;
         const int4 ps = passes[pass];
         switch (ps.w) {
-            case 1: gu_item<1, SPLIT>(tab, x, entry, ps, tile, H, I, k, out0, out1, red); break;
-            case 2: gu_item<2, SPLIT>(tab, x, entry, ps, tile, H, I, k, out0, out1, red); break;
-            case 3: gu_item<3, SPLIT>(tab, x, entry, ps, tile, H, I, k, out0, out1, red); break;
-            case 4: gu_item<4, SPLIT>(tab, x, entry, ps, tile, H, I, k, out0, out1, red); break;
-            case 5: gu_item<5, SPLIT>(tab, x, entry, ps, tile, H, I, k, out0, out1, red); break;
-            case 6: gu_item<6, SPLIT>(tab, x, entry, ps, tile, H, I, k, out0, out1, red); break;
-            case 7: gu_item<7, SPLIT>(tab, x, entry, ps, tile, H, I, k, out0, out1, red); break;
-            case 8: gu_item<8, SPLIT>(tab, x, entry, ps, tile, H, I, k, out0, out1, red); break;
+            case 1: gu_item<1, OUT>(tab, x, entry, ps, tile, H, I, k, out0, out1, red); break;
+            case 2: gu_item<2, OUT>(tab, x, entry, ps, tile, H, I, k, out0, out1, red); break;
+            case 3: gu_item<3, OUT>(tab, x, entry, ps, tile, H, I, k, out0, out1, red); break;
+            case 4: gu_item<4, OUT>(tab, x, entry, ps, tile, H, I, k, out0, out1, red); break;
+            case 5: gu_item<5, OUT>(tab, x, entry, ps, tile, H, I, k, out0, out1, red); break;
+            case 6: gu_item<6, OUT>(tab, x, entry, ps, tile, H, I, k, out0, out1, red); break;
+            case 7: gu_item<7, OUT>(tab, x, entry, ps, tile, H, I, k, out0, out1, red); break;
+            case 8: gu_item<8, OUT>(tab, x, entry, ps, tile, H, I, k, out0, out1, red); break;
             default: break;
         }
     }
@@ -285,11 +292,13 @@ __global__ __launch_bounds__(1024) void gateup_one_row_kernel(const xp_expert* _
         if (publish) publish_one_row(ri, k, mo, mi);
     }
     __syncthreads();
-    gu_item<1, false>(experts, x, s_entry, make_int4(s_pick, 0, 1, 1), tile, H, I, k, act, nullptr, red);
+    gu_item<1, kActF32>(experts, x, s_entry, make_int4(s_pick, 0, 1, 1), tile, H, I, k, act, nullptr, red);
 }
 
-template <int P>
-__device__ __forceinline__ void dn_item(const xp_expert* __restrict__ experts, const float* __restrict__ act,
+// A16: act is bf16 (the bf16-storage variant); its pairs reach the chain as
+// gate/up's x does (one dword of two bf16 per lane of each row of 16).
+template <int P, bool A16>
+__device__ __forceinline__ void dn_item(const xp_expert* __restrict__ experts, const void* __restrict__ act,
                         const int32_t* __restrict__ entry, int4 ps, int tile, int H, int I,
                         float* __restrict__ out, float* red) {
     constexpr int D = DnDepth<P>::value;
@@ -305,8 +314,13 @@ __device__ __forceinline__ void dn_item(const xp_expert* __restrict__ experts, c
     const gbytes_t ss = (gbytes_t)ex.down_scales + tile_chunks + lane;
 
     const float* ar[P];
+    const uint32_t* ar16[P];
 #pragma unroll
-    for (int r = 0; r < P; ++r) ar[r] = act + (size_t)entry[first + (r < real ? r : real - 1)] * I;
+    for (int r = 0; r < P; ++r) {
+        const size_t row = (size_t)entry[first + (r < real ? r : real - 1)] * I;
+        ar[r] = (const float*)act + row;
+        ar16[r] = (const uint32_t*)((const uint16_t*)act + row);
+    }
 
     // Branch-free ring over ceil(G/8) groups per leaf, as in gu_leaf.
     const int ng = (G + 7) >> 3;
@@ -316,12 +330,18 @@ __device__ __forceinline__ void dn_item(const xp_expert* __restrict__ experts, c
     u32x4 bc[D];
     uint32_t bs[D];
     float2 bx[D][P];
+    uint32_t bx16[D][P];
     auto load = [&](int s, int i) {
         const int g = min(leaf + 8 * i, G - 1);
         bc[s] = load_codes(cc + (size_t)g * kTile);
         bs[s] = ss[(size_t)g * kTile];
 #pragma unroll
-        for (int r = 0; r < P; ++r) bx[s][r] = *(const float2*)(ar[r] + 32 * g + xl);
+        for (int r = 0; r < P; ++r) {
+            if constexpr (A16)
+                bx16[s][r] = ar16[r][16 * g + (lane & 15)];
+            else
+                bx[s][r] = *(const float2*)(ar[r] + 32 * g + xl);
+        }
     };
 #pragma unroll
     for (int s = 0; s < D; ++s) load(s, s);
@@ -332,12 +352,20 @@ __device__ __forceinline__ void dn_item(const xp_expert* __restrict__ experts, c
             float w[32];
             decode32(bc[s], w);
             const float sc = e4m3(bs[s]);
-            float xa[P], xb[P];
-#pragma unroll
-            for (int r = 0; r < P; ++r) { xa[r] = bx[s][r].x; xb[r] = bx[s][r].y; }
-            load(s, i + D);
             float p[P];
-            Chain<P>::f32(w, xa, xb, p);
+            if constexpr (A16) {
+                uint32_t xc[P];
+#pragma unroll
+                for (int r = 0; r < P; ++r) xc[r] = bx16[s][r];
+                load(s, i + D);
+                Chain<P>::bf16(w, xc, p);
+            } else {
+                float xa[P], xb[P];
+#pragma unroll
+                for (int r = 0; r < P; ++r) { xa[r] = bx[s][r].x; xb[r] = bx[s][r].y; }
+                load(s, i + D);
+                Chain<P>::f32(w, xa, xb, p);
+            }
             const bool valid = leaf + 8 * i < G;
 #pragma unroll
             for (int r = 0; r < P; ++r) {
@@ -361,8 +389,9 @@ __device__ __forceinline__ void dn_item(const xp_expert* __restrict__ experts, c
     __syncthreads();
 }
 
+template <bool A16>
 __global__ __launch_bounds__(512, 4) void down_kernel(const xp_expert* __restrict__ experts,
-                                                      const float* __restrict__ act,
+                                                      const void* __restrict__ act,
                                                       const int32_t* __restrict__ hdr,
                                                       const int32_t* __restrict__ entry,
                                                       const int4* __restrict__ passes, int E, int H, int I,
@@ -376,14 +405,14 @@ __global__ __launch_bounds__(512, 4) void down_kernel(const xp_expert* __restric
         const int tile = item - pass * n_tiles;
         const int4 ps = passes[pass];
         switch (ps.w) {
-            case 1: dn_item<1>(tab, act, entry, ps, tile, H, I, out, red); break;
-            case 2: dn_item<2>(tab, act, entry, ps, tile, H, I, out, red); break;
-            case 3: dn_item<3>(tab, act, entry, ps, tile, H, I, out, red); break;
-            case 4: dn_item<4>(tab, act, entry, ps, tile, H, I, out, red); break;
-            case 5: dn_item<5>(tab, act, entry, ps, tile, H, I, out, red); break;
-            case 6: dn_item<6>(tab, act, entry, ps, tile, H, I, out, red); break;
-            case 7: dn_item<7>(tab, act, entry, ps, tile, H, I, out, red); break;
-            case 8: dn_item<8>(tab, act, entry, ps, tile, H, I, out, red); break;
+            case 1: dn_item<1, A16>(tab, act, entry, ps, tile, H, I, out, red); break;
+            case 2: dn_item<2, A16>(tab, act, entry, ps, tile, H, I, out, red); break;
+            case 3: dn_item<3, A16>(tab, act, entry, ps, tile, H, I, out, red); break;
+            case 4: dn_item<4, A16>(tab, act, entry, ps, tile, H, I, out, red); break;
+            case 5: dn_item<5, A16>(tab, act, entry, ps, tile, H, I, out, red); break;
+            case 6: dn_item<6, A16>(tab, act, entry, ps, tile, H, I, out, red); break;
+            case 7: dn_item<7, A16>(tab, act, entry, ps, tile, H, I, out, red); break;
+            case 8: dn_item<8, A16>(tab, act, entry, ps, tile, H, I, out, red); break;
             default: break;
         }
     }
@@ -395,21 +424,25 @@ static int grid_for(int rows, int k, int n_tiles) {
 }
 
 static int gateup_common(const xp_dims* dims, int32_t rows, const uint16_t* x, const xp_expert* experts,
-                         const void* ws, size_t ws_bytes, float* o0, float* o1, bool split, void* stream) {
+                         const void* ws, size_t ws_bytes, float* o0, float* o1, int mode, void* stream) {
     int st = check_dims(dims);
     if (st != XP_OK) return st;
     if (rows < 0) return XP_ERR_SHAPE;
     if (rows == 0) return XP_OK;
-    if (!x || !experts || !ws || !o0 || (split && !o1)) return XP_ERR_NULL;
+    if (!x || !experts || !ws || !o0 || (mode == kSplit && !o1)) return XP_ERR_NULL;
     if (ws_bytes < ws_layout(dims, rows).total) return XP_ERR_WORKSPACE;
     Plan pl = plan_view(ws, dims, rows);
     const int grid = grid_for(rows, dims->top_k, dims->inter / kTile);
     hipStream_t s = (hipStream_t)stream;
-    if (split)
-        hipLaunchKernelGGL((gateup_kernel<true>), dim3(grid), dim3(1024), 0, s, experts, x, pl.hdr, pl.entry,
+    if (mode == kSplit)
+        hipLaunchKernelGGL((gateup_kernel<kSplit>), dim3(grid), dim3(1024), 0, s, experts, x, pl.hdr, pl.entry,
                            pl.gu_pass, dims->n_experts, dims->hidden, dims->inter, dims->top_k, o0, o1);
+    else if (mode == kActBf16)
+        hipLaunchKernelGGL((gateup_kernel<kActBf16>), dim3(grid), dim3(1024), 0, s, experts, x, pl.hdr,
+                           pl.entry, pl.gu_pass, dims->n_experts, dims->hidden, dims->inter, dims->top_k, o0,
+                           (float*)nullptr);
     else
-        hipLaunchKernelGGL((gateup_kernel<false>), dim3(grid), dim3(1024), 0, s, experts, x, pl.hdr, pl.entry,
+        hipLaunchKernelGGL((gateup_kernel<kActF32>), dim3(grid), dim3(1024), 0, s, experts, x, pl.hdr, pl.entry,
                            pl.gu_pass, dims->n_experts, dims->hidden, dims->inter, dims->top_k, o0,
                            (float*)nullptr);
     return launch_status();
@@ -421,16 +454,21 @@ using namespace xp;
 
 XP_API int xp_gateup_rows(const xp_dims* dims, int32_t rows, const uint16_t* x, const xp_expert* experts,
                           const void* workspace, size_t ws_bytes, float* act, void* stream) {
-    return gateup_common(dims, rows, x, experts, workspace, ws_bytes, act, nullptr, false, stream);
+    return gateup_common(dims, rows, x, experts, workspace, ws_bytes, act, nullptr, kActF32, stream);
 }
 
 XP_API int xp_gateup_rows_split(const xp_dims* dims, int32_t rows, const uint16_t* x, const xp_expert* experts,
                                 const void* workspace, size_t ws_bytes, float* g, float* u, void* stream) {
-    return gateup_common(dims, rows, x, experts, workspace, ws_bytes, g, u, true, stream);
+    return gateup_common(dims, rows, x, experts, workspace, ws_bytes, g, u, kSplit, stream);
 }
 
-XP_API int xp_down_rows(const xp_dims* dims, int32_t rows, const float* act, const xp_expert* experts,
-                        const void* workspace, size_t ws_bytes, float* out, void* stream) {
+XP_API int xp_gateup_rows_act16(const xp_dims* dims, int32_t rows, const uint16_t* x, const xp_expert* experts,
+                                const void* workspace, size_t ws_bytes, uint16_t* act16, void* stream) {
+    return gateup_common(dims, rows, x, experts, workspace, ws_bytes, (float*)act16, nullptr, kActBf16, stream);
+}
+
+static int down_common(const xp_dims* dims, int32_t rows, const void* act, const xp_expert* experts,
+                       const void* workspace, size_t ws_bytes, float* out, bool a16, void* stream) {
     int st = check_dims(dims);
     if (st != XP_OK) return st;
     if (rows < 0) return XP_ERR_SHAPE;
@@ -439,9 +477,23 @@ XP_API int xp_down_rows(const xp_dims* dims, int32_t rows, const float* act, con
     if (ws_bytes < ws_layout(dims, rows).total) return XP_ERR_WORKSPACE;
     Plan pl = plan_view(workspace, dims, rows);
     const int grid = grid_for(rows, dims->top_k, dims->hidden / kTile);
-    hipLaunchKernelGGL(down_kernel, dim3(grid), dim3(512), 0, (hipStream_t)stream, experts, act, pl.hdr, pl.entry,
-                       pl.dn_pass, dims->n_experts, dims->hidden, dims->inter, out);
+    if (a16)
+        hipLaunchKernelGGL(down_kernel<true>, dim3(grid), dim3(512), 0, (hipStream_t)stream, experts, act, pl.hdr,
+                           pl.entry, pl.dn_pass, dims->n_experts, dims->hidden, dims->inter, out);
+    else
+        hipLaunchKernelGGL(down_kernel<false>, dim3(grid), dim3(512), 0, (hipStream_t)stream, experts, act, pl.hdr,
+                           pl.entry, pl.dn_pass, dims->n_experts, dims->hidden, dims->inter, out);
     return launch_status();
+}
+
+XP_API int xp_down_rows(const xp_dims* dims, int32_t rows, const float* act, const xp_expert* experts,
+                        const void* workspace, size_t ws_bytes, float* out, void* stream) {
+    return down_common(dims, rows, act, experts, workspace, ws_bytes, out, false, stream);
+}
+
+XP_API int xp_down_rows_act16(const xp_dims* dims, int32_t rows, const uint16_t* act16, const xp_expert* experts,
+                              const void* workspace, size_t ws_bytes, float* out, void* stream) {
+    return down_common(dims, rows, act16, experts, workspace, ws_bytes, out, true, stream);
 }
 
 XP_API int xp_route_gateup(const xp_dims* dims, int32_t rows, const float* logits, const uint16_t* x,

@@ -23,6 +23,7 @@ EXPORTS = (
     "xp_gateup_rows", "xp_gateup_rows_split", "xp_down_rows", "xp_combine",
     "xp_set_tiers", "xp_get_tiers", "xp_status_string", "xp_route_gateup", "xp_down_combine",
     "xp_prefill_gateup", "xp_prefill_down", "xp_fp8_packed_bytes", "xp_fp8_pack", "xp_fp8_rows",
+    "xp_gateup_rows_act16", "xp_down_rows_act16", "xp_combine_y16",
 )
 
 
@@ -71,6 +72,9 @@ def lib():
         L.xp_down_combine.argtypes = [D, i32, P, P, P, P, sz, P, P, P]
         L.xp_prefill_gateup.argtypes = [D, i32, P, P, P, sz, P, P]
         L.xp_prefill_down.argtypes = [D, i32, P, P, P, sz, P, P]
+        L.xp_gateup_rows_act16.argtypes = [D, i32, P, P, P, sz, P, P]
+        L.xp_down_rows_act16.argtypes = [D, i32, P, P, P, sz, P, P]
+        L.xp_combine_y16.argtypes = [D, i32, P, P, P, P]
         L.xp_fp8_packed_bytes.argtypes = [i32, i32]
         L.xp_fp8_packed_bytes.restype = sz
         L.xp_fp8_pack.argtypes = [i32, i32, P, P, P]
@@ -82,7 +86,8 @@ def lib():
         for name in ("xp_pack_matrix", "xp_workspace_layout", "xp_route_bucket", "xp_gateup_rows",
                      "xp_gateup_rows_split", "xp_down_rows", "xp_combine", "xp_set_tiers", "xp_get_tiers",
                      "xp_route_gateup", "xp_down_combine", "xp_prefill_gateup", "xp_prefill_down",
-                     "xp_fp8_pack", "xp_fp8_rows"):
+                     "xp_fp8_pack", "xp_fp8_rows", "xp_gateup_rows_act16", "xp_down_rows_act16",
+                     "xp_combine_y16"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -268,6 +273,42 @@ def xp_prefill_down(d: xp_dims, rows: int, act, experts, workspace, out, stream=
     nbytes = workspace.numel() if workspace is not None else 0
     _check(lib().xp_prefill_down(ctypes.byref(d), int(rows), _ptr(act), _ptr(experts), _ptr(workspace), nbytes,
                                  _ptr(out), _stream(stream)), "xp_prefill_down")
+
+
+def _dev_u16(t: torch.Tensor, name: str, numel: int) -> None:
+    """bf16 storage: 16-bit patterns (int16/uint16) or a bfloat16 tensor."""
+    if not isinstance(t, torch.Tensor) or t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise ValueError("%s must hold bf16 (bfloat16, or int16/uint16 bit patterns)" % name)
+    _dev(t, t.dtype, name, numel)
+
+
+def xp_gateup_rows_act16(d: xp_dims, rows: int, x, experts, workspace, act16, stream=None) -> None:
+    if rows > 0:
+        _dev_bf16(x, "x", rows * d.hidden)
+        _dev(experts, torch.int64, "experts", d.n_experts * 6)
+        _dev_u16(act16, "act16", rows * d.top_k * d.inter)
+    nbytes = workspace.numel() if workspace is not None else 0
+    _check(lib().xp_gateup_rows_act16(ctypes.byref(d), int(rows), _ptr(x), _ptr(experts), _ptr(workspace),
+                                      nbytes, _ptr(act16), _stream(stream)), "xp_gateup_rows_act16")
+
+
+def xp_down_rows_act16(d: xp_dims, rows: int, act16, experts, workspace, out, stream=None) -> None:
+    if rows > 0:
+        _dev_u16(act16, "act16", rows * d.top_k * d.inter)
+        _dev(experts, torch.int64, "experts", d.n_experts * 6)
+        _dev(out, torch.float32, "out", rows * d.top_k * d.hidden)
+    nbytes = workspace.numel() if workspace is not None else 0
+    _check(lib().xp_down_rows_act16(ctypes.byref(d), int(rows), _ptr(act16), _ptr(experts), _ptr(workspace),
+                                    nbytes, _ptr(out), _stream(stream)), "xp_down_rows_act16")
+
+
+def xp_combine_y16(d: xp_dims, rows: int, out, topk_w, y16, stream=None) -> None:
+    if rows > 0:
+        _dev(out, torch.float32, "out", rows * d.top_k * d.hidden)
+        _dev(topk_w, torch.float32, "topk_w", rows * d.top_k)
+        _dev_u16(y16, "y16", rows * d.hidden)
+    _check(lib().xp_combine_y16(ctypes.byref(d), int(rows), _ptr(out), _ptr(topk_w), _ptr(y16),
+                                _stream(stream)), "xp_combine_y16")
 
 
 def xp_fp8_packed_bytes(n: int, k: int) -> int:

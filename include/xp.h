@@ -193,6 +193,26 @@ int xp_prefill_gateup(const xp_dims* dims, int32_t rows, const uint16_t* x, cons
 int xp_prefill_down(const xp_dims* dims, int32_t rows, const float* act, const xp_expert* experts,
                     const void* workspace, size_t ws_bytes, float* out, void* stream);
 
+/* ------------------------------------------------------ bf16 storage
+ * Variants that store act or y as bf16 (the width x arrives in [#2983, "What
+ * this changes": bf16 activations into gate/up]) instead of fp32. Each is the
+ * fp32 call followed by one rounding, bit for bit: the stored value is the
+ * fp32 result rounded to the nearest bf16, ties to even (a NaN stays a NaN,
+ * quiet). Same buffers, plans and errors as the fp32 calls they name. */
+
+/* act16[row][slot][I] = bf16 of the act xp_gateup_rows computes. */
+int xp_gateup_rows_act16(const xp_dims* dims, int32_t rows, const uint16_t* x, const xp_expert* experts,
+                         const void* workspace, size_t ws_bytes, uint16_t* act16, void* stream);
+
+/* out as xp_down_rows computes it from act = act16 widened to fp32 (exact):
+ * the same per-row chain, scaled fma and tree. */
+int xp_down_rows_act16(const xp_dims* dims, int32_t rows, const uint16_t* act16, const xp_expert* experts,
+                       const void* workspace, size_t ws_bytes, float* out, void* stream);
+
+/* y16[row][H] = bf16 of the y xp_combine computes. */
+int xp_combine_y16(const xp_dims* dims, int32_t rows, const float* out, const float* topk_w, uint16_t* y16,
+                   void* stream);
+
 /* ------------------------------------------------- dense FP8 projections
  * The decode layer's other weight stream: y = x W^T for a dense projection
  * whose weights are E4M3FN bytes with one fp32 scale per 128 x 128 block

@@ -72,6 +72,9 @@ def test_bad_dims_rejected_before_any_launch(dims, status):
     assert L.xp_combine(ctypes.byref(d), 4, P, P, P, None) == status
     assert L.xp_prefill_gateup(ctypes.byref(d), 4, P, P, P, 1 << 30, P, None) == status
     assert L.xp_prefill_down(ctypes.byref(d), 4, P, P, P, 1 << 30, P, None) == status
+    assert L.xp_gateup_rows_act16(ctypes.byref(d), 4, P, P, P, 1 << 30, P, None) == status
+    assert L.xp_down_rows_act16(ctypes.byref(d), 4, P, P, P, 1 << 30, P, None) == status
+    assert L.xp_combine_y16(ctypes.byref(d), 4, P, P, P, None) == status
 
 
 def test_null_rows_and_workspace_checks():
@@ -139,3 +142,19 @@ def test_fp8_argument_checks():
     for slices in (3, 32, -1, 8):
         assert L.xp_fp8_rows(1, 16, 512, P, P, P, P, slices, None) == xp.XP_ERR_SHAPE, slices
     assert L.xp_fp8_rows(1, 16, 128 * 40, P, P, P, P, 4, None) == xp.XP_ERR_SHAPE  # P = 64: 16 blocks a slice
+
+
+def test_bf16_storage_argument_checks():
+    L = xp.lib()
+    d = xp.dims(256, 128, 8, 2)
+    P = ctypes.c_void_p(0x1000)
+    need = xp.xp_workspace_bytes(d, 4)
+    assert L.xp_gateup_rows_act16(ctypes.byref(d), 0, None, None, None, 0, None, None) == xp.XP_OK
+    assert L.xp_down_rows_act16(ctypes.byref(d), 0, None, None, None, 0, None, None) == xp.XP_OK
+    assert L.xp_combine_y16(ctypes.byref(d), 0, None, None, None, None) == xp.XP_OK
+    assert L.xp_gateup_rows_act16(ctypes.byref(d), 4, P, P, P, need, None, None) == xp.XP_ERR_NULL
+    assert L.xp_down_rows_act16(ctypes.byref(d), 4, None, P, P, need, P, None) == xp.XP_ERR_NULL
+    assert L.xp_combine_y16(ctypes.byref(d), 4, P, P, None, None) == xp.XP_ERR_NULL
+    assert L.xp_gateup_rows_act16(ctypes.byref(d), 4, P, P, P, need - 1, P, None) == xp.XP_ERR_WORKSPACE
+    assert L.xp_down_rows_act16(ctypes.byref(d), 4, P, P, P, need - 1, P, None) == xp.XP_ERR_WORKSPACE
+    assert L.xp_combine_y16(ctypes.byref(d), -1, P, P, P, None) == xp.XP_ERR_SHAPE
