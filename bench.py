@@ -153,6 +153,8 @@ class Cell:
         self.act = torch.empty((R, k, I), dtype=torch.float32, device="cuda")
         self.out = torch.empty((R, k, H), dtype=torch.float32, device="cuda")
         self.y = torch.empty((R, H), dtype=torch.float32, device="cuda")
+        self.act16 = torch.empty((R, k, I), dtype=torch.int16, device="cuda")
+        self.y16 = torch.empty((R, H), dtype=torch.int16, device="cuda")
 
     def call(self, kind: str, l: int) -> None:
         """One library call of layer l."""
@@ -170,6 +172,12 @@ class Cell:
             xp.xp_route_gateup(d, R, self.logits[l], self.x[l], tab, self.topk_id, self.topk_w, ws, self.act)
         elif kind == "down_combine":
             xp.xp_down_combine(d, R, self.act, tab, self.topk_w, ws, self.out, self.y)
+        elif kind == "gateup_act16":
+            xp.xp_gateup_rows_act16(d, R, self.x[l], tab, ws, self.act16)
+        elif kind == "down_act16":
+            xp.xp_down_rows_act16(d, R, self.act16, tab, ws, self.out)
+        elif kind == "combine_y16":
+            xp.xp_combine_y16(d, R, self.out, self.topk_w, self.y16)
         elif kind == "prefill_gateup":
             xp.xp_prefill_gateup(d, R, self.x[l], tab, ws, self.act)
         elif kind == "prefill_down":
@@ -202,6 +210,7 @@ class Cell:
 
 
 PATHS = {"four_calls": ("route", "gateup", "down", "combine"), "two_calls": ("route_gateup", "down_combine"),
+         "bf16_storage": ("route", "gateup_act16", "down_act16", "combine_y16"),
          "prefill": ("route", "prefill_gateup", "prefill_down", "combine")}
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PREFILL_LAYERS = 4               # prefill cells rotate over this many layers (3.4 GB of weights each)
@@ -275,11 +284,14 @@ def cell_report(cell: Cell, t: dict, copy_gbps: float) -> dict:
     layer_us = t["ms_per_round"] * 1e3 / L
     gbps = unique_bytes / (layer_us * 1e-6) / 1e9
     fused = t["path"] == "two_calls"
-    gu_kind, dn_kind = ("route_gateup", "down_combine") if fused else ("gateup", "down")
+    b16 = t["path"] == "bf16_storage"
+    gu_kind, dn_kind = ("route_gateup", "down_combine") if fused else (
+        ("gateup_act16", "down_act16") if b16 else ("gateup", "down"))
     # algorithmic bytes of the gate/up launch: its distinct experts' gate+up weights, x read,
     # act written (+ logits read, top-k and plan written when it routes)
-    gu_bytes = distinct * gu_w + R * H * 2 + R * k * I * 4 + ((R * E * 4 + R * k * 8) if fused else 0)
-    dn_bytes = distinct * dn_w + R * k * I * 4 + R * k * H * 4 + ((R * k * H * 4 + R * H * 4) if fused else 0)
+    act_b = 2 if b16 else 4
+    gu_bytes = distinct * gu_w + R * H * 2 + R * k * I * act_b + ((R * E * 4 + R * k * 8) if fused else 0)
+    dn_bytes = distinct * dn_w + R * k * I * act_b + R * k * H * 4 + ((R * k * H * 4 + R * H * 4) if fused else 0)
     gu_us, dn_us = t["kernel_us"][gu_kind], t["kernel_us"][dn_kind]
     # VALU lane-ops: one fma per weight per computed row (padding included), one
     # decode per two weights per pass, one scaled fma per group per row
@@ -483,7 +495,7 @@ def main():
             del cell
             continue
         cell = Cell(model, cfg, args.layers)
-        for path in ("two_calls", "four_calls"):
+        for path in ("two_calls", "four_calls", "bf16_storage"):
             t = time_cell(cell, path, args.steps, args.warmup)
             key = "%s/%s" % (name, path)
             timings[key] = t
