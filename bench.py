@@ -37,27 +37,32 @@ CSRC = os.path.join(ROOT, "fp4_routed_expert_xp_amd", "csrc")
 # 1,048,590 KiB for 2,097,152 KiB fetched, WRITE_SIZE read exactly 2,097,152 KiB.
 # The figure belongs to the sources the kernel is built from (their digest below);
 # after any change to them the bench reports traffic as null.
-TRAFFIC = dict(sources="57df728e", fetch_kib=34978.2, write_kib=66.4,
+TRAFFIC = dict(sources="57bee98b", fetch_kib=34982.2, write_kib=66.4,
                fetch_factor=2097152 / 1048590.0, write_factor=1.0)
 ROOFLINE_SOURCES = ("xp_rows.hip", "xp_common.h", "xp_route_dev.h", "xp_chain_asm.h")
+# The same for the dense FP8 projection kernel at 4096 x 4096 (grid of 256
+# workgroups; mean over its launches at 1, 8 and 16 rows), tied to xp_fp8.hip.
+FP8_TRAFFIC = dict(sources="96a0d483", fetch_kib=8519.4, write_kib=133.3)
+FP8_SOURCES = ("xp_fp8.hip", "xp_common.h")
 
 
-def csrc_digest() -> str:
-    """Digest of the roofline kernel's translation unit (its source and headers)."""
+def csrc_digest(sources=ROOFLINE_SOURCES) -> str:
+    """Digest of a kernel's translation unit (its source and headers)."""
     import hashlib
     h = hashlib.sha256()
-    for name in ROOFLINE_SOURCES:
+    for name in sources:
         h.update(name.encode())
         h.update(open(os.path.join(CSRC, name), "rb").read())
     h.update(open(os.path.join(ROOT, "include", "xp.h"), "rb").read())
     return h.hexdigest()[:8]
 
 
-def measured_traffic():
-    """HBM bytes per launch of the roofline kernel, or None once the sources changed."""
-    if csrc_digest() != TRAFFIC["sources"]:
+def measured_traffic(t=None, sources=ROOFLINE_SOURCES):
+    """HBM bytes per launch of a roofline kernel, or None once its sources changed."""
+    t = TRAFFIC if t is None else t
+    if csrc_digest(sources) != t["sources"]:
         return None
-    kib = TRAFFIC["fetch_kib"] * TRAFFIC["fetch_factor"] + TRAFFIC["write_kib"] * TRAFFIC["write_factor"]
+    kib = t["fetch_kib"] * TRAFFIC["fetch_factor"] + t["write_kib"] * TRAFFIC["write_factor"]
     return int(round(kib * 1024))
 
 
@@ -543,7 +548,7 @@ def main():
                    "rows": head["rows"], "layers": args.layers, "hidden": base.H, "inter": base.I,
                    "experts": base.E, "top_k": base.k, "path": "two_calls"},
         "roofline": {"kernel": "gateup_one_row_kernel (xp_route_gateup)" if head["rows"] == 1
-                     else "route_*_kernel + gateup_kernel<false> (xp_route_gateup)", "bound": "hbm",
+                     else "route_*_kernel + gateup_kernel<0> (xp_route_gateup)", "bound": "hbm",
                      "achieved": round(achieved, 1), "bytes_per_launch": head["gateup_bytes"],
                      "launch_us": head["kernel_us"]["route_gateup"],
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
@@ -569,7 +574,7 @@ def main():
             "kernel": "fp8_rows_kernel (xp_fp8_rows, %dx%d, %d row)" % (N, K, fp8[0]["rows"]), "bound": "hbm",
             "achieved": round(nbytes / (us * 1e-6) / 1e9, 1), "bytes_per_launch": nbytes, "launch_us": us,
             "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-            "traffic": None}
+            "traffic": measured_traffic(FP8_TRAFFIC, FP8_SOURCES)}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

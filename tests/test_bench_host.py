@@ -25,6 +25,12 @@ def test_traffic_is_tied_to_the_kernel_sources():
         assert 0.99 * alg < t < 1.05 * alg
     else:
         assert t is None
+    f = bench.measured_traffic(bench.FP8_TRAFFIC, bench.FP8_SOURCES)
+    if bench.csrc_digest(bench.FP8_SOURCES) == bench.FP8_TRAFFIC["sources"]:
+        alg = 4096 * 4096 + 32 * 32 * 4       # weight bytes and scales of the 4096 x 4096 launch
+        assert 0.99 * alg < f < 1.1 * alg
+    else:
+        assert f is None
 
 
 def test_sweep_sets_are_valid_pass_sizes():
