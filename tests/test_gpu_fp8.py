@@ -77,6 +77,20 @@ def test_fp8_rows_match_oracle(N, K):
     log("  worst per-row relative error %.2e" % worst)
 
 
+def test_fp8_largest_k_and_many_row_tiles():
+    """K = 8192 (64 blocks: 16 slices of four) and up to 100 rows (seven 16-row tiles,
+    the weights held in registers across them)."""
+    m = Fp8Matrix(64, 8192, layer=3)
+    for R in (1, 16, 100):
+        x = synth.activations(SEED + 7, R, R, 8192)
+        err = rel_err_rows(m.run(x), m.oracle(x))
+        assert np.all(err <= TOL), (R, float(err.max()))
+    x = synth.activations(SEED + 7, 100, 100, 8192)
+    full = m.run(x)
+    for r in (0, 47, 99):
+        assert np.array_equal(bits(full[r:r + 1]), bits(m.run(x[r:r + 1]))), r
+
+
 def test_fp8_pack_layout():
     N, K = 48, 384
     m = Fp8Matrix(N, K)
