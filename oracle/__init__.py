@@ -56,6 +56,8 @@ def lib():
         L.or_route.restype = None
         L.or_fp8_proj.argtypes = [i32, i32, i32, P, P, P, P]
         L.or_fp8_proj.restype = None
+        L.or_fp8_proj_f32.argtypes = [i32, i32, i32, P, P, P, P]
+        L.or_fp8_proj_f32.restype = None
         L.or_bucket.argtypes = [i32, i32, i32, P, P, P, P]
         L.or_bucket.restype = None
         L.or_passes.argtypes = [i32, P, i32, P, P, i32]
@@ -274,4 +276,18 @@ def fp8_proj(x_bits: np.ndarray, w: np.ndarray, s: np.ndarray) -> np.ndarray:
     assert s.shape == ((N + 127) // 128, K // 128)
     y = np.zeros((R, N), dtype=np.float64)
     lib().or_fp8_proj(R, N, K, _p(x_bits), _p(w), _p(s), _p(y))
+    return y
+
+
+def fp8_proj_f32(x: np.ndarray, w: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """float64 y [R][N] of the dense FP8 projection of fp32 rows (see or_fp8_proj_f32)."""
+    x = _c(x, np.float32)
+    w = _c(w, np.uint8)
+    s = _c(s, np.float32)
+    R, K = x.shape
+    N = w.shape[0]
+    assert w.shape == (N, K) and K % 128 == 0
+    assert s.shape == ((N + 127) // 128, K // 128)
+    y = np.zeros((R, N), dtype=np.float64)
+    lib().or_fp8_proj_f32(R, N, K, _p(x), _p(w), _p(s), _p(y))
     return y

@@ -351,3 +351,19 @@ void or_fp8_proj(int R, int N, int K, const uint16_t* x, const uint8_t* w, const
             y[(size_t)r * N + n] = acc;
         }
 }
+
+/* The same projection for fp32 rows: y[r][n] = sum over k of x[r][k] *
+ * e4m3fn(w[n][k]) * s[n/128][k/128], float64, k ascending (the pages register
+ * fp32 and bf16 activation forms of the FP8 projections). */
+void or_fp8_proj_f32(int R, int N, int K, const float* x, const uint8_t* w, const float* s, double* y) {
+    const int KB = K / 128;
+    for (int r = 0; r < R; ++r)
+        for (int n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int k = 0; k < K; ++k) {
+                double wv = or_e4m3fn(w[(size_t)n * K + k]) * (double)s[(size_t)(n / 128) * KB + k / 128];
+                acc += (double)x[(size_t)r * K + k] * wv;
+            }
+            y[(size_t)r * N + n] = acc;
+        }
+}

@@ -72,6 +72,8 @@ void or_combine32(int k, int H, const float* w, const float* out, float* y);
 /* dense FP8 projection, float64: y [R][N] = x [R][K] (bf16 bits) times the
  * transpose of w [N][K] (E4M3FN bytes) scaled by s [ceil(N/128)][K/128]. */
 void or_fp8_proj(int R, int N, int K, const uint16_t* x, const uint8_t* w, const float* s, double* y);
+/* the same for fp32 rows x [R][K] */
+void or_fp8_proj_f32(int R, int N, int K, const float* x, const uint8_t* w, const float* s, double* y);
 
 int or_omp_threads(void);
 

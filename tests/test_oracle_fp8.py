@@ -128,3 +128,18 @@ def test_fp8_rows_are_independent():
     x = synth.activations(23, 0, R, K)
     p = rng.permutation(R)
     assert np.array_equal(oracle.fp8_proj(x[p], w, s), oracle.fp8_proj(x, w, s)[p])
+
+
+def test_fp8_f32_rows_match_numpy_and_the_bf16_form():
+    rng = np.random.default_rng(16)
+    R, N, K = 3, 144, 256
+    w = _valid_bytes(rng, (N, K))
+    s = (2.0 ** rng.integers(-6, 2, size=(2, 2))).astype(np.float32)
+    x = (rng.standard_normal((R, K)) * 3).astype(np.float32)
+    W = _torch_decode(w) * _block_scales(s, N, K)
+    ref = x.astype(np.float64) @ W.T
+    y = oracle.fp8_proj_f32(x, w, s)
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+    # rows whose values are bf16 values give the bf16 form's result exactly
+    xb = synth.activations(25, 0, R, K)
+    assert np.array_equal(oracle.fp8_proj_f32(synth.bf16_bits_to_f32(xb), w, s), oracle.fp8_proj(xb, w, s))
