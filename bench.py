@@ -382,6 +382,7 @@ class Fp8Cell:
         nmax = max(N for N, _ in FP8_SHAPES)
         xb = synth.activations(5002, 0, rmax, kmax)
         self.x = torch.from_numpy(xb.view(np.int16).copy()).cuda()
+        self.xf = torch.from_numpy(synth.bf16_bits_to_f32(xb) + np.float32(1.0 / 3.0)).cuda()  # full fp32 values
         self.y = torch.empty((rmax, nmax), dtype=torch.float32, device="cuda")
         self.set_bytes = sum(N * K + ((N + 127) // 128) * (K // 128) * 4 for N, K in FP8_SHAPES)
         torch.cuda.synchronize()
@@ -413,18 +414,27 @@ def time_fp8(cell: Fp8Cell, steps: int, warmup: int) -> dict:
         torch.cuda.synchronize()
         ms = _replay_ms(g, steps)
         del g
-        per = {}
+        xfs = {K: cell.xf[:R, :K].contiguous() for _, K in FP8_SHAPES}
+
+        def run_f32(i, l):
+            from fp4_routed_expert_xp_amd import xp
+            N, K = FP8_SHAPES[i]
+            packed, sc = cell.mats[l][i]
+            xp.xp_fp8_rows_f32(R, N, K, xfs[K], packed, sc, cell.y, 0)
+
+        per, per_f32 = {}, {}
         for i, (N, K) in enumerate(FP8_SHAPES):
-            gk = _graph(lambda: [run(i, l) for l in range(cell.layers)])
-            gk.replay()
-            torch.cuda.synchronize()
-            per["%dx%d" % (N, K)] = round(_replay_ms(gk, 5) * 1e3 / cell.layers, 3)
-            del gk
+            for fn, dst in ((run, per), (run_f32, per_f32)):
+                gk = _graph(lambda: [fn(i, l) for l in range(cell.layers)])
+                gk.replay()
+                torch.cuda.synchronize()
+                dst["%dx%d" % (N, K)] = round(_replay_ms(gk, 5) * 1e3 / cell.layers, 3)
+                del gk
         layer_us = ms * 1e3 / cell.layers
         out[R] = dict(rows=R, round_ms=round(ms, 4), layer_us=round(layer_us, 3),
                       weight_gbps=round(cell.set_bytes / (layer_us * 1e-6) / 1e9, 1),
                       pct_hbm_peak=round(100 * cell.set_bytes / (layer_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 2),
-                      kernel_us=per)
+                      kernel_us=per, kernel_us_f32_rows=per_f32)
     return out
 
 

@@ -9,5 +9,5 @@ from .xp import (  # noqa: F401
     XPError, dims, xp_combine, xp_down_combine, xp_down_rows, xp_gateup_rows, xp_gateup_rows_split,
     xp_get_tiers, xp_pack_matrix, xp_prefill_down, xp_prefill_gateup, xp_route_bucket, xp_route_gateup, xp_set_tiers, xp_status_string,
     xp_workspace_bytes, xp_workspace_layout, xp_fp8_pack, xp_fp8_packed_bytes, xp_fp8_rows,
-    xp_gateup_rows_act16, xp_down_rows_act16, xp_combine_y16,
+    xp_gateup_rows_act16, xp_down_rows_act16, xp_combine_y16, xp_fp8_rows_f32,
 )

@@ -53,82 +53,128 @@ __device__ __forceinline__ bf16x8 group_bf16(uint32_t d0, uint32_t d1) {
 
 // The operands one slice works on: its weights (32 bytes per lane per block:
 // groups 0..3, 8 k each) and scales, and its LDS chunk of x for the current
-// 16-row tile (two blocks at a time).
+// 16-row tile: two blocks of bf16 rows at a time, or one block of fp32 rows.
 constexpr int kXBlocks = 2;
-constexpr int kXRow = 33;   // LDS row of a wave's x chunk: 256 k (512 B) + 16 B pad, in 16-B units
+constexpr int kXRow = 33;   // LDS row of a wave's x chunk: 512 B + 16 B pad, in 16-B units
 
-template <int RUN>
+template <int RUN, bool F32>
 struct Slice {
+    static constexpr int XB = F32 ? 1 : (RUN < kXBlocks ? RUN : kXBlocks);  // blocks per chunk
     u32x4v w[RUN][2];
     float sc[RUN];
     u32x4v* xs;          // this wave's LDS x chunk: 16 rows x kXRow
-    const uint16_t* x;
+    const void* x;
     int R, K, m0;
     bool row_ok;         // row m0 + (lane % 16) exists
     int lane;
     int j0, KB;
 };
 
-// Stage x of blocks b0 .. b0+n-1 (n <= 2) for rows m0 .. m0+15 in this wave's
-// LDS chunk, with whole-row coalesced loads (16 lanes per 256 B of a row).
-template <int RUN>
-__device__ __forceinline__ void load_x(Slice<RUN>& sl, int b0, int n) {
-    const int lpr = 16 * n, rpi = 64 / lpr;
+// Stage x of the chunk starting at block b0 for rows m0 .. m0+15 in this wave's
+// LDS chunk, with whole-row coalesced loads (16 B per lane, 512 B per row).
+template <int RUN, bool F32>
+__device__ __forceinline__ void load_x(Slice<RUN, F32>& sl, int b0) {
+    constexpr int n = Slice<RUN, F32>::XB;
+    constexpr int lpr = F32 ? 32 : 16 * n, rpi = 64 / lpr;
     const int sub = sl.lane % lpr, rr = sl.lane / lpr;
     const int jb = sl.j0 + b0;
     for (int i = 0; i < 16 / rpi; ++i) {
         const int rl = i * rpi + rr;
         const int r = sl.m0 + rl;
-        if (r < sl.R && jb + (sub >> 4) < sl.KB)
-            sl.xs[rl * kXRow + sub] = *(const u32x4v*)(sl.x + (size_t)r * sl.K + (size_t)jb * kBlock + 8 * sub);
+        if (F32) {
+            if (r < sl.R && jb < sl.KB)
+                sl.xs[rl * kXRow + sub] =
+                    *(const u32x4v*)((const float*)sl.x + (size_t)r * sl.K + (size_t)jb * kBlock + 4 * sub);
+        } else {
+            if (r < sl.R && jb + (sub >> 4) < sl.KB)
+                sl.xs[rl * kXRow + sub] =
+                    *(const u32x4v*)((const uint16_t*)sl.x + (size_t)r * sl.K + (size_t)jb * kBlock + 8 * sub);
+        }
     }
 }
 
-// Leaf j0 + b: four matrix-core steps from +0 over the block's 128 k in k
-// order, then the block scale; +0 for a padding block. ai: the block's place in
-// the LDS chunk. A fragment: lane (c, q) holds row c at k = 32g + 8q .. +7.
-template <int RUN>
-__device__ __forceinline__ f32x4 leaf(Slice<RUN>& sl, int b, int ai) {
+// Eight fp32 values as three bf16 parts whose sum is each value exactly (for
+// |v| >= 2^-110; non-finite values keep only their first part): v = a + b + c
+// with a = v cut to bf16, b = (v - a) cut to bf16, c = v - a - b (both
+// differences exact). Pairs pack element 2i in the low half.
+__device__ __forceinline__ void split3(const u32x4v& lo, const u32x4v& hi, bf16x8& pa, bf16x8& pb, bf16x8& pc) {
+    const uint32_t u[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    uint32_t a[8], b[8], c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float v = __uint_as_float(u[i]);
+        a[i] = u[i] & 0xffff0000u;
+        const float r1 = v - __uint_as_float(a[i]);
+        b[i] = __float_as_uint(r1) & 0xffff0000u;
+        const float r2 = r1 - __uint_as_float(b[i]);
+        c[i] = __float_as_uint(r2) & 0xffff0000u;
+        if ((u[i] & 0x7f800000u) == 0x7f800000u) b[i] = c[i] = 0u;
+    }
+    u32x4v A, B, C;
+    A.x = (a[0] >> 16) | a[1]; A.y = (a[2] >> 16) | a[3]; A.z = (a[4] >> 16) | a[5]; A.w = (a[6] >> 16) | a[7];
+    B.x = (b[0] >> 16) | b[1]; B.y = (b[2] >> 16) | b[3]; B.z = (b[4] >> 16) | b[5]; B.w = (b[6] >> 16) | b[7];
+    C.x = (c[0] >> 16) | c[1]; C.y = (c[2] >> 16) | c[3]; C.z = (c[4] >> 16) | c[5]; C.w = (c[6] >> 16) | c[7];
+    pa = __builtin_bit_cast(bf16x8, A);
+    pb = __builtin_bit_cast(bf16x8, B);
+    pc = __builtin_bit_cast(bf16x8, C);
+}
+
+// Leaf j0 + b: matrix-core steps from +0 over the block's 128 k in k order,
+// then the block scale; +0 for a padding block. bf16 rows: four steps, one per
+// 32-k group; fp32 rows: twelve, the group's three bf16 parts in turn. ai: the
+// block's place in the LDS chunk. A fragment: lane (c, q) holds row c at
+// k = 32g + 8q .. +7.
+template <int RUN, bool F32>
+__device__ __forceinline__ f32x4 leaf(Slice<RUN, F32>& sl, int b, int ai) {
     if (sl.j0 + b >= sl.KB) return f32x4{0.f, 0.f, 0.f, 0.f};
     // decode here, per row tile, so the x loads are not held behind the weights
     asm volatile("" : "+v"(sl.w[b][0]), "+v"(sl.w[b][1]));
     const int c = sl.lane & 15, q = sl.lane >> 4;
-    bf16x8 a[4];
+    const u32x4v z = u32x4v{0, 0, 0, 0};
+    const bf16x8 wg[4] = {group_bf16(sl.w[b][0].x, sl.w[b][0].y), group_bf16(sl.w[b][0].z, sl.w[b][0].w),
+                          group_bf16(sl.w[b][1].x, sl.w[b][1].y), group_bf16(sl.w[b][1].z, sl.w[b][1].w)};
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-        const u32x4v v = sl.xs[c * kXRow + 16 * ai + 4 * g + q];
-        a[g] = __builtin_bit_cast(bf16x8, sl.row_ok ? v : u32x4v{0, 0, 0, 0});
+        if constexpr (F32) {
+            const u32x4v* p = sl.xs + c * kXRow + 8 * g + 2 * q;
+            bf16x8 pa, pb, pc;
+            split3(sl.row_ok ? p[0] : z, sl.row_ok ? p[1] : z, pa, pb, pc);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, wg[g], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb, wg[g], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pc, wg[g], acc, 0, 0, 0);
+        } else {
+            const u32x4v v = sl.xs[c * kXRow + 16 * ai + 4 * g + q];
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, sl.row_ok ? v : z), wg[g],
+                                                          acc, 0, 0, 0);
+        }
     }
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], group_bf16(sl.w[b][0].x, sl.w[b][0].y), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], group_bf16(sl.w[b][0].z, sl.w[b][0].w), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2], group_bf16(sl.w[b][1].x, sl.w[b][1].y), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[3], group_bf16(sl.w[b][1].z, sl.w[b][1].w), acc, 0, 0, 0);
     return acc * sl.sc[b];
 }
 
 // Root of the aligned run of LEN leaves starting at b0: (left subtree) + (right
-// subtree). The x of a two-block subtree (one block when RUN = 1) is staged on entering it.
-template <int RUN, int LEN>
+// subtree). A chunk's x is staged on entering the subtree it covers.
+template <int RUN, bool F32, int LEN>
 struct Run {
-    static __device__ __forceinline__ f32x4 root(Slice<RUN>& sl, int b0) {
-        if constexpr (LEN == kXBlocks) load_x(sl, b0, LEN);
-        const f32x4 l = Run<RUN, LEN / 2>::root(sl, b0);
-        const f32x4 r = Run<RUN, LEN / 2>::root(sl, b0 + LEN / 2);
+    static __device__ __forceinline__ f32x4 root(Slice<RUN, F32>& sl, int b0) {
+        if constexpr (LEN == Slice<RUN, F32>::XB) load_x(sl, b0);
+        const f32x4 l = Run<RUN, F32, LEN / 2>::root(sl, b0);
+        const f32x4 r = Run<RUN, F32, LEN / 2>::root(sl, b0 + LEN / 2);
         return l + r;
     }
 };
-template <int RUN>
-struct Run<RUN, 1> {
-    static __device__ __forceinline__ f32x4 root(Slice<RUN>& sl, int b0) {
-        if constexpr (RUN == 1) load_x(sl, b0, 1);
-        return leaf<RUN>(sl, b0, b0 % kXBlocks);
+template <int RUN, bool F32>
+struct Run<RUN, F32, 1> {
+    static __device__ __forceinline__ f32x4 root(Slice<RUN, F32>& sl, int b0) {
+        if constexpr (Slice<RUN, F32>::XB == 1) load_x(sl, b0);
+        return leaf(sl, b0, b0 % Slice<RUN, F32>::XB);
     }
 };
 
-// One workgroup: 16 columns [16t, 16t + 16), all rows. RUN = blocks per slice.
-template <int RUN>
-__global__ __launch_bounds__(1024) void fp8_rows_kernel(int R, int N, int KB, const uint16_t* __restrict__ x,
+// One workgroup: 16 columns [16t, 16t + 16), all rows. RUN = blocks per slice;
+// F32: rows of x are fp32 (else bf16).
+template <int RUN, bool F32>
+__global__ __launch_bounds__(1024) void fp8_rows_kernel(int R, int N, int KB, const void* __restrict__ x,
                                                         const uint8_t* __restrict__ pw,
                                                         const float* __restrict__ scale, float* __restrict__ y) {
     __shared__ float red[kMaxSlices * 4 * 64];
@@ -140,7 +186,7 @@ __global__ __launch_bounds__(1024) void fp8_rows_kernel(int R, int N, int KB, co
     const int t = blockIdx.x;
     const int K = KB * kBlock;
 
-    Slice<RUN> sl;
+    Slice<RUN, F32> sl;
     sl.xs = xsh + slice * 16 * kXRow;
     sl.x = x;
     sl.R = R;
@@ -168,7 +214,7 @@ __global__ __launch_bounds__(1024) void fp8_rows_kernel(int R, int N, int KB, co
         sl.m0 = m0;
         sl.row_ok = m0 + c < R;
         // low levels of the pair tree: the slice's run
-        const f32x4 v = Run<RUN, RUN>::root(sl, 0);
+        const f32x4 v = Run<RUN, F32, RUN>::root(sl, 0);
         if (S == 1) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -244,8 +290,8 @@ XP_API int xp_fp8_pack(int32_t n, int32_t k, const uint8_t* w, uint8_t* packed, 
     return launch_status();
 }
 
-XP_API int xp_fp8_rows(int32_t rows, int32_t n, int32_t k, const uint16_t* x, const uint8_t* packed,
-                       const float* scales, float* y, int32_t slices, void* stream) {
+static int fp8_rows_common(int32_t rows, int32_t n, int32_t k, const void* x, const uint8_t* packed,
+                           const float* scales, float* y, int32_t slices, bool f32, void* stream) {
     if (!fp8_shape_ok(n, k) || rows < 0) return XP_ERR_SHAPE;
     if (rows == 0) return XP_OK;
     if (!x || !packed || !scales || !y) return XP_ERR_NULL;
@@ -258,11 +304,33 @@ XP_API int xp_fp8_rows(int32_t rows, int32_t n, int32_t k, const uint16_t* x, co
     if (run > kMaxRun) return XP_ERR_SHAPE;
     hipStream_t s = (hipStream_t)stream;
     const dim3 grid(n / kCols), block(64 * S);
-    switch (run) {
-        case 1: hipLaunchKernelGGL(fp8_rows_kernel<1>, grid, block, 0, s, rows, n, KB, x, packed, scales, y); break;
-        case 2: hipLaunchKernelGGL(fp8_rows_kernel<2>, grid, block, 0, s, rows, n, KB, x, packed, scales, y); break;
-        case 4: hipLaunchKernelGGL(fp8_rows_kernel<4>, grid, block, 0, s, rows, n, KB, x, packed, scales, y); break;
-        default: return XP_ERR_SHAPE;
+#define XP_FP8_LAUNCH(RUN_, F32_)                                                                            \
+    hipLaunchKernelGGL((fp8_rows_kernel<RUN_, F32_>), grid, block, 0, s, rows, n, KB, x, packed, scales, y)
+    if (f32) {
+        switch (run) {
+            case 1: XP_FP8_LAUNCH(1, true); break;
+            case 2: XP_FP8_LAUNCH(2, true); break;
+            case 4: XP_FP8_LAUNCH(4, true); break;
+            default: return XP_ERR_SHAPE;
+        }
+    } else {
+        switch (run) {
+            case 1: XP_FP8_LAUNCH(1, false); break;
+            case 2: XP_FP8_LAUNCH(2, false); break;
+            case 4: XP_FP8_LAUNCH(4, false); break;
+            default: return XP_ERR_SHAPE;
+        }
     }
+#undef XP_FP8_LAUNCH
     return launch_status();
+}
+
+XP_API int xp_fp8_rows(int32_t rows, int32_t n, int32_t k, const uint16_t* x, const uint8_t* packed,
+                       const float* scales, float* y, int32_t slices, void* stream) {
+    return fp8_rows_common(rows, n, k, x, packed, scales, y, slices, false, stream);
+}
+
+XP_API int xp_fp8_rows_f32(int32_t rows, int32_t n, int32_t k, const float* x, const uint8_t* packed,
+                           const float* scales, float* y, int32_t slices, void* stream) {
+    return fp8_rows_common(rows, n, k, x, packed, scales, y, slices, true, stream);
 }

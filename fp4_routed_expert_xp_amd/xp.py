@@ -23,7 +23,7 @@ EXPORTS = (
     "xp_gateup_rows", "xp_gateup_rows_split", "xp_down_rows", "xp_combine",
     "xp_set_tiers", "xp_get_tiers", "xp_status_string", "xp_route_gateup", "xp_down_combine",
     "xp_prefill_gateup", "xp_prefill_down", "xp_fp8_packed_bytes", "xp_fp8_pack", "xp_fp8_rows",
-    "xp_gateup_rows_act16", "xp_down_rows_act16", "xp_combine_y16",
+    "xp_gateup_rows_act16", "xp_down_rows_act16", "xp_combine_y16", "xp_fp8_rows_f32",
 )
 
 
@@ -79,6 +79,7 @@ def lib():
         L.xp_fp8_packed_bytes.restype = sz
         L.xp_fp8_pack.argtypes = [i32, i32, P, P, P]
         L.xp_fp8_rows.argtypes = [i32, i32, i32, P, P, P, P, i32, P]
+        L.xp_fp8_rows_f32.argtypes = [i32, i32, i32, P, P, P, P, i32, P]
         L.xp_set_tiers.argtypes = [P, i32, P, i32]
         L.xp_get_tiers.argtypes = [P, P, P, P]
         L.xp_status_string.argtypes = [ctypes.c_int]
@@ -87,7 +88,7 @@ def lib():
                      "xp_gateup_rows_split", "xp_down_rows", "xp_combine", "xp_set_tiers", "xp_get_tiers",
                      "xp_route_gateup", "xp_down_combine", "xp_prefill_gateup", "xp_prefill_down",
                      "xp_fp8_pack", "xp_fp8_rows", "xp_gateup_rows_act16", "xp_down_rows_act16",
-                     "xp_combine_y16"):
+                     "xp_combine_y16", "xp_fp8_rows_f32"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -332,6 +333,17 @@ def xp_fp8_rows(rows: int, n: int, k: int, x, packed, scales, y, slices: int = 0
         _dev(y, torch.float32, "y", rows * n)
     _check(lib().xp_fp8_rows(int(rows), int(n), int(k), _ptr(x), _ptr(packed), _ptr(scales), _ptr(y),
                              int(slices), _stream(stream)), "xp_fp8_rows")
+
+
+def xp_fp8_rows_f32(rows: int, n: int, k: int, x, packed, scales, y, slices: int = 0, stream=None) -> None:
+    """y[rows][n] fp32 = x[rows][k] (fp32) times the packed FP8 matrix (see xp_fp8_rows_f32 in xp.h)."""
+    if rows > 0:
+        _dev(x, torch.float32, "x", rows * k)
+        _dev(packed, torch.uint8, "packed", n * k)
+        _dev(scales, torch.float32, "scales", ((n + 127) // 128) * (k // 128))
+        _dev(y, torch.float32, "y", rows * n)
+    _check(lib().xp_fp8_rows_f32(int(rows), int(n), int(k), _ptr(x), _ptr(packed), _ptr(scales), _ptr(y),
+                                 int(slices), _stream(stream)), "xp_fp8_rows_f32")
 
 
 # -------------------------------------------------------------- conveniences

@@ -252,6 +252,16 @@ int xp_fp8_pack(int32_t n, int32_t k, const uint8_t* w, uint8_t* packed, void* s
 int xp_fp8_rows(int32_t rows, int32_t n, int32_t k, const uint16_t* x, const uint8_t* packed,
                 const float* scales, float* y, int32_t slices, void* stream);
 
+/* The same for fp32 rows x[rows][k] (16-byte aligned). Each x value enters as
+ * three bf16 parts whose sum is the value exactly (for |x| >= 2^-110; an
+ * infinity or NaN enters as its first part alone), so every product is exact;
+ * block root q_j = twelve matrix-core steps from +0: for each 32-k group in k
+ * order, its three parts in turn. Same scale, tree, forms, invariance and
+ * tolerance as xp_fp8_rows [#2983, commit list: the FP8 commit registers f32
+ * and bf16 activation forms]. */
+int xp_fp8_rows_f32(int32_t rows, int32_t n, int32_t k, const float* x, const uint8_t* packed,
+                    const float* scales, float* y, int32_t slices, void* stream);
+
 /* ------------------------------------------------------------ pass sizes */
 
 /* Set the pass sizes used by later xp_route_bucket calls (host, process-wide,

@@ -142,6 +142,9 @@ def test_fp8_argument_checks():
     for slices in (3, 32, -1, 8):
         assert L.xp_fp8_rows(1, 16, 512, P, P, P, P, slices, None) == xp.XP_ERR_SHAPE, slices
     assert L.xp_fp8_rows(1, 16, 128 * 40, P, P, P, P, 4, None) == xp.XP_ERR_SHAPE  # P = 64: 16 blocks a slice
+    assert L.xp_fp8_rows_f32(1, 100, 4096, P, P, P, P, 0, None) == xp.XP_ERR_SHAPE
+    assert L.xp_fp8_rows_f32(1, 16, 128, None, P, P, P, 0, None) == xp.XP_ERR_NULL
+    assert L.xp_fp8_rows_f32(0, 16, 128, None, None, None, None, 0, None) == xp.XP_OK
 
 
 def test_bf16_storage_argument_checks():

@@ -54,6 +54,14 @@ class Fp8Matrix:
     def oracle(self, x_bits):
         return oracle.fp8_proj(x_bits, self.w, self.s)
 
+    def run_f32(self, x, slices=0):
+        R = x.shape[0]
+        y = torch.full((max(R, 1), self.N), float("nan"), dtype=torch.float32, device="cuda")
+        xd = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda() if R else None
+        xp.xp_fp8_rows_f32(R, self.N, self.K, xd, self.packed, self.s_dev, y, slices)
+        torch.cuda.synchronize()
+        return y.cpu().numpy()[:R]
+
 
 def bits(a):
     return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
@@ -190,3 +198,44 @@ def test_fp8_empty_and_errors():
     with pytest.raises(xp.XPError) as ei:
         xp.xp_fp8_rows(1, 16, 128, x, m.packed, m.s_dev, y, slices=2)   # P = 1: at most one slice
     assert ei.value.status == xp.XP_ERR_SHAPE
+
+
+def f32_rows(seed, R, K):
+    return (np.random.default_rng(seed).standard_normal((R, K)) * 2).astype(np.float32)
+
+
+@pytest.mark.parametrize("N,K", [(48, 384), (576, 4096), (64, 8192)])
+def test_fp8_f32_rows_match_oracle(N, K):
+    m = Fp8Matrix(N, K, layer=4)
+    for R in (1, 6, 16, 33):
+        x = f32_rows(SEED + R, R, K)
+        err = rel_err_rows(m.run_f32(x), oracle.fp8_proj_f32(x, m.w, m.s))
+        assert np.all(err <= TOL), (R, float(err.max()))
+
+
+def test_fp8_f32_rows_invariance():
+    """Row counts 1..17, every form, and planted NaN / +Inf rows: each row's bits
+    equal its one-row launch."""
+    m = Fp8Matrix(304, 1536, layer=5)
+    x = f32_rows(SEED, 17, 1536)
+    x[4, 100] = np.nan
+    x[9, 1000] = np.inf
+    alone = np.stack([m.run_f32(x[r:r + 1])[0] for r in range(17)])
+    for R in range(1, 18):
+        assert np.array_equal(bits(m.run_f32(x[:R])), bits(alone[:R])), R
+    for f in (4, 8, 16):
+        assert np.array_equal(bits(m.run_f32(x, slices=f)), bits(alone)), f
+    assert np.all(np.isnan(alone[4]))
+    ref = oracle.fp8_proj_f32(x[9:10], m.w, m.s)[0]
+    assert np.array_equal(np.isnan(alone[9]), np.isnan(ref))
+    assert np.array_equal(np.isposinf(alone[9]), np.isposinf(ref))
+
+
+def test_fp8_f32_one_hot_rows_are_exact():
+    """One-hot fp32 rows (parts 1, 0, 0) read back weight x block scale exactly."""
+    m = Fp8Matrix(304, 512, layer=6)
+    ks = [0, 5, 127, 128, 300, 511]
+    x = np.zeros((len(ks), 512), dtype=np.float32)
+    for r, k in enumerate(ks):
+        x[r, k] = 1.0
+    assert np.array_equal(bits(m.run_f32(x)), bits(oracle.fp8_proj_f32(x, m.w, m.s).astype(np.float32)))
