@@ -201,7 +201,7 @@ class Cell:
         from fp4_routed_expert_xp_amd import xp
         off = xp.xp_workspace_layout(self.d, self.cfg.R)
         E = self.cfg.E
-        distinct, gu_rows, dn_rows = [], [], []
+        distinct, gu_rows, dn_rows, gu_passes, dn_passes = [], [], [], [], []
         for ws in self.ws:
             b = ws.cpu().numpy()
             hdr = b[off[0]:off[0] + 8].view(np.int32)
@@ -211,7 +211,9 @@ class Cell:
             distinct.append(int((cnt > 0).sum()))
             gu_rows.append(int(gu[:, 3].sum()))     # rows computed incl. padding
             dn_rows.append(int(dn[:, 3].sum()))
-        return dict(distinct=distinct, gu_rows=gu_rows, dn_rows=dn_rows)
+            gu_passes.append(int(hdr[0]))
+            dn_passes.append(int(hdr[1]))
+        return dict(distinct=distinct, gu_rows=gu_rows, dn_rows=dn_rows, gu_passes=gu_passes, dn_passes=dn_passes)
 
 
 PATHS = {"four_calls": ("route", "gateup", "down", "combine"), "two_calls": ("route_gateup", "down_combine"),
@@ -257,15 +259,16 @@ def time_cell(cell: Cell, path: str, steps: int, warmup: int) -> dict:
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
-    e0.record()
-    for _ in range(steps):
+    ev[0].record()
+    for i in range(steps):
         g.replay()
-    e1.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / steps
+    ms = ev[0].elapsed_time(ev[steps]) / steps
+    each = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
     per = {}
     for kind in kinds:
         gk = _graph(lambda: [cell.call(kind, l) for l in range(cell.layers)])
@@ -274,7 +277,8 @@ def time_cell(cell: Cell, path: str, steps: int, warmup: int) -> dict:
         per[kind] = _replay_ms(gk, 5) * 1e3 / cell.layers
         del gk
     del g
-    return dict(path=path, ms_per_round=ms, wall_s=wall, kernel_us=per)
+    return dict(path=path, ms_per_round=ms, ms_min=each[0], ms_median=each[len(each) // 2], wall_s=wall,
+                kernel_us=per)
 
 
 def cell_report(cell: Cell, t: dict, copy_gbps: float) -> dict:
@@ -305,9 +309,12 @@ def cell_report(cell: Cell, t: dict, copy_gbps: float) -> dict:
     ops = gu_rows * 2 * I * H * (1 + 1 / 32) + dn_rows * H * I * (1 + 1 / 32)
     ops += (distinct * (2 * I * H + H * I)) / 2     # at least one decode pass per expert
     valu_us = ops / (CUS * LANES * CLOCK_GHZ * 1e9) * 1e6
+    # weight bytes streamed again by an expert's second and later passes
+    pass_bytes = (sum(st["gu_passes"]) * gu_w + sum(st["dn_passes"]) * dn_w) / L - distinct * (gu_w + dn_w)
     return dict(
         workload=cfg.name, path=t["path"], rows=R, layers=L,
-        round_ms=round(t["ms_per_round"], 4), layer_us=round(layer_us, 3),
+        round_ms=round(t["ms_per_round"], 4), round_ms_fastest=round(t["ms_min"], 4),
+        round_ms_median=round(t["ms_median"], 4), layer_us=round(layer_us, 3),
         rows_per_s=round(R / (t["ms_per_round"] / 1e3), 2),
         row_layers_per_s=round(R * L / (t["ms_per_round"] / 1e3), 1),
         distinct_experts=round(distinct, 2), unique_weight_bytes=int(unique_bytes),
@@ -316,7 +323,7 @@ def cell_report(cell: Cell, t: dict, copy_gbps: float) -> dict:
         kernel_us={kk: round(v, 3) for kk, v in t["kernel_us"].items()},
         gateup_kernel=gu_kind, gateup_gbps=round(gu_bytes / (gu_us * 1e-6) / 1e9, 1), gateup_bytes=int(gu_bytes),
         down_kernel=dn_kind, down_gbps=round(dn_bytes / (dn_us * 1e-6) / 1e9, 1), down_bytes=int(dn_bytes),
-        valu_bound_us=round(valu_us, 2),
+        valu_bound_us=round(valu_us, 2), pass_bytes=int(round(pass_bytes)),
     )
 
 
@@ -462,10 +469,28 @@ def cpu_baseline(budget_s: float) -> dict:
         if time.process_time() - cpu0 >= budget_s or l >= 8 or (time.process_time() - c0) * (l + 1) > 4 * budget_s:
             break
     per_layer = sum(times) / len(times)
+    # the multi-row workloads, one layer each, for context (same oracle, same threads)
+    others = {}
+    for name in ("four_same", "sixteen_random"):
+        c2 = synth.CONFIGS[name]
+        x, lg = synth.layer_inputs(c2, 0, plant=False)
+        ids, _ = oracle.route(lg, c2.k)
+        ex = {int(e): synth.layer_expert(c2, 0, int(e)) for e in np.unique(ids)}
+        t0 = time.perf_counter()
+        oracle.layer(x, lg, ex, c2.H, c2.I, c2.E, c2.k)
+        dt = time.perf_counter() - t0
+        others[name] = dict(rows_per_s=round(c2.R / (dt * 40), 4), s_per_layer=round(dt, 3))
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
     return dict(value=round(cfg.R / (per_layer * 40), 4), unit="rows/s", cores=int(threads), kind="oracle",
                 sample="%d of the 40 layers of the one-row round (1 row x 8 experts each), float64 C oracle, "
                        "OpenMP over (row, slot) pairs; %.3f s per layer, scaled to a 40-layer round" %
-                       (len(times), per_layer))
+                       (len(times), per_layer),
+                host={"cpu": model, "logical_cpus": os.cpu_count()}, other_workloads=others)
 
 
 def main():
