@@ -281,9 +281,12 @@ XP_API size_t xp_fp8_packed_bytes(int32_t n, int32_t k) {
     return fp8_shape_ok(n, k) ? (size_t)n * (size_t)k : 0;
 }
 
+static bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
 XP_API int xp_fp8_pack(int32_t n, int32_t k, const uint8_t* w, uint8_t* packed, void* stream) {
     if (!fp8_shape_ok(n, k)) return XP_ERR_SHAPE;
     if (!w || !packed) return XP_ERR_NULL;
+    if (!aligned(w, 8) || !aligned(packed, 16)) return XP_ERR_SHAPE;
     const size_t threads = (size_t)(n / kCols) * (k / kBlock) * 64;
     const unsigned grid = (unsigned)((threads + 255) / 256);
     hipLaunchKernelGGL(fp8_pack_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, n, k, w, packed);
@@ -295,6 +298,7 @@ static int fp8_rows_common(int32_t rows, int32_t n, int32_t k, const void* x, co
     if (!fp8_shape_ok(n, k) || rows < 0) return XP_ERR_SHAPE;
     if (rows == 0) return XP_OK;
     if (!x || !packed || !scales || !y) return XP_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 4) || !aligned(y, 4)) return XP_ERR_SHAPE;
     const int KB = k / kBlock;
     const int P = next_pow2(KB);
     int S = slices;

@@ -242,11 +242,13 @@ size_t xp_fp8_packed_bytes(int32_t n, int32_t k);
 /* Repack w [n][k] (row n = output column n, E4M3FN bytes, k contiguous) into
  * the kernel's layout: per 16-column tile and 128-k block, 2,048 bytes, lane
  * l's 32 bytes at l*32 holding, for g = 0..3, the 8 bytes of column
- * 16*tile + l%16 at k = 128*block + 32g + 8*(l/16) .. +7. One-time setup. */
+ * 16*tile + l%16 at k = 128*block + 32g + 8*(l/16) .. +7. One-time setup.
+ * w must be 8-byte and packed 16-byte aligned (else XP_ERR_SHAPE). */
 int xp_fp8_pack(int32_t n, int32_t k, const uint8_t* w, uint8_t* packed, void* stream);
 
-/* y[rows][n] fp32 = x[rows][k] (bf16 bit patterns, 16-byte aligned) times the
- * packed matrix, scaled per block. slices: 0 picks the form (min(16, P) waves
+/* y[rows][n] fp32 = x[rows][k] (bf16 bit patterns) times the packed matrix,
+ * scaled per block. x and packed must be 16-byte aligned, scales and y 4-byte
+ * aligned (else XP_ERR_SHAPE). slices: 0 picks the form (min(16, P) waves
  * per 16 columns); 1, 2, 4, 8 or 16 forces that many (at most P, and P/slices
  * <= 8), else XP_ERR_SHAPE. Any row count >= 0. */
 int xp_fp8_rows(int32_t rows, int32_t n, int32_t k, const uint16_t* x, const uint8_t* packed,

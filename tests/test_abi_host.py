@@ -145,6 +145,11 @@ def test_fp8_argument_checks():
     assert L.xp_fp8_rows_f32(1, 100, 4096, P, P, P, P, 0, None) == xp.XP_ERR_SHAPE
     assert L.xp_fp8_rows_f32(1, 16, 128, None, P, P, P, 0, None) == xp.XP_ERR_NULL
     assert L.xp_fp8_rows_f32(0, 16, 128, None, None, None, None, 0, None) == xp.XP_OK
+    # misaligned pointers are refused before any launch
+    odd = ctypes.c_void_p(0x1008)
+    assert L.xp_fp8_rows(1, 16, 128, odd, P, P, P, 0, None) == xp.XP_ERR_SHAPE
+    assert L.xp_fp8_rows_f32(1, 16, 128, P, odd, P, P, 0, None) == xp.XP_ERR_SHAPE
+    assert L.xp_fp8_pack(16, 128, ctypes.c_void_p(0x1004), P, None) == xp.XP_ERR_SHAPE
 
 
 def test_bf16_storage_argument_checks():
