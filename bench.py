@@ -42,7 +42,7 @@ TRAFFIC = dict(sources="73054fba", fetch_kib=34974.5, write_kib=66.4,
 ROOFLINE_SOURCES = ("xp_rows.hip", "xp_common.h", "xp_route_dev.h", "xp_chain_asm.h")
 # The same for the dense FP8 projection kernel at 4096 x 4096 (grid of 256
 # workgroups; mean over its launches at 1, 8 and 16 rows), tied to xp_fp8.hip.
-FP8_TRAFFIC = dict(sources="6d034b72", fetch_kib=8525.3, write_kib=133.3)
+FP8_TRAFFIC = dict(sources="fe07a71a", fetch_kib=8525.4, write_kib=133.3)
 FP8_SOURCES = ("xp_fp8.hip", "xp_common.h")
 
 
