@@ -543,12 +543,13 @@ def main():
         if name in SWEEP_CELLS and not args.no_tier_sweep:
             # same rows, other pass sizes: the bits are unchanged (the probe
             # tests check it), only the time moves
+            in_force = xp.xp_get_tiers()
             for gu, dn in TIER_SWEEP:
                 xp.xp_set_tiers(list(gu), list(dn))
                 try:
                     t = time_cell(cell, "two_calls", args.steps, args.warmup)
                 finally:
-                    xp.xp_set_tiers(None, None)
+                    xp.xp_set_tiers(*in_force)
                 key = "%s/two_calls/tiers_gu%s_dn%s" % (name, "-".join(map(str, gu)), "-".join(map(str, dn)))
                 rep = cell_report(cell, t, copy_gbps)
                 rep["tiers"] = {"gate_up": list(gu), "down": list(dn)}
@@ -580,7 +581,8 @@ def main():
                                "(xp_route_gateup, xp_down_combine)" % (decode[0], head["rows"], args.layers,
                                                                         base.H, base.I, base.E, base.k),
                    "rows": head["rows"], "layers": args.layers, "hidden": base.H, "inter": base.I,
-                   "experts": base.E, "top_k": base.k, "path": "two_calls"},
+                   "experts": base.E, "top_k": base.k, "path": "two_calls",
+                   "pass_sizes": dict(zip(("gate_up", "down"), xp.xp_get_tiers()))},
         "roofline": {"kernel": "gateup_one_row_kernel (xp_route_gateup)" if head["rows"] == 1
                      else "route_*_kernel + gateup_kernel<0> (xp_route_gateup)", "bound": "hbm",
                      "achieved": round(achieved, 1), "bytes_per_launch": head["gateup_bytes"],

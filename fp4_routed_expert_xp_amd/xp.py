@@ -91,7 +91,38 @@ def lib():
                      "xp_combine_y16", "xp_fp8_rows_f32"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
+        try:
+            _tiers_from_env()
+        except ValueError:
+            _lib = None
+            raise
     return _lib
+
+
+TIER_ENV = ("XP_TIERS_GU", "XP_TIERS_DN")
+
+
+def _tiers_from_env() -> None:
+    """Pass sizes from XP_TIERS_GU / XP_TIERS_DN ("2,4,6,8" style; unset or blank
+    keeps the library's default). A malformed value is refused by name."""
+    vals = []
+    for name in TIER_ENV:
+        v = os.environ.get(name, "").strip()
+        if not v:
+            vals.append(None)
+            continue
+        try:
+            vals.append([int(t) for t in v.split(",")])
+        except ValueError:
+            raise ValueError("%s=%r: expected a comma-separated list of pass sizes" % (name, v)) from None
+    if vals == [None, None]:
+        return
+    try:
+        xp_set_tiers(*vals)
+    except XPError:
+        raise ValueError("%s=%r, %s=%r: pass sizes must be strictly increasing, each in 2..8"
+                         % (TIER_ENV[0], os.environ.get(TIER_ENV[0], ""), TIER_ENV[1],
+                            os.environ.get(TIER_ENV[1], ""))) from None
 
 
 def xp_status_string(status: int) -> str:

@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -166,3 +167,21 @@ def test_bf16_storage_argument_checks():
     assert L.xp_gateup_rows_act16(ctypes.byref(d), 4, P, P, P, need - 1, P, None) == xp.XP_ERR_WORKSPACE
     assert L.xp_down_rows_act16(ctypes.byref(d), 4, P, P, P, need - 1, P, None) == xp.XP_ERR_WORKSPACE
     assert L.xp_combine_y16(ctypes.byref(d), -1, P, P, P, None) == xp.XP_ERR_SHAPE
+
+
+def _tiers_in_child(env):
+    code = ("from fp4_routed_expert_xp_amd import xp\n"
+            "xp.lib()\n"
+            "print(xp.xp_get_tiers())\n")
+    full = dict(os.environ, **env)
+    return subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=full, cwd=ROOT)
+
+
+def test_tiers_from_environment():
+    r = _tiers_in_child({"XP_TIERS_GU": "4", "XP_TIERS_DN": " "})
+    assert r.returncode == 0, r.stderr
+    assert "[4]" in r.stdout and "[2, 4]" in r.stdout          # blank keeps the default for down
+    r = _tiers_in_child({"XP_TIERS_GU": "2,x", "XP_TIERS_DN": ""})
+    assert r.returncode != 0 and "XP_TIERS_GU" in r.stderr
+    r = _tiers_in_child({"XP_TIERS_GU": "", "XP_TIERS_DN": "4,2"})
+    assert r.returncode != 0 and "XP_TIERS_DN" in r.stderr
