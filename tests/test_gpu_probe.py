@@ -63,7 +63,7 @@ def release_layer():
 
 def _matrix(layer, tag):
     cfg = layer.cfg
-    differ = 0
+    differ, cases, red = 0, 0, 0
     for R in PROBE_ROWS:
         for routing in ROUTINGS:
             for planted in (False, True):
@@ -72,6 +72,9 @@ def _matrix(layer, tag):
                 log("probe %s R=%d %s %s: %d rows differ" % (tag, R, routing, "planted" if planted else "finite",
                                                                bad))
                 differ += bad
+                cases += 1
+                red += 1 if bad else 0
+    log("SUMMARY probe %s: %d cases, %d equal to their solo launches, %d differ" % (tag, cases, cases - red, red))
     return differ
 
 
