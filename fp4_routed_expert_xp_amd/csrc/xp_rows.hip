@@ -7,7 +7,8 @@
 // the up leaves); down items run 8 waves. For each of its groups a lane loads
 // 16 bytes of codes (one coalesced 1 KiB read per wave in the packed layout) and
 // one scale byte, decodes the 32 weights once (v_cvt_scalef32_pk_f32_fp4 with
-// scale 1, exact) and runs every row of the pass through them: per row a fused
+// scale 1, exact; eight at a time, each dword just before its quarter of the
+// chain) and runs every row of the pass through them: per row a fused
 // multiply-add chain from +0 over the 32 products in k order (Chain<P>), then
 // the group's scale applied by one fused multiply-add into the row's leaf. The
 // leaves meet in LDS and one thread per (row, column) adds them by the fixed
@@ -35,15 +36,15 @@ __device__ __forceinline__ f32x2 fp4x2(uint32_t v) {
 
 __device__ __forceinline__ float e4m3(uint32_t byte) { return __builtin_amdgcn_cvt_f32_fp8((int)byte, 0); }
 
-__device__ __forceinline__ void decode32(u32x4 c, float (&w)[32]) {
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        f32x2 a;
-        a = fp4x2<0>(c[d]); w[8 * d + 0] = a.x; w[8 * d + 1] = a.y;
-        a = fp4x2<1>(c[d]); w[8 * d + 2] = a.x; w[8 * d + 3] = a.y;
-        a = fp4x2<2>(c[d]); w[8 * d + 4] = a.x; w[8 * d + 5] = a.y;
-        a = fp4x2<3>(c[d]); w[8 * d + 6] = a.x; w[8 * d + 7] = a.y;
-    }
+// One dword of codes (k ascending from the low nibble) -> its eight weights,
+// exact fp32. A group is decoded one dword at a time, just before the quarter
+// of the chain that uses it, so only eight decoded weights are live at once.
+__device__ __forceinline__ void decode8(uint32_t c, float (&w)[8]) {
+    f32x2 a;
+    a = fp4x2<0>(c); w[0] = a.x; w[1] = a.y;
+    a = fp4x2<1>(c); w[2] = a.x; w[3] = a.y;
+    a = fp4x2<2>(c); w[4] = a.x; w[5] = a.y;
+    a = fp4x2<3>(c); w[6] = a.x; w[7] = a.y;
 }
 
 // Leaves l0..l7 at a[0], a[stride], ..., a[7*stride].
@@ -81,13 +82,19 @@ __device__ __forceinline__ u32x4 load_codes(gcodes_t p) {
 #ifndef XP_DN_DEPTH_1
 #define XP_DN_DEPTH_1 2
 #endif
+#ifndef XP_GU_DEPTH_4
+#define XP_GU_DEPTH_4 2  // passes of 3-4 rows (5-8 rows: one group in flight)
+#endif
+#ifndef XP_DN_DEPTH_4
+#define XP_DN_DEPTH_4 2
+#endif
 template <int P>
 struct GuDepth {
-    static constexpr int value = P <= 2 ? XP_GU_DEPTH_1 : (P <= 4 ? 4 : 2);
+    static constexpr int value = P <= 2 ? XP_GU_DEPTH_1 : (P <= 4 ? XP_GU_DEPTH_4 : 1);
 };
 template <int P>
 struct DnDepth {
-    static constexpr int value = P == 1 ? XP_DN_DEPTH_1 : (P <= 4 ? 4 : 1);
+    static constexpr int value = P == 1 ? XP_DN_DEPTH_1 : (P <= 4 ? XP_DN_DEPTH_4 : 1);
 };
 
 // ------------------------------------------------------------------ gate/up
@@ -121,15 +128,17 @@ __device__ __forceinline__ void gu_leaf(gcodes_t cc, gbytes_t ss, const uint32_t
 #pragma unroll
         for (int s = 0; s < D; ++s) {
             const int i = i0 + s;
-            float w[32];
-            decode32(bc[s], w);
             const float sc = e4m3(bs[s]);
             uint32_t xc[P];
 #pragma unroll
             for (int r = 0; r < P; ++r) xc[r] = bx[s][r];
+            const u32x4 cw = bc[s];
             load(s, i + D);
-            float p[P];
-            Chain<P>::bf16(w, xc, p);
+            float p[P], xa[P], xb[P];
+            { float w[8]; decode8(cw[0], w); Chain<P>::head_bf16(w, xc, xa, xb, p); }
+            { float w[8]; decode8(cw[1], w); Chain<P>::tail1(w, xa, xb, p); }
+            { float w[8]; decode8(cw[2], w); Chain<P>::tail2(w, xa, xb, p); }
+            { float w[8]; decode8(cw[3], w); Chain<P>::tail3(w, xa, xb, p); }
             const bool valid = leaf + 8 * i < G;
 #pragma unroll
             for (int r = 0; r < P; ++r) {
@@ -349,23 +358,24 @@ __device__ __forceinline__ void dn_item(const xp_expert* __restrict__ experts, c
 #pragma unroll
         for (int s = 0; s < D; ++s) {
             const int i = i0 + s;
-            float w[32];
-            decode32(bc[s], w);
             const float sc = e4m3(bs[s]);
-            float p[P];
+            const u32x4 cw = bc[s];
+            float p[P], xa[P], xb[P];
             if constexpr (A16) {
                 uint32_t xc[P];
 #pragma unroll
                 for (int r = 0; r < P; ++r) xc[r] = bx16[s][r];
                 load(s, i + D);
-                Chain<P>::bf16(w, xc, p);
+                { float w[8]; decode8(cw[0], w); Chain<P>::head_bf16(w, xc, xa, xb, p); }
             } else {
-                float xa[P], xb[P];
 #pragma unroll
                 for (int r = 0; r < P; ++r) { xa[r] = bx[s][r].x; xb[r] = bx[s][r].y; }
                 load(s, i + D);
-                Chain<P>::f32(w, xa, xb, p);
+                { float w[8]; decode8(cw[0], w); Chain<P>::head_f32(w, xa, xb, p); }
             }
+            { float w[8]; decode8(cw[1], w); Chain<P>::tail1(w, xa, xb, p); }
+            { float w[8]; decode8(cw[2], w); Chain<P>::tail2(w, xa, xb, p); }
+            { float w[8]; decode8(cw[3], w); Chain<P>::tail3(w, xa, xb, p); }
             const bool valid = leaf + 8 * i < G;
 #pragma unroll
             for (int r = 0; r < P; ++r) {
