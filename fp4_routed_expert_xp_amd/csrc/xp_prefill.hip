@@ -103,6 +103,32 @@ __device__ __forceinline__ bf16x8 decode8(uint32_t v, float s) {
 
 __device__ __forceinline__ float e4m3f(uint32_t byte) { return __builtin_amdgcn_cvt_f32_fp8((int)byte, 0); }
 
+// The same eight products when the scale is a positive power of two: the
+// convert applies only the exponent of its fp32 scale operand (its sign and
+// mantissa are not used), which for 2^e is the whole scale, so each bf16 is
+// code * 2^e exactly, one instruction per two weights.
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16x8 decode8_pow2(uint32_t v, float s) {
+    u32x4v r;
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 0));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 1));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 2));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 3));
+    return __builtin_bit_cast(bf16x8, r);
+}
+
+// True on every lane when the four E4M3 scale bytes a..d of every lane of the
+// wave are positive normal powers of two (sign and mantissa bits clear,
+// exponent field non-zero); then decode8_pow2 is exact for the whole group.
+__device__ __forceinline__ bool wave_scales_pow2(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    const uint32_t v = a | (b << 8) | (c << 16) | (d << 24);
+    const bool sign_mant_clear = (v & 0x87878787u) == 0u;
+    // each byte's exponent field (a multiple of 8 in 0x08..0x78) plus 0x78 sets
+    // that byte's top bit exactly when the field is non-zero
+    const bool exp_nonzero = (((v & 0x78787878u) + 0x78787878u) & 0x80808080u) == 0x80808080u;
+    return __all(sign_mant_clear && exp_nonzero);
+}
+
 // Item i -> (expert, first row of the block, rows in the block, column block).
 struct Item {
     int e, m0, rows, nt;
@@ -225,8 +251,13 @@ __device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint16_
     };
     bf16x8 bf[2][4];
     auto decode_b = [&](int buf, int slot) {
+        if (wave_scales_pow2(bs[slot][0], bs[slot][1], bs[slot][2], bs[slot][3])) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) bf[buf][q] = decode8(bc[slot][q], e4m3f(bs[slot][q]));
+            for (int q = 0; q < 4; ++q) bf[buf][q] = decode8_pow2(bc[slot][q], e4m3f(bs[slot][q]));
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) bf[buf][q] = decode8(bc[slot][q], e4m3f(bs[slot][q]));
+        }
     };
 
     f32x4 acc[NS][2][2];
@@ -425,8 +456,13 @@ __device__ __forceinline__ void dn_item(const DnArgs& a, const Item& it, uint16_
     };
     bf16x8 bf[2][2];
     auto decode_b = [&](int buf, int slot) {
-        bf[buf][0] = decode8(bc[slot][0], e4m3f(bs[slot][0]));
-        bf[buf][1] = decode8(bc[slot][1], e4m3f(bs[slot][1]));
+        if (wave_scales_pow2(bs[slot][0], bs[slot][1], 0x38u, 0x38u)) {  // two fragments: pad with 1.0
+            bf[buf][0] = decode8_pow2(bc[slot][0], e4m3f(bs[slot][0]));
+            bf[buf][1] = decode8_pow2(bc[slot][1], e4m3f(bs[slot][1]));
+        } else {
+            bf[buf][0] = decode8(bc[slot][0], e4m3f(bs[slot][0]));
+            bf[buf][1] = decode8(bc[slot][1], e4m3f(bs[slot][1]));
+        }
     };
 
     f32x4 acc[NS][2];

@@ -83,6 +83,39 @@ def scales(seed: int, layer: int, expert: int, tensor: int, N: int, K: int,
     return ((e + 7) << 3).astype(np.uint8).reshape(N, K // 32)
 
 
+def any_scales(seed: int, layer: int, expert: int, tensor: int, N: int, K: int) -> np.ndarray:
+    """E4M3FN bytes uniform over the 254 non-NaN codes (both signs, zero, subnormals,
+    every mantissa; 0x7F and 0xFF skipped); plain layout [N][K/32] uint8. Drawn from
+    the stream of ``tensor`` + 100, so they differ from the power-of-two scales."""
+    w = stream(stream_key(seed, layer, tensor + 100, expert), 0, N * (K // 32))
+    b = ((w >> np.uint64(32)) * np.uint64(254)) >> np.uint64(32)
+    b = np.where(b >= np.uint64(0x7F), b + np.uint64(1), b)
+    return b.astype(np.uint8).reshape(N, K // 32)
+
+
+def mixed_scales(seed: int, layer: int, expert: int, tensor: int, N: int, K: int,
+                 emin: int, emax: int) -> np.ndarray:
+    """Scale bytes that mix both kinds by 32-group column: groups g = 0 mod 3 take
+    any_scales in every row, groups g = 1 mod 3 take them in rows n = 0 mod 5, and
+    the rest keep the power-of-two draw of ``scales``."""
+    s = scales(seed, layer, expert, tensor, N, K, emin, emax)
+    a = any_scales(seed, layer, expert, tensor, N, K)
+    g = np.arange(K // 32)[None, :]
+    n = np.arange(N)[:, None]
+    pick = (g % 3 == 0) | ((g % 3 == 1) & (n % 5 == 0))
+    return np.where(pick, a, s)
+
+
+def expert_mixed(seed: int, layer: int, e: int, H: int, I: int, emin: int, emax: int) -> dict:
+    """``expert`` with every matrix's scales from ``mixed_scales``."""
+    out = expert(seed, layer, e, H, I, emin, emax)
+    shapes = {"gate": (I, H), "up": (I, H), "down": (H, I)}
+    for m, (_, ts) in MATRICES.items():
+        N, K = shapes[m]
+        out[m + "_scales"] = mixed_scales(seed, layer, e, ts, N, K, emin, emax)
+    return out
+
+
 def expert(seed: int, layer: int, e: int, H: int, I: int, emin: int, emax: int) -> dict:
     """The six plain-layout arrays of one expert: gate/up are [I][H], down is [H][I]."""
     return dict(

@@ -37,6 +37,22 @@ class DeviceLayer:
         return synth.layer_expert(self.cfg, self.layer, e)
 
 
+class HostLayer:
+    """A layer built from host experts (plain layout), packed on the GPU: for
+    weights the device generator does not draw, such as general E4M3 scales."""
+
+    def __init__(self, cfg: synth.Config, experts: dict):
+        self.cfg = cfg
+        self.d = xp.dims(cfg.H, cfg.I, cfg.E, cfg.k)
+        self.host = experts
+        self.packed = {e: xp.pack_expert({n: to_dev(a) for n, a in ex.items()}) for e, ex in experts.items()}
+        self.table = xp.expert_table(cfg.E, self.packed)
+        torch.cuda.synchronize()
+
+    def host_expert(self, e: int) -> dict:
+        return self.host[e]
+
+
 def to_dev(a: np.ndarray) -> torch.Tensor:
     if a.dtype == np.uint16:
         return torch.from_numpy(a.view(np.int16).copy()).cuda()

@@ -242,3 +242,21 @@ def test_largest_experts_and_topk(maxed_layer, R):
     fused = run_fused(maxed_layer, x, lg)
     for n in ("topk_w", "act", "out", "y"):
         assert np.array_equal(bits(res[n]), bits(fused[n])), n
+
+
+@pytest.mark.parametrize("R", [1, 5, 16])
+def test_tiny_general_scales(R):
+    """Scale bytes over every finite E4M3FN value (negative, zero, subnormal,
+    non-power-of-two) in part of the groups: values within the tolerance of the
+    float64 oracle, g and u bit-equal to the fp32 replay."""
+    from gpu_helpers import HostLayer
+    experts = {e: synth.expert_mixed(TINY.weight_seed, 0, e, TINY.H, TINY.I, TINY.emin, TINY.emax)
+               for e in range(TINY.E)}
+    layer = HostLayer(TINY, experts)
+    log("tiny general scales R=%d" % R)
+    x = synth.activations(TINY.seed, 600 + R, R, TINY.H)
+    lg = synth.logits(TINY.seed, 600 + R, R, TINY.E)
+    res = run_path(layer, x, lg, split=True, canary=True)
+    ref = _oracle_layer(layer, x, lg)
+    _check_values(res, ref, R)
+    _check_chains(layer, x, res, range(R))

@@ -208,3 +208,21 @@ def test_prefill_chunk_invariance_release_width(prefill_layer):
             a = np.ascontiguousarray(full[name][r0:r0 + n]).view(np.uint32)
             b = np.ascontiguousarray(part[name]).view(np.uint32)
             assert np.array_equal(a, b), (r0, n, name)
+
+
+def test_prefill_general_scales():
+    """Scale bytes over every finite E4M3FN value (negative, zero, subnormal,
+    non-power-of-two) in a third of the groups and in some rows of another third;
+    the rest powers of two, so both weight decodes of the kernels run in one launch."""
+    from gpu_helpers import HostLayer
+    cfg = MID
+    experts = {e: synth.expert_mixed(cfg.weight_seed, 0, e, cfg.H, cfg.I, cfg.emin, cfg.emax) for e in range(cfg.E)}
+    layer = HostLayer(cfg, experts)
+    for R in (3, 300):
+        log("prefill mid, general scales, R=%d" % R)
+        x = synth.activations(cfg.seed, 500 + R, R, cfg.H)
+        lg = synth.logits(cfg.seed, 500 + R, R, cfg.E, bias_sigma=0.5)
+        res = run_prefill(layer, x, lg)
+        ref = oracle_rows(layer, x, lg)
+        worst = check_rows(res, ref)
+        log("  worst per-row relative error %.2e" % worst)

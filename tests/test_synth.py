@@ -68,3 +68,23 @@ def test_fp8_generators():
     assert s.shape == (3, 4) and s.dtype == np.float32
     e = np.log2(s)
     assert np.all(e == np.round(e)) and e.min() >= -10 and e.max() <= -6
+
+
+def test_general_and_mixed_scales():
+    # any_scales: every non-NaN E4M3FN byte is possible, NaN bytes never appear
+    a = synth.any_scales(5, 0, 1, synth.GATE_SCALES, 512, 4096)
+    assert not np.any((a == 0x7F) | (a == 0xFF))
+    assert np.unique(a).size == 254
+    # mixed_scales: power-of-two draw except where the rule puts general bytes
+    N, K = 40, 32 * 9
+    m = synth.mixed_scales(5, 0, 1, synth.UP_SCALES, N, K, -4, 2)
+    p = synth.scales(5, 0, 1, synth.UP_SCALES, N, K, -4, 2)
+    g = synth.any_scales(5, 0, 1, synth.UP_SCALES, N, K)
+    for n in range(N):
+        for j in range(K // 32):
+            want = g[n, j] if (j % 3 == 0 or (j % 3 == 1 and n % 5 == 0)) else p[n, j]
+            assert m[n, j] == want
+    ex = synth.expert_mixed(5, 0, 1, 64, 32, -4, 2)
+    plain = synth.expert(5, 0, 1, 64, 32, -4, 2)
+    for name in ("gate_codes", "up_codes", "down_codes"):
+        assert np.array_equal(ex[name], plain[name])
