@@ -226,3 +226,41 @@ def test_prefill_general_scales():
         ref = oracle_rows(layer, x, lg)
         worst = check_rows(res, ref)
         log("  worst per-row relative error %.2e" % worst)
+
+
+def test_prefill_weight_decodes_agree_bit_for_bit():
+    """The power-of-two weight decode and the general one give the same bf16
+    weights. Layer B differs from layer A only in one scale byte per 32 columns
+    and group, made 1.375 (0x3B) where that column's 32 codes of the group are
+    +0, so B's weights equal A's; every wave-group of A runs the power-of-two
+    decode and every wave-group of B the general one, and the outputs must be
+    bit-equal."""
+    from gpu_helpers import HostLayer, bits
+    cfg = MID
+    a_ex, b_ex = {}, {}
+    for e in range(cfg.E):
+        ex = synth.expert(cfg.weight_seed, 0, e, cfg.H, cfg.I, cfg.emin, cfg.emax)
+        bx = {k: v.copy() for k, v in ex.items()}
+        for m in ("gate", "up", "down"):
+            codes, scales = ex[m + "_codes"], ex[m + "_scales"]
+            N, G = scales.shape
+            for g in range(G):
+                for blk in range(N // 32):
+                    n = 32 * blk + g % 32
+                    codes[n, 16 * g:16 * g + 16] = 0
+            bx[m + "_codes"] = codes.copy()
+            sb = scales.copy()
+            for g in range(G):
+                for blk in range(N // 32):
+                    sb[32 * blk + g % 32, g] = 0x3B
+            bx[m + "_scales"] = sb
+        a_ex[e], b_ex[e] = ex, bx
+    la, lb = HostLayer(cfg, a_ex), HostLayer(cfg, b_ex)
+    R = 300
+    log("prefill mid, two weight decodes, R=%d" % R)
+    x = synth.activations(cfg.seed, 700, R, cfg.H)
+    lg = synth.logits(cfg.seed, 700, R, cfg.E, bias_sigma=0.5)
+    ra, rb = run_prefill(la, x, lg), run_prefill(lb, x, lg)
+    for name in ("act", "out", "y"):
+        assert np.array_equal(bits(ra[name]), bits(rb[name])), name
+    check_rows(ra, oracle_rows(la, x, lg))
