@@ -428,6 +428,92 @@ __global__ __launch_bounds__(512, 4) void down_kernel(const xp_expert* __restric
     }
 }
 
+// ------------------------------------------------- one-row down + combine
+// With one row every down pass is a one-slot pass, and a set of columns needs
+// only the k passes' outputs for those columns to be combined. Workgroup b
+// owns the 16 columns 16b .. 16b+15 for every pass: wave w walks leaf w % 8
+// for passes 4*(w/8) .. 4*(w/8)+3, one pass per row of 16 lanes, so the DPP
+// row broadcast hands each row its own pass's act values (lane m of a row
+// holds the act pair (2m, 2m+1) of its pass's group). Per (pass, column) the
+// arithmetic is dn_item's: the same chain, scaled fma, leaf order and tree.
+// The leaves meet in LDS, out is stored, and the combine's fma chain over
+// slots runs in the same workgroup, so no combine launch follows.
+// Workgroups: hidden / 16; waves: 8 * ceil(k / 4), so k <= 8.
+constexpr int kNarrow = 16;
+
+__global__ __launch_bounds__(1024) void down_combine_one_row_kernel(
+    const xp_expert* __restrict__ experts, const float* __restrict__ act, const int32_t* __restrict__ entry,
+    const int4* __restrict__ passes, const float* __restrict__ topk_w, int H, int I, int k,
+    float* __restrict__ out, float* __restrict__ y) {
+    __shared__ float red[16][kTile];          // [wave][lane] leaf values
+    __shared__ float sout[8][kNarrow];        // [slot][column] outputs
+    constexpr int D = DnDepth<1>::value;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int leaf = wave & 7, grp = wave >> 3;
+    const int c = lane & 15;
+    const int pass = min(4 * grp + (lane >> 4), k - 1);  // rows past the k-th pass repeat the last
+    const int4 ps = passes[pass];
+    const int slot = entry[ps.y];                        // one row: entry = slot
+    const int n = blockIdx.x * kNarrow + c;
+    const int G = I >> 5;
+    const xp_expert ex = experts[ps.x];
+    const size_t ch = (size_t)(n / kTile) * G * kTile + (n % kTile);
+    const gcodes_t cc = (gcodes_t)ex.down_codes + ch;
+    const gbytes_t ss = (gbytes_t)ex.down_scales + ch;
+    const float* ar = act + (size_t)slot * I + 2 * c;
+
+    const int ng = (G + 7) >> 3;
+    float acc = 0.0f;
+    u32x4 bc[D];
+    uint32_t bs[D];
+    float2 bx[D];
+    auto load = [&](int s, int i) {
+        const int g = min(leaf + 8 * i, G - 1);
+        bc[s] = load_codes(cc + (size_t)g * kTile);
+        bs[s] = ss[(size_t)g * kTile];
+        bx[s] = *(const float2*)(ar + 32 * g);
+    };
+#pragma unroll
+    for (int s = 0; s < D; ++s) load(s, s);
+    for (int i0 = 0; i0 < ng; i0 += D) {
+#pragma unroll
+        for (int s = 0; s < D; ++s) {
+            const int i = i0 + s;
+            const float sc = e4m3(bs[s]);
+            const u32x4 cw = bc[s];
+            float p[1], xa[1] = {bx[s].x}, xb[1] = {bx[s].y};
+            load(s, i + D);
+            { float w[8]; decode8(cw[0], w); Chain<1>::head_f32(w, xa, xb, p); }
+            { float w[8]; decode8(cw[1], w); Chain<1>::tail1(w, xa, xb, p); }
+            { float w[8]; decode8(cw[2], w); Chain<1>::tail2(w, xa, xb, p); }
+            { float w[8]; decode8(cw[3], w); Chain<1>::tail3(w, xa, xb, p); }
+            const float v = __builtin_fmaf(p[0], sc, acc);
+            acc = (leaf + 8 * i < G) ? v : acc;
+        }
+    }
+    red[wave][lane] = acc;
+    __syncthreads();
+    const int t = threadIdx.x;
+    const int n_grp = (k + 3) >> 2;
+    if (t < n_grp * kTile) {
+        const int g2 = t >> 6, l2 = t & 63;
+        const int p2 = 4 * g2 + (l2 >> 4);
+        if (p2 < k) {
+            const float v = tree8(&red[8 * g2][l2], kTile);
+            const int s2 = entry[passes[p2].y];
+            out[(size_t)s2 * H + (size_t)blockIdx.x * kNarrow + (l2 & 15)] = v;
+            sout[s2][l2 & 15] = v;
+        }
+    }
+    __syncthreads();
+    if (t < kNarrow) {
+        float sum = 0.0f;
+        for (int j = 0; j < k; ++j) sum = __builtin_fmaf(topk_w[j], sout[j][t], sum);
+        y[(size_t)blockIdx.x * kNarrow + t] = sum;
+    }
+}
+
 static int grid_for(int rows, int k, int n_tiles) {
     long items = (long)rows * k * n_tiles;  // passes <= rows*k
     return (int)(items < kMaxItemsGrid ? items : kMaxItemsGrid);
@@ -537,6 +623,17 @@ XP_API int xp_down_combine(const xp_dims* dims, int32_t rows, const float* act, 
     if (rows < 0) return XP_ERR_SHAPE;
     if (rows == 0) return XP_OK;
     if (!topk_w || !y) return XP_ERR_NULL;
+    if (rows == 1 && dims->top_k <= 8) {
+        // one row: down and combine in one launch (down_combine_one_row_kernel)
+        if (!act || !experts || !workspace || !out) return XP_ERR_NULL;
+        if (ws_bytes < ws_layout(dims, rows).total) return XP_ERR_WORKSPACE;
+        Plan pl = plan_view(workspace, dims, rows);
+        const int waves = 8 * ((dims->top_k + 3) / 4);
+        hipLaunchKernelGGL(down_combine_one_row_kernel, dim3(dims->hidden / kNarrow), dim3(64 * waves), 0,
+                           (hipStream_t)stream, experts, act, pl.entry, pl.dn_pass, topk_w, dims->hidden,
+                           dims->inter, dims->top_k, out, y);
+        return launch_status();
+    }
     st = xp_down_rows(dims, rows, act, experts, workspace, ws_bytes, out, stream);
     if (st != XP_OK) return st;
     return xp_combine(dims, rows, out, topk_w, y, stream);
