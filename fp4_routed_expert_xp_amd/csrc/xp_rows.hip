@@ -455,7 +455,12 @@ __global__ __launch_bounds__(1024) void down_combine_one_row_kernel(
     const int pass = min(4 * grp + (lane >> 4), k - 1);  // rows past the k-th pass repeat the last
     const int4 ps = passes[pass];
     const int slot = entry[ps.y];                        // one row: entry = slot
-    const int n = blockIdx.x * kNarrow + c;
+    // the four 16-column slices of a 64-column tile go to workgroups on one XCD
+    // (workgroup b runs on XCD b mod 8), so they share that L2's lines of the tile
+    const int b = blockIdx.x, n_tiles = gridDim.x >> 2;
+    const int tile = (n_tiles & 7) == 0 ? (b >> 5) * 8 + (b & 7) : b >> 2;
+    const int col0 = tile * kTile + ((n_tiles & 7) == 0 ? (b >> 3) & 3 : b & 3) * kNarrow;
+    const int n = col0 + c;
     const int G = I >> 5;
     const xp_expert ex = experts[ps.x];
     const size_t ch = (size_t)(n / kTile) * G * kTile + (n % kTile);
@@ -502,7 +507,7 @@ __global__ __launch_bounds__(1024) void down_combine_one_row_kernel(
         if (p2 < k) {
             const float v = tree8(&red[8 * g2][l2], kTile);
             const int s2 = entry[passes[p2].y];
-            out[(size_t)s2 * H + (size_t)blockIdx.x * kNarrow + (l2 & 15)] = v;
+            out[(size_t)s2 * H + col0 + (l2 & 15)] = v;
             sout[s2][l2 & 15] = v;
         }
     }
@@ -510,7 +515,7 @@ __global__ __launch_bounds__(1024) void down_combine_one_row_kernel(
     if (t < kNarrow) {
         float sum = 0.0f;
         for (int j = 0; j < k; ++j) sum = __builtin_fmaf(topk_w[j], sout[j][t], sum);
-        y[(size_t)blockIdx.x * kNarrow + t] = sum;
+        y[col0 + t] = sum;
     }
 }
 

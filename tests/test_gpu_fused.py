@@ -80,3 +80,18 @@ def test_fused_probe_tiny(tiny_layer):
             solo = run_fused(tiny_layer, x[r:r + 1], lg[r:r + 1])
             for n in ("act", "out", "y"):
                 assert np.array_equal(bits(batch[n][r]), bits(solo[n][0])), (R, r, n)
+
+
+@pytest.mark.parametrize("k", [1, 3, 4, 5, 8, 9])
+def test_fused_one_row_every_top_k(k):
+    """One row: xp_down_combine runs down and combine in one launch for top-k up
+    to 8 (passes 4 per row-group of lanes, the last group partly idle when k is
+    not a multiple of 4) and the two calls above 8; every case bit-equal to the
+    four calls. Width 256 x 192 (three 64-column tiles, six groups per leaf walk)."""
+    import dataclasses
+    cfg = dataclasses.replace(synth.CONFIGS["tiny"], name="tiny_k%d" % k, H=256, I=192, E=12, k=k,
+                              seed=1200 + k, weight_seed=1200)
+    layer = DeviceLayer(cfg, 0)
+    x = synth.activations(cfg.seed, 1, 1, cfg.H)
+    lg = synth.logits(cfg.seed, 1, 1, cfg.E)
+    _compare(layer, x, lg, "one row k=%d" % k)
