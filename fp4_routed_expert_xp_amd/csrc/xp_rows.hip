@@ -440,6 +440,9 @@ __global__ __launch_bounds__(512, 4) void down_kernel(const xp_expert* __restric
 // slots runs in the same workgroup, so no combine launch follows.
 // Workgroups: hidden / 16; waves: 8 * ceil(k / 4), so k <= 8.
 constexpr int kNarrow = 16;
+#ifndef XP_DC_DEPTH
+#define XP_DC_DEPTH 2  // groups in flight per wave (4 and 8 measured slower: 10.1 -> 11.4 / 13.4 us)
+#endif
 
 __global__ __launch_bounds__(1024) void down_combine_one_row_kernel(
     const xp_expert* __restrict__ experts, const float* __restrict__ act, const int32_t* __restrict__ entry,
@@ -447,7 +450,7 @@ __global__ __launch_bounds__(1024) void down_combine_one_row_kernel(
     float* __restrict__ out, float* __restrict__ y) {
     __shared__ float red[16][kTile];          // [wave][lane] leaf values
     __shared__ float sout[8][kNarrow];        // [slot][column] outputs
-    constexpr int D = DnDepth<1>::value;
+    constexpr int D = XP_DC_DEPTH;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int leaf = wave & 7, grp = wave >> 3;
