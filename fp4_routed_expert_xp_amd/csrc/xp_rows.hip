@@ -522,6 +522,138 @@ __global__ __launch_bounds__(1024) void down_combine_one_row_kernel(
     }
 }
 
+// ------------------------------------------ down + combine, few entries
+// The one-row layout for any plan with rows * top_k <= kFusedEntries: a
+// workgroup owns 16 columns of every down pass and walks the passes eight at
+// a time (waves 0-7 the leaves of four passes, one per row of 16 lanes; waves
+// 8-15 the next four). A wave runs the largest pass size among its four rows
+// of lanes; a shorter pass pads with its last real row, as every pass does.
+// Per (row, slot, column) the chain, leaf order and tree are dn_item's; each
+// (row, slot)'s 16 outputs wait in LDS until the combine, which runs the same
+// slot-order fma chain as combine_kernel once every pass is done.
+constexpr int kFusedEntries = 64;
+
+// Column slice of workgroup b: the four 16-column slices of a 64-column tile
+// go to workgroups on one XCD (workgroup b runs on XCD b mod 8).
+__device__ __forceinline__ int narrow_col0(int b, int n_slices) {
+    const int n_tiles = n_slices >> 2;
+    const int tile = (n_tiles & 7) == 0 ? (b >> 5) * 8 + (b & 7) : b >> 2;
+    return tile * kTile + ((n_tiles & 7) == 0 ? (b >> 3) & 3 : b & 3) * kNarrow;
+}
+
+template <int P>
+__device__ __forceinline__ void dc_pass_leaf(const xp_expert* __restrict__ experts, const float* __restrict__ act,
+                                             const int32_t* __restrict__ entry, int4 ps, int n, int I, int leaf,
+                                             int lane, float* red_wave /* [kMaxPass][kTile] */) {
+    constexpr int D = DnDepth<P>::value;
+    const int G = I >> 5;
+    const int c = lane & 15;
+    const xp_expert ex = experts[ps.x];
+    const size_t ch = (size_t)(n / kTile) * G * kTile + (n % kTile);
+    const gcodes_t cc = (gcodes_t)ex.down_codes + ch;
+    const gbytes_t ss = (gbytes_t)ex.down_scales + ch;
+    const float* ar[P];
+#pragma unroll
+    for (int r = 0; r < P; ++r) ar[r] = act + (size_t)entry[ps.y + min(r, ps.z - 1)] * I + 2 * c;
+
+    const int ng = (G + 7) >> 3;
+    float acc[P];
+#pragma unroll
+    for (int r = 0; r < P; ++r) acc[r] = 0.0f;
+    u32x4 bc[D];
+    uint32_t bs[D];
+    float2 bx[D][P];
+    auto load = [&](int s, int i) {
+        const int g = min(leaf + 8 * i, G - 1);
+        bc[s] = load_codes(cc + (size_t)g * kTile);
+        bs[s] = ss[(size_t)g * kTile];
+#pragma unroll
+        for (int r = 0; r < P; ++r) bx[s][r] = *(const float2*)(ar[r] + 32 * g);
+    };
+#pragma unroll
+    for (int s = 0; s < D; ++s) load(s, s);
+    for (int i0 = 0; i0 < ng; i0 += D) {
+#pragma unroll
+        for (int s = 0; s < D; ++s) {
+            const int i = i0 + s;
+            const float sc = e4m3(bs[s]);
+            const u32x4 cw = bc[s];
+            float p[P], xa[P], xb[P];
+#pragma unroll
+            for (int r = 0; r < P; ++r) { xa[r] = bx[s][r].x; xb[r] = bx[s][r].y; }
+            load(s, i + D);
+            { float w[8]; decode8(cw[0], w); Chain<P>::head_f32(w, xa, xb, p); }
+            { float w[8]; decode8(cw[1], w); Chain<P>::tail1(w, xa, xb, p); }
+            { float w[8]; decode8(cw[2], w); Chain<P>::tail2(w, xa, xb, p); }
+            { float w[8]; decode8(cw[3], w); Chain<P>::tail3(w, xa, xb, p); }
+            const bool valid = leaf + 8 * i < G;
+#pragma unroll
+            for (int r = 0; r < P; ++r) {
+                const float v = __builtin_fmaf(p[r], sc, acc[r]);
+                acc[r] = valid ? v : acc[r];
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < P; ++r) red_wave[r * kTile + lane] = acc[r];
+}
+
+__global__ __launch_bounds__(1024) void down_combine_rows_kernel(
+    const xp_expert* __restrict__ experts, const float* __restrict__ act, const int32_t* __restrict__ hdr,
+    const int32_t* __restrict__ entry, const int4* __restrict__ passes, const float* __restrict__ topk_w, int R,
+    int H, int I, int k, float* __restrict__ out, float* __restrict__ y) {
+    __shared__ float red[16][kMaxPass * kTile];        // [wave][row][lane] leaf values
+    __shared__ float sout[kFusedEntries][kNarrow];     // [row * k + slot][column] outputs
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int leaf = wave & 7, half = wave >> 3;
+    const int col0 = narrow_col0(blockIdx.x, gridDim.x);
+    const int n = col0 + (lane & 15);
+    const int t = threadIdx.x;
+    const int n_passes = hdr[1];
+    for (int pg = 0; pg < n_passes; pg += 8) {
+        const int pidx = min(pg + 4 * half + (lane >> 4), n_passes - 1);  // rows past the last pass repeat it
+        const int4 ps = passes[pidx];
+        // the wave's pass size: the largest of its four rows of lanes
+        int pw = max(__builtin_amdgcn_readlane(ps.w, 0), __builtin_amdgcn_readlane(ps.w, 16));
+        pw = max(pw, max(__builtin_amdgcn_readlane(ps.w, 32), __builtin_amdgcn_readlane(ps.w, 48)));
+        float* rw = &red[wave][0];
+        switch (pw) {
+            case 1: dc_pass_leaf<1>(experts, act, entry, ps, n, I, leaf, lane, rw); break;
+            case 2: dc_pass_leaf<2>(experts, act, entry, ps, n, I, leaf, lane, rw); break;
+            case 3: dc_pass_leaf<3>(experts, act, entry, ps, n, I, leaf, lane, rw); break;
+            case 4: dc_pass_leaf<4>(experts, act, entry, ps, n, I, leaf, lane, rw); break;
+            case 5: dc_pass_leaf<5>(experts, act, entry, ps, n, I, leaf, lane, rw); break;
+            case 6: dc_pass_leaf<6>(experts, act, entry, ps, n, I, leaf, lane, rw); break;
+            case 7: dc_pass_leaf<7>(experts, act, entry, ps, n, I, leaf, lane, rw); break;
+            case 8: dc_pass_leaf<8>(experts, act, entry, ps, n, I, leaf, lane, rw); break;
+            default: break;
+        }
+        __syncthreads();
+        // thread t: half t>>9, row of lanes (t>>7)&3, pass row (t>>4)&7, column t&15
+        {
+            const int h2 = t >> 9, q2 = (t >> 7) & 3, r2 = (t >> 4) & 7, c2 = t & 15;
+            const int p2 = pg + 4 * h2 + q2;
+            if (p2 < n_passes) {
+                const int4 ps2 = passes[p2];
+                if (r2 < ps2.z) {
+                    const float v = tree8(&red[8 * h2][r2 * kTile + 16 * q2 + c2], kMaxPass * kTile);
+                    const int e2 = entry[ps2.y + r2];
+                    out[(size_t)e2 * H + col0 + c2] = v;
+                    sout[e2][c2] = v;
+                }
+            }
+        }
+        __syncthreads();
+    }
+    if (t < R * kNarrow) {
+        const int r = t >> 4, c2 = t & 15;
+        float sum = 0.0f;
+        for (int j = 0; j < k; ++j) sum = __builtin_fmaf(topk_w[r * k + j], sout[r * k + j][c2], sum);
+        y[(size_t)r * H + col0 + c2] = sum;
+    }
+}
+
 static int grid_for(int rows, int k, int n_tiles) {
     long items = (long)rows * k * n_tiles;  // passes <= rows*k
     return (int)(items < kMaxItemsGrid ? items : kMaxItemsGrid);
@@ -640,6 +772,16 @@ XP_API int xp_down_combine(const xp_dims* dims, int32_t rows, const float* act, 
         hipLaunchKernelGGL(down_combine_one_row_kernel, dim3(dims->hidden / kNarrow), dim3(64 * waves), 0,
                            (hipStream_t)stream, experts, act, pl.entry, pl.dn_pass, topk_w, dims->hidden,
                            dims->inter, dims->top_k, out, y);
+        return launch_status();
+    }
+    if ((long)rows * dims->top_k <= kFusedEntries) {
+        // few (row, slot) entries: down and combine in one launch (down_combine_rows_kernel)
+        if (!act || !experts || !workspace || !out) return XP_ERR_NULL;
+        if (ws_bytes < ws_layout(dims, rows).total) return XP_ERR_WORKSPACE;
+        Plan pl = plan_view(workspace, dims, rows);
+        hipLaunchKernelGGL(down_combine_rows_kernel, dim3(dims->hidden / kNarrow), dim3(1024), 0,
+                           (hipStream_t)stream, experts, act, pl.hdr, pl.entry, pl.dn_pass, topk_w, rows,
+                           dims->hidden, dims->inter, dims->top_k, out, y);
         return launch_status();
     }
     st = xp_down_rows(dims, rows, act, experts, workspace, ws_bytes, out, stream);
