@@ -164,12 +164,12 @@ int xp_route_gateup(const xp_dims* dims, int32_t rows, const float* logits, cons
                     const xp_expert* experts, int32_t* topk_id, float* topk_w, void* workspace,
                     size_t ws_bytes, float* act, void* stream);
 
-/* xp_down_rows followed by xp_combine. With one row and top_k <= 8 this is
- * one launch: each workgroup computes 16 output columns of every slot's down
- * projection (the same per-(slot, column) chain, leaf order and tree as
- * xp_down_rows) and then their combine, and writes both out and y. Otherwise
- * the two calls run (two launches on the stream). The bits equal the two
- * calls' in every case. */
+/* xp_down_rows followed by xp_combine. When rows * top_k <= 64 this is one
+ * launch: each workgroup computes 16 output columns of every down pass (the
+ * same per-(row, slot, column) chain, leaf order and tree as xp_down_rows),
+ * keeps them until every pass is done, then runs the combine for those
+ * columns, and writes both out and y. Otherwise the two calls run (two
+ * launches on the stream). The bits equal the two calls' in every case. */
 int xp_down_combine(const xp_dims* dims, int32_t rows, const float* act, const xp_expert* experts,
                     const float* topk_w, void* workspace, size_t ws_bytes, float* out, float* y,
                     void* stream);
