@@ -430,8 +430,8 @@ __global__ __launch_bounds__(512, 4) void down_kernel(const xp_expert* __restric
 
 // ------------------------------------------------- one-row down + combine
 // With one row every down pass is a one-slot pass, and a set of columns needs
-// only the k passes' outputs for those columns to be combined. Workgroup b
-// owns the 16 columns 16b .. 16b+15 for every pass: wave w walks leaf w % 8
+// only the k passes' outputs for those columns to be combined. A workgroup
+// owns 16 columns (narrow_col0) for every pass: wave w walks leaf w % 8
 // for passes 4*(w/8) .. 4*(w/8)+3, one pass per row of 16 lanes, so the DPP
 // row broadcast hands each row its own pass's act values (lane m of a row
 // holds the act pair (2m, 2m+1) of its pass's group). Per (pass, column) the
@@ -443,6 +443,15 @@ constexpr int kNarrow = 16;
 #ifndef XP_DC_DEPTH
 #define XP_DC_DEPTH 2  // groups in flight per wave (4 and 8 measured slower: 10.1 -> 11.4 / 13.4 us)
 #endif
+
+// Column slice of workgroup b: the four 16-column slices of a 64-column tile
+// go to workgroups on one XCD (workgroup b runs on XCD b mod 8), so the tile's
+// lines are fetched into that XCD's L2 once; n_slices = hidden / 16.
+__device__ __forceinline__ int narrow_col0(int b, int n_slices) {
+    const int n_tiles = n_slices >> 2;
+    const int tile = (n_tiles & 7) == 0 ? (b >> 5) * 8 + (b & 7) : b >> 2;
+    return tile * kTile + ((n_tiles & 7) == 0 ? (b >> 3) & 3 : b & 3) * kNarrow;
+}
 
 __global__ __launch_bounds__(1024) void down_combine_one_row_kernel(
     const xp_expert* __restrict__ experts, const float* __restrict__ act, const int32_t* __restrict__ entry,
@@ -458,11 +467,7 @@ __global__ __launch_bounds__(1024) void down_combine_one_row_kernel(
     const int pass = min(4 * grp + (lane >> 4), k - 1);  // rows past the k-th pass repeat the last
     const int4 ps = passes[pass];
     const int slot = entry[ps.y];                        // one row: entry = slot
-    // the four 16-column slices of a 64-column tile go to workgroups on one XCD
-    // (workgroup b runs on XCD b mod 8), so they share that L2's lines of the tile
-    const int b = blockIdx.x, n_tiles = gridDim.x >> 2;
-    const int tile = (n_tiles & 7) == 0 ? (b >> 5) * 8 + (b & 7) : b >> 2;
-    const int col0 = tile * kTile + ((n_tiles & 7) == 0 ? (b >> 3) & 3 : b & 3) * kNarrow;
+    const int col0 = narrow_col0(blockIdx.x, gridDim.x);
     const int n = col0 + c;
     const int G = I >> 5;
     const xp_expert ex = experts[ps.x];
@@ -533,13 +538,6 @@ __global__ __launch_bounds__(1024) void down_combine_one_row_kernel(
 // slot-order fma chain as combine_kernel once every pass is done.
 constexpr int kFusedEntries = 64;
 
-// Column slice of workgroup b: the four 16-column slices of a 64-column tile
-// go to workgroups on one XCD (workgroup b runs on XCD b mod 8).
-__device__ __forceinline__ int narrow_col0(int b, int n_slices) {
-    const int n_tiles = n_slices >> 2;
-    const int tile = (n_tiles & 7) == 0 ? (b >> 5) * 8 + (b & 7) : b >> 2;
-    return tile * kTile + ((n_tiles & 7) == 0 ? (b >> 3) & 3 : b & 3) * kNarrow;
-}
 
 template <int P>
 __device__ __forceinline__ void dc_pass_leaf(const xp_expert* __restrict__ experts, const float* __restrict__ act,
