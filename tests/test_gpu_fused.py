@@ -95,3 +95,21 @@ def test_fused_one_row_every_top_k(k):
     x = synth.activations(cfg.seed, 1, 1, cfg.H)
     lg = synth.logits(cfg.seed, 1, 1, cfg.E)
     _compare(layer, x, lg, "one row k=%d" % k)
+
+
+@pytest.mark.parametrize("dn", [(2, 4, 8), (3, 5, 7), (8,)])
+def test_fused_few_entries_large_passes(tiny_layer, dn):
+    """At most 64 (row, slot) entries: xp_down_combine's one-launch kernel with
+    down passes of 5 to 8 rows (a wave running the largest size among its rows
+    of lanes, shorter passes padded), same-expert and mixed routing; bit-equal
+    to the four calls."""
+    cfg = tiny_layer.cfg
+    xp.xp_set_tiers([2, 4, 6, 8], list(dn))
+    try:
+        for R in (8, 13, 32):
+            x = synth.activations(cfg.seed + 11, R, R, cfg.H)
+            lg = synth.logits_same(cfg.seed + 11, R, R, cfg.E)
+            lg[R // 2:] = synth.logits(cfg.seed + 12, R, R - R // 2, cfg.E)
+            _compare(tiny_layer, x, lg, "dn %s R=%d" % (dn, R))
+    finally:
+        xp.xp_set_tiers(None, None)
