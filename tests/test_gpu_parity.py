@@ -260,3 +260,7 @@ def test_tiny_general_scales(R):
     ref = _oracle_layer(layer, x, lg)
     _check_values(res, ref, R)
     _check_chains(layer, x, res, range(R))
+    # the two-call path (down + combine in one launch at these sizes): same bits
+    fused = run_fused(layer, x, lg)
+    for name in ("act", "out", "y"):
+        assert np.array_equal(bits(fused[name]), bits(res[name])), name
