@@ -40,9 +40,11 @@ CSRC = os.path.join(ROOT, "fp4_routed_expert_xp_amd", "csrc")
 TRAFFIC = dict(sources="7a76f4fa", fetch_kib=34964.6, write_kib=66.4,
                fetch_factor=2097152 / 1048590.0, write_factor=1.0)
 ROOFLINE_SOURCES = ("xp_rows.hip", "xp_common.h", "xp_route_dev.h", "xp_chain_asm.h")
+# The same counters for the one-row down + combine launch (down_combine_one_row_kernel).
+DOWN_TRAFFIC = dict(sources="7a76f4fa", fetch_kib=17712.6, write_kib=144.0)
 # The same for the dense FP8 projection kernel at 4096 x 4096 (grid of 256
 # workgroups; mean over its launches at 1, 8 and 16 rows), tied to xp_fp8.hip.
-FP8_TRAFFIC = dict(sources="7a76f4fa", fetch_kib=8525.4, write_kib=133.3)
+FP8_TRAFFIC = dict(sources="fe07a71a", fetch_kib=8525.4, write_kib=133.3)
 FP8_SOURCES = ("xp_fp8.hip", "xp_common.h")
 
 
@@ -215,6 +217,39 @@ class Cell:
         return dict(distinct=distinct, gu_rows=gu_rows, dn_rows=dn_rows, gu_passes=gu_passes, dn_passes=dn_passes)
 
 
+def time_stream(cell: Cell) -> dict:
+    """The read-only ceiling of the cell's weight stream: xp_stream_weights over
+    each layer's distinct routed experts (read back from the plans in the
+    workspaces), a graph of one launch per layer, timed with events on the
+    launch stream; microseconds per layer and GB/s on the same unique bytes."""
+    import numpy as np
+    import torch
+    from fp4_routed_expert_xp_amd import xp
+    off = xp.xp_workspace_layout(cell.d, cell.cfg.R)
+    E = cell.cfg.E
+    ids, nbytes = [], 0
+    for ws in cell.ws:
+        cnt = ws[off[1]:off[1] + 4 * E].cpu().numpy().view(np.int32)
+        e = np.nonzero(cnt > 0)[0].astype(np.int32)
+        ids.append(torch.from_numpy(e).cuda())
+        nbytes += len(e) * cell.cfg.expert_bytes
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def rnd():
+        for l in range(cell.layers):
+            xp.xp_stream_weights(cell.d, cell.model.tables[l], ids[l], sink)
+    rnd()
+    torch.cuda.synchronize()
+    g = _graph(rnd)
+    g.replay()
+    torch.cuda.synchronize()
+    us = _replay_ms(g, 5) * 1e3 / cell.layers
+    del g
+    per_layer = nbytes / cell.layers
+    return dict(us_per_layer=round(us, 3), gbps=round(per_layer / (us * 1e-6) / 1e9, 1),
+                bytes_per_layer=int(per_layer))
+
+
 PATHS = {"four_calls": ("route", "gateup", "down", "combine"), "two_calls": ("route_gateup", "down_combine"),
          "bf16_storage": ("route", "gateup_act16", "down_act16", "combine_y16"),
          "prefill": ("route", "prefill_gateup", "prefill_down", "combine")}
@@ -280,7 +315,7 @@ def time_cell(cell: Cell, path: str, steps: int, warmup: int) -> dict:
                 kernel_us=per)
 
 
-def cell_report(cell: Cell, t: dict, copy_gbps: float) -> dict:
+def cell_report(cell: Cell, t: dict, copy_gbps: float, ceiling: dict | None = None) -> dict:
     cfg = cell.cfg
     st = cell.plan_stats()
     L = cell.layers
@@ -299,7 +334,11 @@ def cell_report(cell: Cell, t: dict, copy_gbps: float) -> dict:
     # act written (+ logits read, top-k and plan written when it routes)
     act_b = 2 if b16 else 4
     gu_bytes = distinct * gu_w + R * H * 2 + R * k * I * act_b + ((R * E * 4 + R * k * 8) if fused else 0)
-    dn_bytes = distinct * dn_w + R * k * I * act_b + R * k * H * 4 + ((R * k * H * 4 + R * H * 4) if fused else 0)
+    # down: its experts' weights, act read, out written; the fused call also writes y, and
+    # reads out back only when it runs as two launches (more than 64 (row, slot) entries)
+    dn_bytes = distinct * dn_w + R * k * I * act_b + R * k * H * 4
+    if fused:
+        dn_bytes += R * H * 4 + (R * k * H * 4 if R * k > 64 else 0)
     gu_us, dn_us = t["kernel_us"][gu_kind], t["kernel_us"][dn_kind]
     # VALU lane-ops: one fma per weight per computed row (padding included), one
     # decode per two weights per pass, one scaled fma per group per row
@@ -323,7 +362,9 @@ def cell_report(cell: Cell, t: dict, copy_gbps: float) -> dict:
         gateup_kernel=gu_kind, gateup_gbps=round(gu_bytes / (gu_us * 1e-6) / 1e9, 1), gateup_bytes=int(gu_bytes),
         down_kernel=dn_kind, down_gbps=round(dn_bytes / (dn_us * 1e-6) / 1e9, 1), down_bytes=int(dn_bytes),
         valu_bound_us=round(valu_us, 2), pass_bytes=int(round(pass_bytes)),
-    )
+    ) | ({} if ceiling is None else dict(
+        stream_ceiling_us=ceiling["us_per_layer"], stream_ceiling_gbps=ceiling["gbps"],
+        pct_stream_ceiling=round(100 * ceiling["us_per_layer"] / layer_us, 2)))
 
 
 def prefill_report(cell: Cell, t: dict) -> dict:
@@ -479,6 +520,18 @@ def cpu_baseline(budget_s: float) -> dict:
         oracle.layer(x, lg, ex, c2.H, c2.I, c2.E, c2.k)
         dt = time.perf_counter() - t0
         others[name] = dict(rows_per_s=round(c2.R / (dt * 40), 4), s_per_layer=round(dt, 3))
+    # one layer of the one-row round on a single thread, for the per-core figure
+    omp_default = oracle.omp_threads()
+    x, lg = synth.layer_inputs(cfg, 0, plant=False)
+    ids, _ = oracle.route(lg, cfg.k)
+    ex = {int(e): synth.layer_expert(cfg, 0, int(e)) for e in np.unique(ids)}
+    oracle.set_threads(1)
+    try:
+        t0 = time.perf_counter()
+        oracle.layer(x, lg, ex, cfg.H, cfg.I, cfg.E, cfg.k)
+        single = time.perf_counter() - t0
+    finally:
+        oracle.set_threads(omp_default)
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -489,7 +542,30 @@ def cpu_baseline(budget_s: float) -> dict:
                 sample="%d of the 40 layers of the one-row round (1 row x 8 experts each), float64 C oracle, "
                        "OpenMP over (row, slot) pairs; %.3f s per layer, scaled to a 40-layer round" %
                        (len(times), per_layer),
-                host={"cpu": model, "logical_cpus": os.cpu_count()}, other_workloads=others)
+                host={"cpu": model, "logical_cpus": os.cpu_count()}, other_workloads=others,
+                single_thread=dict(value=round(cfg.R / (single * 40), 4), unit="rows/s", cores=1,
+                                   s_per_layer=round(single, 3),
+                                   sample="layer 0 of the one-row round on one thread, scaled to 40 layers"))
+
+
+DECODE_CELLS = ("one_row", "four_same", "sixteen_random")
+
+
+def decode_pct(reports: dict) -> dict:
+    """% of the HBM peak on expert-weight bytes of the two-call path per decode
+    workload (1, 4 and 16 rows), their minimum, and the same against the
+    read-only stream ceiling."""
+    out = {}
+    for name in DECODE_CELLS:
+        r = reports.get("%s/two_calls" % name)
+        if r is not None:
+            out["%d_rows" % r["rows"]] = r["pct_hbm_peak"]
+            if "pct_stream_ceiling" in r:
+                out["%d_rows_vs_stream_ceiling" % r["rows"]] = r["pct_stream_ceiling"]
+    peaks = [v for kk, v in out.items() if kk.endswith("_rows")]
+    if peaks:
+        out["min"] = min(peaks)
+    return out
 
 
 def main():
@@ -534,11 +610,15 @@ def main():
             del cell
             continue
         cell = Cell(model, cfg, args.layers)
+        ceiling = None
         for path in ("two_calls", "four_calls", "bf16_storage"):
             t = time_cell(cell, path, args.steps, args.warmup)
+            if ceiling is None:     # the plans are in place after the first path's rounds
+                ceiling = time_stream(cell)
+                log("%s: read-only stream ceiling %s" % (name, json.dumps(ceiling)))
             key = "%s/%s" % (name, path)
             timings[key] = t
-            reports[key] = cell_report(cell, t, copy_gbps)
+            reports[key] = cell_report(cell, t, copy_gbps, ceiling)
             log("%s: %s" % (key, json.dumps(reports[key])))
         if name in SWEEP_CELLS and not args.no_tier_sweep:
             # same rows, other pass sizes: the bits are unchanged (the probe
@@ -551,7 +631,7 @@ def main():
                 finally:
                     xp.xp_set_tiers(*in_force)
                 key = "%s/two_calls/tiers_gu%s_dn%s" % (name, "-".join(map(str, gu)), "-".join(map(str, dn)))
-                rep = cell_report(cell, t, copy_gbps)
+                rep = cell_report(cell, t, copy_gbps, ceiling)
                 rep["tiers"] = {"gate_up": list(gu), "down": list(dn)}
                 reports[key] = rep
                 log("%s: %s" % (key, json.dumps(rep)))
@@ -590,9 +670,18 @@ def main():
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic()},
         "copy_gbps": round(copy_gbps, 1),
+        "decode_pct_hbm_peak": decode_pct(reports),
         "wall_s_timed": round(th["wall_s"], 4),
         "cells": reports,
     }
+    dn_kernel = "down_combine_one_row_kernel (xp_down_combine)" if head["rows"] == 1 else (
+        "down_combine_rows_kernel (xp_down_combine)" if head["rows"] * base.k <= 64
+        else "down_kernel<false> + combine_kernel<false> (xp_down_combine)")
+    line["roofline_down"] = {
+        "kernel": dn_kernel, "bound": "hbm", "achieved": head["down_gbps"], "bytes_per_launch": head["down_bytes"],
+        "launch_us": head["kernel_us"]["down_combine"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+        "frac": round(head["down_gbps"] / HBM_PEAK_GBPS, 4),
+        "traffic": measured_traffic(DOWN_TRAFFIC) if head["rows"] == 1 else None}
     if "prefill/prefill" in reports:
         pf = reports["prefill/prefill"]
         cfg = synth.CONFIGS["prefill"]

@@ -23,7 +23,7 @@ EXPORTS = (
     "xp_gateup_rows", "xp_gateup_rows_split", "xp_down_rows", "xp_combine",
     "xp_set_tiers", "xp_get_tiers", "xp_status_string", "xp_route_gateup", "xp_down_combine",
     "xp_prefill_gateup", "xp_prefill_down", "xp_fp8_packed_bytes", "xp_fp8_pack", "xp_fp8_rows",
-    "xp_gateup_rows_act16", "xp_down_rows_act16", "xp_combine_y16", "xp_fp8_rows_f32",
+    "xp_gateup_rows_act16", "xp_down_rows_act16", "xp_combine_y16", "xp_fp8_rows_f32", "xp_stream_weights",
 )
 
 
@@ -80,6 +80,7 @@ def lib():
         L.xp_fp8_pack.argtypes = [i32, i32, P, P, P]
         L.xp_fp8_rows.argtypes = [i32, i32, i32, P, P, P, P, i32, P]
         L.xp_fp8_rows_f32.argtypes = [i32, i32, i32, P, P, P, P, i32, P]
+        L.xp_stream_weights.argtypes = [D, P, P, i32, P, P]
         L.xp_set_tiers.argtypes = [P, i32, P, i32]
         L.xp_get_tiers.argtypes = [P, P, P, P]
         L.xp_status_string.argtypes = [ctypes.c_int]
@@ -88,7 +89,7 @@ def lib():
                      "xp_gateup_rows_split", "xp_down_rows", "xp_combine", "xp_set_tiers", "xp_get_tiers",
                      "xp_route_gateup", "xp_down_combine", "xp_prefill_gateup", "xp_prefill_down",
                      "xp_fp8_pack", "xp_fp8_rows", "xp_gateup_rows_act16", "xp_down_rows_act16",
-                     "xp_combine_y16", "xp_fp8_rows_f32"):
+                     "xp_combine_y16", "xp_fp8_rows_f32", "xp_stream_weights"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
         try:
@@ -375,6 +376,17 @@ def xp_fp8_rows_f32(rows: int, n: int, k: int, x, packed, scales, y, slices: int
         _dev(y, torch.float32, "y", rows * n)
     _check(lib().xp_fp8_rows_f32(int(rows), int(n), int(k), _ptr(x), _ptr(packed), _ptr(scales), _ptr(y),
                                  int(slices), _stream(stream)), "xp_fp8_rows_f32")
+
+
+def xp_stream_weights(d: xp_dims, experts, ids, sink, stream=None) -> None:
+    """Bandwidth probe: read the packed weights of the experts in ``ids`` once (see xp.h)."""
+    n = 0 if ids is None else ids.numel()
+    if n > 0:
+        _dev(experts, torch.int64, "experts", d.n_experts * 6)
+        _dev(ids, torch.int32, "ids")
+        _dev(sink, torch.int32 if sink.dtype == torch.int32 else torch.uint32, "sink", 1)
+    _check(lib().xp_stream_weights(ctypes.byref(d), _ptr(experts), _ptr(ids), int(n), _ptr(sink),
+                                   _stream(stream)), "xp_stream_weights")
 
 
 # -------------------------------------------------------------- conveniences

@@ -78,6 +78,8 @@ def lib():
         L.or_combine32.restype = None
         L.or_omp_threads.argtypes = []
         L.or_omp_threads.restype = i32
+        L.or_set_threads.argtypes = [i32]
+        L.or_set_threads.restype = None
         _lib = L
     return _lib
 
@@ -263,6 +265,11 @@ def combine32(w_f32, out_f32) -> np.ndarray:
 
 def omp_threads() -> int:
     return lib().or_omp_threads()
+
+
+def set_threads(n: int) -> None:
+    """Threads the oracle's parallel loops use from now on (timing only)."""
+    lib().or_set_threads(int(n))
 
 
 def fp8_proj(x_bits: np.ndarray, w: np.ndarray, s: np.ndarray) -> np.ndarray:

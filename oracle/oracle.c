@@ -247,6 +247,16 @@ int or_omp_threads(void) {
 #endif
 }
 
+/* Threads later parallel regions use (n >= 1); timing only, the results do
+ * not depend on it (each (row, slot) pair is computed whole by one thread). */
+void or_set_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 int or_layer(int H, int I, int E, int k, int R, const uint16_t* x_bf16, const float* logits,
              const uint8_t* const* gate_codes, const uint8_t* const* gate_scales,
              const uint8_t* const* up_codes, const uint8_t* const* up_scales,

@@ -76,6 +76,7 @@ void or_fp8_proj(int R, int N, int K, const uint16_t* x, const uint8_t* w, const
 void or_fp8_proj_f32(int R, int N, int K, const float* x, const uint8_t* w, const float* s, double* y);
 
 int or_omp_threads(void);
+void or_set_threads(int n);
 
 #ifdef __cplusplus
 }

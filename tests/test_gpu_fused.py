@@ -2,7 +2,11 @@
 
 Both paths run the same per-row arithmetic, so every output must be bit-equal,
 the published plan must be the same, and repeated down+combine launches on one
-plan must keep giving the same y (the combine counts are left cleared)."""
+plan must keep giving the same y. xp_down_combine runs one of three forms: one
+row with top-k up to 8 in down_combine_one_row_kernel, at most 64 (row, slot)
+entries in down_combine_rows_kernel, and more entries as the two launches
+(down, then combine); each form is covered below, and the two-call path is
+also probed row by row against its own solo launches at release width."""
 import numpy as np
 import pytest
 
@@ -84,10 +88,11 @@ def test_fused_probe_tiny(tiny_layer):
 
 @pytest.mark.parametrize("k", [1, 3, 4, 5, 8, 9])
 def test_fused_one_row_every_top_k(k):
-    """One row: xp_down_combine runs down and combine in one launch for top-k up
-    to 8 (passes 4 per row-group of lanes, the last group partly idle when k is
-    not a multiple of 4) and the two calls above 8; every case bit-equal to the
-    four calls. Width 256 x 192 (three 64-column tiles, six groups per leaf walk)."""
+    """One row: xp_down_combine runs down and combine in down_combine_one_row_kernel
+    for top-k up to 8 (passes 4 per row-group of lanes, the last group partly idle
+    when k is not a multiple of 4) and in down_combine_rows_kernel above 8 (one
+    row's k entries are at most 64); every case bit-equal to the four calls.
+    Width 256 x 192 (three 64-column tiles, six groups per leaf walk)."""
     import dataclasses
     cfg = dataclasses.replace(synth.CONFIGS["tiny"], name="tiny_k%d" % k, H=256, I=192, E=12, k=k,
                               seed=1200 + k, weight_seed=1200)
@@ -111,5 +116,56 @@ def test_fused_few_entries_large_passes(tiny_layer, dn):
             lg = synth.logits_same(cfg.seed + 11, R, R, cfg.E)
             lg[R // 2:] = synth.logits(cfg.seed + 12, R, R - R // 2, cfg.E)
             _compare(tiny_layer, x, lg, "dn %s R=%d" % (dn, R))
+    finally:
+        xp.xp_set_tiers(None, None)
+
+
+PROBE_FUSED_ROWS = [2, 3, 5, 7, 8]
+
+
+@pytest.mark.parametrize("routing", ["same", "disjoint", "random"])
+def test_fused_probe_release(release_layer, routing):
+    """The headline two-call path at release width, at the row counts whose down
+    passes take every form of down_combine_rows_kernel (2 to 8 rows, 16 to 64
+    entries): each row of the batch bit-equal to the same row launched alone on
+    the two-call path, and the batch bit-equal to the four calls."""
+    cfg = release_layer.cfg
+    for R in PROBE_FUSED_ROWS:
+        x = synth.activations(cfg.seed + 31, R, R, cfg.H)
+        if routing == "same":
+            lg = synth.logits_same(cfg.seed + 31, R, R, cfg.E)
+        elif routing == "disjoint":
+            lg = synth.logits_disjoint(R, cfg.E, cfg.k)
+        else:
+            lg = synth.logits(cfg.seed + 31, R, R, cfg.E)
+        x, _, _ = synth.plant_nan_inf(cfg.seed + 31, R, x)
+        log("fused probe release R=%d %s" % (R, routing))
+        batch = run_fused(release_layer, x, lg)
+        four = run_path(release_layer, x, lg)
+        for n in ("act", "out", "y"):
+            assert np.array_equal(bits(batch[n]), bits(four[n])), (R, routing, n)
+        for r in range(R):
+            solo = run_fused(release_layer, x[r:r + 1], lg[r:r + 1])
+            for n in ("act", "out", "y"):
+                assert np.array_equal(bits(batch[n][r]), bits(solo[n][0])), (R, routing, r, n)
+
+
+@pytest.mark.parametrize("dn", [(3, 5, 7), (8,)])
+def test_fused_large_passes_long_leaf_walk(dn):
+    """down_combine_rows_kernel with passes of 3 to 8 rows on a layer whose down
+    K (intermediate 1024: 32 groups, four per leaf) is longer than every pass
+    size's weight ring, so each ring refills inside the leaf walk; bit-equal to
+    the four calls under same-expert and mixed routing."""
+    import dataclasses
+    cfg = dataclasses.replace(synth.CONFIGS["tiny"], name="tiny_i1024", H=256, I=1024, E=8, k=2,
+                              seed=1300, weight_seed=1300)
+    layer = DeviceLayer(cfg, 0)
+    xp.xp_set_tiers([2, 4, 6, 8], list(dn))
+    try:
+        for R in (3, 8, 13, 32):
+            x = synth.activations(cfg.seed, R, R, cfg.H)
+            lg = synth.logits_same(cfg.seed, R, R, cfg.E)
+            lg[R // 2:] = synth.logits(cfg.seed + 1, R, R - R // 2, cfg.E)
+            _compare(layer, x, lg, "I=1024 dn %s R=%d" % (dn, R))
     finally:
         xp.xp_set_tiers(None, None)

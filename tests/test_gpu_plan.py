@@ -7,7 +7,7 @@ import oracle
 import synth
 from fp4_routed_expert_xp_amd import xp
 
-from gpu_helpers import log, read_plan, to_dev
+from gpu_helpers import DeviceLayer, log, read_plan, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -88,3 +88,14 @@ def test_plan_other_tier_sets(tiers):
     lg[8:] = synth.logits(6, 0, 8, 64)
     ids, w, plan, (oid, ow, count, offset, entry, gu, dn) = _route_case(16, 64, 8, lg, tiers)
     assert np.array_equal(plan["gu"], gu) and np.array_equal(plan["dn"], dn)
+
+
+def test_stream_probe_reads_and_writes_nothing():
+    """The bandwidth probe over every expert of the tiny layer runs and leaves its
+    sink untouched unless a folded word hit the fixed constant."""
+    layer = DeviceLayer(synth.CONFIGS["tiny"], 0)
+    ids = torch.arange(layer.cfg.E, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    xp.xp_stream_weights(layer.d, layer.table, ids, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) in (0, 0x9E3779B9 - (1 << 32))

@@ -135,12 +135,52 @@ def prefill_layer():
     return DeviceLayer(PREFILL, 0)
 
 
+def slab_class(rows_in_block: int) -> int:
+    """16-row slabs a 128-row block of an expert computes: its rows rounded up to 2, 4, 6 or 8."""
+    s = (rows_in_block + 15) // 16
+    return 2 if s <= 2 else 4 if s <= 4 else 6 if s <= 6 else 8
+
+
+def shape_chosen_rows(count, offset, entry, k, R, seed=5):
+    """Rows of a chunk picked by the work items they fall in: for every slab class
+    2/4/6/8, the first and last row of the last (ragged) block of two experts of
+    that class; the last row of the busiest expert's ragged block and the first
+    row of one of its full blocks; every row of the least-loaded routed expert
+    (up to four); the first and last chunk rows; and random rows up to 40."""
+    rows = set([0, R - 1])
+    E = len(count)
+    routed = [e for e in range(E) if count[e] > 0]
+    members = lambda e: [int(entry[i]) // k for i in range(offset[e], offset[e + 1])]
+    by_class = {2: [], 4: [], 6: [], 8: []}
+    for e in routed:
+        last = count[e] - 128 * ((count[e] - 1) // 128)
+        by_class[slab_class(last)].append(e)
+    for cls, es in by_class.items():
+        for e in es[:2]:
+            m = members(e)
+            b0 = 128 * ((len(m) - 1) // 128)
+            rows.update([m[b0], m[-1]])
+    busiest = int(np.argmax(count))
+    m = members(busiest)
+    rows.add(m[-1])
+    if len(m) > 128:
+        rows.add(m[128 * ((len(m) - 1) // 128) - 128])   # first row of its last full block
+    least = min(routed, key=lambda e: count[e])
+    rows.update(members(least)[:4])
+    rng = np.random.default_rng(seed)
+    while len(rows) < 40:
+        rows.add(int(rng.integers(0, R)))
+    return sorted(rows), by_class, busiest, least
+
+
 def test_prefill_chunk_release_width(prefill_layer):
     """4,096 rows, 256 experts, top-8, logits with a per-expert bias (sigma 0.5).
 
     Routing, counts, offsets and entries are bit-exact for every row; act, out
-    and y are compared with the float64 oracle on sampled rows, among them the
-    rows in the last (ragged) block of the most loaded expert.
+    and y are compared with the float64 oracle on 40 rows chosen by the work
+    item they fall in (every slab class of an expert's ragged last block, the
+    busiest expert's full and ragged blocks, the least-loaded expert) plus
+    random rows; the whole chunk is checked to be finite.
     """
     cfg = PREFILL
     x, lg = synth.layer_inputs(cfg, 0)
@@ -155,14 +195,15 @@ def test_prefill_chunk_release_width(prefill_layer):
     assert np.array_equal(plan["entry"], entry)
     for name in ("act", "out", "y"):
         assert np.all(np.isfinite(res[name])), name
-    busiest = int(np.argmax(count))
-    log("  busiest expert %d with %d rows; %d experts routed" % (busiest, count[busiest], int((count > 0).sum())))
-    tail = entry[offset[busiest + 1] - 1] // cfg.k
-    rng = np.random.default_rng(5)
-    rows = sorted(set([0, cfg.R - 1, int(tail)] + [int(r) for r in rng.integers(0, cfg.R, 3)]))
+    rows, by_class, busiest, least = shape_chosen_rows(count, offset, entry, cfg.k, cfg.R)
+    log("  busiest expert %d with %d rows, least-loaded %d with %d; %d experts routed; experts per slab class %s"
+        % (busiest, count[busiest], least, count[least], int((count > 0).sum()),
+           {c: len(v) for c, v in by_class.items()}))
+    assert all(len(v) > 0 for v in by_class.values()), "the chunk exercises every slab class"
+    assert len(rows) >= 32
     ref = oracle_rows(prefill_layer, x[rows], lg[rows])
     worst = check_rows(res, ref, rows)
-    log("  sampled rows %s: worst per-row relative error %.2e" % (rows, worst))
+    log("  %d chosen rows: worst per-row relative error %.2e" % (len(rows), worst))
 
 
 def test_prefill_largest_experts_and_topk():
