@@ -24,6 +24,7 @@ EXPORTS = (
     "xp_set_tiers", "xp_get_tiers", "xp_status_string", "xp_route_gateup", "xp_down_combine",
     "xp_prefill_gateup", "xp_prefill_down", "xp_fp8_packed_bytes", "xp_fp8_pack", "xp_fp8_rows",
     "xp_gateup_rows_act16", "xp_down_rows_act16", "xp_combine_y16", "xp_fp8_rows_f32", "xp_stream_weights",
+    "xp_decode_static",
 )
 
 
@@ -81,6 +82,7 @@ def lib():
         L.xp_fp8_rows.argtypes = [i32, i32, i32, P, P, P, P, i32, P]
         L.xp_fp8_rows_f32.argtypes = [i32, i32, i32, P, P, P, P, i32, P]
         L.xp_stream_weights.argtypes = [D, P, P, i32, P, P]
+        L.xp_decode_static.argtypes = [D, i32, P, P, P, P, P, P, P, P, P]
         L.xp_set_tiers.argtypes = [P, i32, P, i32]
         L.xp_get_tiers.argtypes = [P, P, P, P]
         L.xp_status_string.argtypes = [ctypes.c_int]
@@ -89,7 +91,7 @@ def lib():
                      "xp_gateup_rows_split", "xp_down_rows", "xp_combine", "xp_set_tiers", "xp_get_tiers",
                      "xp_route_gateup", "xp_down_combine", "xp_prefill_gateup", "xp_prefill_down",
                      "xp_fp8_pack", "xp_fp8_rows", "xp_gateup_rows_act16", "xp_down_rows_act16",
-                     "xp_combine_y16", "xp_fp8_rows_f32", "xp_stream_weights"):
+                     "xp_combine_y16", "xp_fp8_rows_f32", "xp_stream_weights", "xp_decode_static"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
         try:
@@ -286,6 +288,23 @@ def xp_down_combine(d: xp_dims, rows: int, act, experts, topk_w, workspace, out,
     nbytes = workspace.numel() if workspace is not None else 0
     _check(lib().xp_down_combine(ctypes.byref(d), int(rows), _ptr(act), _ptr(experts), _ptr(topk_w),
                                  _ptr(workspace), nbytes, _ptr(out), _ptr(y), _stream(stream)), "xp_down_combine")
+
+
+def xp_decode_static(d: xp_dims, rows: int, logits, x, experts, topk_id, topk_w, act, out, y,
+                     stream=None) -> None:
+    """xp_route_gateup + xp_down_combine with the plan in the library's own device array (no workspace)."""
+    if rows > 0:
+        _dev(logits, torch.float32, "logits", rows * d.n_experts)
+        _dev_bf16(x, "x", rows * d.hidden)
+        _dev(experts, torch.int64, "experts", d.n_experts * 6)
+        _dev(topk_id, torch.int32, "topk_id", rows * d.top_k)
+        _dev(topk_w, torch.float32, "topk_w", rows * d.top_k)
+        _dev(act, torch.float32, "act", rows * d.top_k * d.inter)
+        _dev(out, torch.float32, "out", rows * d.top_k * d.hidden)
+        _dev(y, torch.float32, "y", rows * d.hidden)
+    _check(lib().xp_decode_static(ctypes.byref(d), int(rows), _ptr(logits), _ptr(x), _ptr(experts),
+                                  _ptr(topk_id), _ptr(topk_w), _ptr(act), _ptr(out), _ptr(y), _stream(stream)),
+           "xp_decode_static")
 
 
 def xp_prefill_gateup(d: xp_dims, rows: int, x, experts, workspace, act, stream=None) -> None:

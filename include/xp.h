@@ -174,6 +174,24 @@ int xp_down_combine(const xp_dims* dims, int32_t rows, const float* act, const x
                     const float* topk_w, void* workspace, size_t ws_bytes, float* out, float* y,
                     void* stream);
 
+/* For callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid allocation): xp_route_gateup
+ * followed by xp_down_combine, the same kernels and the same bits, with no
+ * workspace argument. The plan lives in a fixed 1 MiB device array inside the
+ * library (each GPU holds its own copy until the process ends); the call makes
+ * no allocation. A plan larger than 1 MiB (xp_workspace_bytes(dims, rows) >
+ * 1,048,576; for hidden 4096, inter 2048, 256 experts, top-8 that is more than
+ * 3,000 rows) is refused with XP_ERR_WORKSPACE before anything is enqueued.
+ * Every call on one GPU shares that array: calls that overlap on one GPU
+ * (other streams, other threads) race and must be serialised by the caller;
+ * calls in order on one stream are safe. The first call on each device looks
+ * up the array's address there (make it outside graph capture); XP_ERR_HIP if
+ * the runtime refuses. Outputs as the two calls: topk_id/topk_w [rows][k],
+ * act [rows][k][I], out [rows][k][H], y [rows][H]. */
+int xp_decode_static(const xp_dims* dims, int32_t rows, const float* logits, const uint16_t* x,
+                     const xp_expert* experts, int32_t* topk_id, float* topk_w, float* act, float* out,
+                     float* y, void* stream);
+
 /* ---------------------------------------------------------- prefill chunk
  * The same layer for a prompt chunk (thousands of rows, about a hundred per
  * expert): gate/up and down as grouped bf16 matrix-core contractions over the
