@@ -39,7 +39,7 @@ CSRC = os.path.join(ROOT, "fp4_routed_expert_xp_amd", "csrc")
 # after any change to them the bench reports traffic as null.
 TRAFFIC = dict(sources="7a76f4fa", fetch_kib=34964.6, write_kib=66.4,
                fetch_factor=2097152 / 1048590.0, write_factor=1.0)
-ROOFLINE_SOURCES = ("xp_rows.hip", "xp_common.h", "xp_route_dev.h", "xp_chain_asm.h")
+ROOFLINE_SOURCES = ("xp_rows.hip", "xp_pass_dev.h", "xp_common.h", "xp_route_dev.h", "xp_chain_asm.h")
 # The same counters for the one-row down + combine launch (down_combine_one_row_kernel).
 DOWN_TRAFFIC = dict(sources="7a76f4fa", fetch_kib=17712.6, write_kib=144.0)
 # The same for the dense FP8 projection kernel at 4096 x 4096 (grid of 256
@@ -235,19 +235,26 @@ def time_stream(cell: Cell) -> dict:
         nbytes += len(e) * cell.cfg.expert_bytes
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
 
-    def rnd():
-        for l in range(cell.layers):
-            xp.xp_stream_weights(cell.d, cell.model.tables[l], ids[l], sink)
-    rnd()
-    torch.cuda.synchronize()
-    g = _graph(rnd)
-    g.replay()
-    torch.cuda.synchronize()
-    us = _replay_ms(g, 5) * 1e3 / cell.layers
-    del g
+    def timed(parts):
+        def rnd():
+            for l in range(cell.layers):
+                xp.xp_stream_weights(cell.d, cell.model.tables[l], ids[l], sink, parts)
+        rnd()
+        torch.cuda.synchronize()
+        g = _graph(rnd)
+        g.replay()
+        torch.cuda.synchronize()
+        us = _replay_ms(g, 5) * 1e3 / cell.layers
+        del g
+        return us
+
+    us = timed(7)
     per_layer = nbytes / cell.layers
+    # the same bytes split as the two launches stream them: gate + up, then down
+    gu_us, dn_us = timed(3), timed(4)
     return dict(us_per_layer=round(us, 3), gbps=round(per_layer / (us * 1e-6) / 1e9, 1),
-                bytes_per_layer=int(per_layer))
+                bytes_per_layer=int(per_layer), gateup_us=round(gu_us, 3), down_us=round(dn_us, 3),
+                two_launch_us=round(gu_us + dn_us, 3))
 
 
 PATHS = {"four_calls": ("route", "gateup", "down", "combine"), "two_calls": ("route_gateup", "down_combine"),
@@ -364,7 +371,9 @@ def cell_report(cell: Cell, t: dict, copy_gbps: float, ceiling: dict | None = No
         valu_bound_us=round(valu_us, 2), pass_bytes=int(round(pass_bytes)),
     ) | ({} if ceiling is None else dict(
         stream_ceiling_us=ceiling["us_per_layer"], stream_ceiling_gbps=ceiling["gbps"],
-        pct_stream_ceiling=round(100 * ceiling["us_per_layer"] / layer_us, 2)))
+        pct_stream_ceiling=round(100 * ceiling["us_per_layer"] / layer_us, 2),
+        stream_ceiling_two_launch_us=ceiling["two_launch_us"],
+        pct_two_launch_ceiling=round(100 * ceiling["two_launch_us"] / layer_us, 2)))
 
 
 def prefill_report(cell: Cell, t: dict) -> dict:

@@ -188,4 +188,47 @@ __device__ void plan_block(int E, const int32_t* cnt, const Tiers& T, int32_t* s
     }
 }
 
+// Routing inputs of the one-row route + gate/up launch.
+struct RouteIn {
+    const float* logits;
+    int E;
+    int32_t* topk_id;
+    float* topk_w;
+    WsPtrs w;
+};
+
+// Publish what xp_route_bucket writes for a batch of one row, from the wave
+// that ran topk_picks for all k rounds (lane j holds pick j's order key mo and
+// id mi): top-k ids and weights, counts, offsets, entries and both pass lists
+// (one one-row pass per chosen expert, experts ascending). Every lane of the
+// wave must call this.
+__device__ __forceinline__ void publish_one_row(const RouteIn& ri, int k, uint32_t mo, uint32_t mi) {
+    const int lane = threadIdx.x & 63;
+    const float w = topk_weight(mo, k);
+    int rank = 0;  // position of this lane's pick among the picks by expert id
+    for (int i = 0; i < k; ++i) rank += ((uint32_t)__builtin_amdgcn_readlane((int)mi, i) < mi) ? 1 : 0;
+    if (lane < k) {
+        ri.topk_id[lane] = (int32_t)mi;
+        ri.topk_w[lane] = w;
+        ri.w.gu_pass[rank] = make_int4((int)mi, rank, 1, 1);
+        ri.w.dn_pass[rank] = make_int4((int)mi, rank, 1, 1);
+        ri.w.entry[rank] = lane;  // row 0, slot lane
+    }
+    for (int e0 = 0; e0 <= ri.E; e0 += 64) {
+        const int e = e0 + lane;
+        int below = 0, hit = 0;
+        for (int i = 0; i < k; ++i) {
+            const int o = __builtin_amdgcn_readlane((int)mi, i);
+            below += o < e ? 1 : 0;
+            hit |= o == e ? 1 : 0;
+        }
+        if (e <= ri.E) ri.w.offset[e] = below;
+        if (e < ri.E) ri.w.count[e] = hit;
+    }
+    if (lane == 0) {
+        ri.w.hdr[0] = k;
+        ri.w.hdr[1] = k;
+    }
+}
+
 }  // namespace xp

@@ -20,197 +20,12 @@
 // The code for a pass of P rows is the one-row code repeated per row with no
 // value crossing between rows, so a row's bits do not depend on P. Padding rows
 // (P > real rows) re-read the last real row and are not stored.
-#include "xp_chain_asm.h"
-#include "xp_common.h"
+#include "xp_pass_dev.h"
 #include "xp_route_dev.h"
 
 #include <algorithm>
 
 namespace xp {
-
-// Two fp4 codes of byte `B` of `v` -> exact fp32 (low nibble first).
-template <int B>
-__device__ __forceinline__ f32x2 fp4x2(uint32_t v) {
-    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, B);
-}
-
-__device__ __forceinline__ float e4m3(uint32_t byte) { return __builtin_amdgcn_cvt_f32_fp8((int)byte, 0); }
-
-// One dword of codes (k ascending from the low nibble) -> its eight weights,
-// exact fp32. A group is decoded one dword at a time, just before the quarter
-// of the chain that uses it, so only eight decoded weights are live at once.
-__device__ __forceinline__ void decode8(uint32_t c, float (&w)[8]) {
-    f32x2 a;
-    a = fp4x2<0>(c); w[0] = a.x; w[1] = a.y;
-    a = fp4x2<1>(c); w[2] = a.x; w[3] = a.y;
-    a = fp4x2<2>(c); w[4] = a.x; w[5] = a.y;
-    a = fp4x2<3>(c); w[6] = a.x; w[7] = a.y;
-}
-
-// Leaves l0..l7 at a[0], a[stride], ..., a[7*stride].
-__device__ __forceinline__ float tree8(const float* a, int stride) {
-    float s01 = a[0] + a[stride];
-    float s23 = a[2 * stride] + a[3 * stride];
-    float s45 = a[4 * stride] + a[5 * stride];
-    float s67 = a[6 * stride] + a[7 * stride];
-    float lo = s01 + s23;
-    float hi = s45 + s67;
-    return lo + hi;
-}
-
-typedef const u32x4 __attribute__((address_space(1)))* gcodes_t;
-typedef const uint8_t __attribute__((address_space(1)))* gbytes_t;
-
-// Weight codes are read once: non-temporal loads keep them out of the caches' way.
-#ifndef XP_NT_CODES
-#define XP_NT_CODES 1
-#endif
-__device__ __forceinline__ u32x4 load_codes(gcodes_t p) {
-#if XP_NT_CODES
-    return __builtin_nontemporal_load(p);
-#else
-    return *p;
-#endif
-}
-
-// Groups kept in flight per wave: deep for small passes, shallower as rows add
-// registers (gate/up keeps within 128 VGPRs for 16-wave workgroups; down within
-// 128 so that two 8-wave workgroups share a CU).
-#ifndef XP_GU_DEPTH_1
-#define XP_GU_DEPTH_1 2
-#endif
-#ifndef XP_DN_DEPTH_1
-#define XP_DN_DEPTH_1 2
-#endif
-#ifndef XP_GU_DEPTH_4
-#define XP_GU_DEPTH_4 2  // passes of 3-4 rows (5-8 rows: one group in flight)
-#endif
-#ifndef XP_DN_DEPTH_4
-#define XP_DN_DEPTH_4 2
-#endif
-template <int P>
-struct GuDepth {
-    static constexpr int value = P <= 2 ? XP_GU_DEPTH_1 : (P <= 4 ? XP_GU_DEPTH_4 : 1);
-};
-template <int P>
-struct DnDepth {
-    static constexpr int value = P == 1 ? XP_DN_DEPTH_1 : (P <= 4 ? XP_DN_DEPTH_4 : 1);
-};
-
-// ------------------------------------------------------------------ gate/up
-
-// One leaf of one matrix (gate or up) for one (pass, tile): returns the P leaf
-// values of this lane's column. The leaf's groups are g = leaf, leaf+8, ...;
-// every leaf walks ceil(G/8) of them so the loop body has no branches (the
-// ring's wait counts then follow it exactly): a group past the end re-reads
-// group G-1 and its product is discarded by a select.
-template <int P>
-__device__ __forceinline__ void gu_leaf(gcodes_t cc, gbytes_t ss, const uint32_t* const (&xr)[P], int leaf, int G,
-                                        int lane, float (&acc)[P]) {
-    constexpr int D = GuDepth<P>::value;
-    const int xl = lane & 15;
-    const int ng = (G + 7) >> 3;
-#pragma unroll
-    for (int r = 0; r < P; ++r) acc[r] = 0.0f;
-    u32x4 bc[D];
-    uint32_t bs[D];
-    uint32_t bx[D][P];
-    auto load = [&](int s, int i) {
-        const int g = min(leaf + 8 * i, G - 1);
-        bc[s] = load_codes(cc + (size_t)g * kTile);
-        bs[s] = ss[(size_t)g * kTile];
-#pragma unroll
-        for (int r = 0; r < P; ++r) bx[s][r] = xr[r][16 * g + xl];
-    };
-#pragma unroll
-    for (int s = 0; s < D; ++s) load(s, s);
-    for (int i0 = 0; i0 < ng; i0 += D) {
-#pragma unroll
-        for (int s = 0; s < D; ++s) {
-            const int i = i0 + s;
-            const float sc = e4m3(bs[s]);
-            uint32_t xc[P];
-#pragma unroll
-            for (int r = 0; r < P; ++r) xc[r] = bx[s][r];
-            const u32x4 cw = bc[s];
-            load(s, i + D);
-            float p[P], xa[P], xb[P];
-            { float w[8]; decode8(cw[0], w); Chain<P>::head_bf16(w, xc, xa, xb, p); }
-            { float w[8]; decode8(cw[1], w); Chain<P>::tail1(w, xa, xb, p); }
-            { float w[8]; decode8(cw[2], w); Chain<P>::tail2(w, xa, xb, p); }
-            { float w[8]; decode8(cw[3], w); Chain<P>::tail3(w, xa, xb, p); }
-            const bool valid = leaf + 8 * i < G;
-#pragma unroll
-            for (int r = 0; r < P; ++r) {
-                const float v = __builtin_fmaf(p[r], sc, acc[r]);
-                acc[r] = valid ? v : acc[r];
-            }
-        }
-    }
-}
-
-// Gate/up outputs: act in fp32, g and u in fp32 (split), or act stored as bf16.
-enum GuOut { kActF32 = 0, kSplit = 1, kActBf16 = 2 };
-
-template <int P, int OUT>
-__device__ __forceinline__ void gu_item(const xp_expert* __restrict__ experts, const uint16_t* __restrict__ x,
-                        const int32_t* __restrict__ entry, int4 ps, int tile, int H, int I, int k,
-                        float* __restrict__ out0, float* __restrict__ out1, float* red) {
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    const int leaf = wave & 7, up = wave >> 3;
-    const int e = ps.x, first = ps.y, real = ps.z;
-    const int G = H >> 5;
-
-    const xp_expert ex = experts[e];
-    const size_t tile_chunks = (size_t)tile * G * kTile;
-    const gcodes_t cc = (gcodes_t)(up ? ex.up_codes : ex.gate_codes) + tile_chunks + lane;
-    const gbytes_t ss = (gbytes_t)(up ? ex.up_scales : ex.gate_scales) + tile_chunks + lane;
-
-    const uint32_t* xr[P];
-#pragma unroll
-    for (int r = 0; r < P; ++r) {
-        const int ent = entry[first + (r < real ? r : real - 1)];
-        xr[r] = (const uint32_t*)(x + (size_t)(ent / k) * H);
-    }
-    float acc[P];
-    gu_leaf<P>(cc, ss, xr, leaf, G, lane, acc);
-
-    // leaves -> LDS: red[wave][row][lane], gate leaves in waves 0-7, up in 8-15
-#pragma unroll
-    for (int r = 0; r < P; ++r) red[(wave * P + r) * kTile + lane] = acc[r];
-    __syncthreads();
-    const int t = threadIdx.x;
-    if (t < P * kTile) {
-        const int r = t >> 6, c = t & 63;
-        if (r < real) {
-            const int stride = P * kTile;
-            const float g = tree8(red + r * kTile + c, stride);
-            const float u = tree8(red + 8 * stride + r * kTile + c, stride);
-            const size_t o = (size_t)entry[first + r] * I + (size_t)tile * kTile + c;
-            if (OUT == kSplit) {
-                out0[o] = g;
-                out1[o] = u;
-            } else {
-                const float a = (g / (1.0f + expf(-g))) * u;
-                if (OUT == kActBf16)
-                    ((uint16_t*)out0)[o] = bf16_rne(a);
-                else
-                    out0[o] = a;
-            }
-        }
-    }
-    __syncthreads();
-}
-
-// Routing inputs of the one-row route + gate/up launch.
-struct RouteIn {
-    const float* logits;
-    int E;
-    int32_t* topk_id;
-    float* topk_w;
-    WsPtrs w;
-};
 
 // Gate/up passes over the plan in the workspace: work item = (pass, tile).
 template <int OUT>
@@ -250,35 +65,6 @@ __global__ __launch_bounds__(1024) void gateup_kernel(const xp_expert* __restric
 // (slot k-1, tile 0) runs all k rounds and publishes what xp_route_bucket
 // writes for this row: top-k ids and weights, counts, offsets, entries and both
 // pass lists (one P=1 pass per chosen expert, experts ascending).
-__device__ void publish_one_row(const RouteIn& ri, int k, uint32_t mo, uint32_t mi) {
-    const int lane = threadIdx.x & 63;
-    const float w = topk_weight(mo, k);
-    int rank = 0;  // position of this lane's pick among the picks by expert id
-    for (int i = 0; i < k; ++i) rank += ((uint32_t)__builtin_amdgcn_readlane((int)mi, i) < mi) ? 1 : 0;
-    if (lane < k) {
-        ri.topk_id[lane] = (int32_t)mi;
-        ri.topk_w[lane] = w;
-        ri.w.gu_pass[rank] = make_int4((int)mi, rank, 1, 1);
-        ri.w.dn_pass[rank] = make_int4((int)mi, rank, 1, 1);
-        ri.w.entry[rank] = lane;  // row 0, slot lane
-    }
-    for (int e0 = 0; e0 <= ri.E; e0 += 64) {
-        const int e = e0 + lane;
-        int below = 0, hit = 0;
-        for (int i = 0; i < k; ++i) {
-            const int o = __builtin_amdgcn_readlane((int)mi, i);
-            below += o < e ? 1 : 0;
-            hit |= o == e ? 1 : 0;
-        }
-        if (e <= ri.E) ri.w.offset[e] = below;
-        if (e < ri.E) ri.w.count[e] = hit;
-    }
-    if (lane == 0) {
-        ri.w.hdr[0] = k;
-        ri.w.hdr[1] = k;
-    }
-}
-
 __global__ __launch_bounds__(1024) void gateup_one_row_kernel(const xp_expert* __restrict__ experts,
                                                               const uint16_t* __restrict__ x, RouteIn ri, int H,
                                                               int I, int k, float* __restrict__ act) {
@@ -439,19 +225,9 @@ __global__ __launch_bounds__(512, 4) void down_kernel(const xp_expert* __restric
 // The leaves meet in LDS, out is stored, and the combine's fma chain over
 // slots runs in the same workgroup, so no combine launch follows.
 // Workgroups: hidden / 16; waves: 8 * ceil(k / 4), so k <= 8.
-constexpr int kNarrow = 16;
 #ifndef XP_DC_DEPTH
 #define XP_DC_DEPTH 2  // groups in flight per wave (4 and 8 measured slower: 10.1 -> 11.4 / 13.4 us)
 #endif
-
-// Column slice of workgroup b: the four 16-column slices of a 64-column tile
-// go to workgroups on one XCD (workgroup b runs on XCD b mod 8), so the tile's
-// lines are fetched into that XCD's L2 once; n_slices = hidden / 16.
-__device__ __forceinline__ int narrow_col0(int b, int n_slices) {
-    const int n_tiles = n_slices >> 2;
-    const int tile = (n_tiles & 7) == 0 ? (b >> 5) * 8 + (b & 7) : b >> 2;
-    return tile * kTile + ((n_tiles & 7) == 0 ? (b >> 3) & 3 : b & 3) * kNarrow;
-}
 
 __global__ __launch_bounds__(1024) void down_combine_one_row_kernel(
     const xp_expert* __restrict__ experts, const float* __restrict__ act, const int32_t* __restrict__ entry,

@@ -81,7 +81,7 @@ def lib():
         L.xp_fp8_pack.argtypes = [i32, i32, P, P, P]
         L.xp_fp8_rows.argtypes = [i32, i32, i32, P, P, P, P, i32, P]
         L.xp_fp8_rows_f32.argtypes = [i32, i32, i32, P, P, P, P, i32, P]
-        L.xp_stream_weights.argtypes = [D, P, P, i32, P, P]
+        L.xp_stream_weights.argtypes = [D, P, P, i32, i32, P, P]
         L.xp_decode_static.argtypes = [D, i32, P, P, P, P, P, P, P, P, P]
         L.xp_set_tiers.argtypes = [P, i32, P, i32]
         L.xp_get_tiers.argtypes = [P, P, P, P]
@@ -397,14 +397,15 @@ def xp_fp8_rows_f32(rows: int, n: int, k: int, x, packed, scales, y, slices: int
                                  int(slices), _stream(stream)), "xp_fp8_rows_f32")
 
 
-def xp_stream_weights(d: xp_dims, experts, ids, sink, stream=None) -> None:
-    """Bandwidth probe: read the packed weights of the experts in ``ids`` once (see xp.h)."""
+def xp_stream_weights(d: xp_dims, experts, ids, sink, parts: int = 7, stream=None) -> None:
+    """Bandwidth probe: read the packed weights of the matrices in ``parts`` (bit 0
+    gate, 1 up, 2 down) of the experts in ``ids`` once (see xp.h)."""
     n = 0 if ids is None else ids.numel()
     if n > 0:
         _dev(experts, torch.int64, "experts", d.n_experts * 6)
         _dev(ids, torch.int32, "ids")
         _dev(sink, torch.int32 if sink.dtype == torch.int32 else torch.uint32, "sink", 1)
-    _check(lib().xp_stream_weights(ctypes.byref(d), _ptr(experts), _ptr(ids), int(n), _ptr(sink),
+    _check(lib().xp_stream_weights(ctypes.byref(d), _ptr(experts), _ptr(ids), int(n), int(parts), _ptr(sink),
                                    _stream(stream)), "xp_stream_weights")
 
 

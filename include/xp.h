@@ -290,17 +290,19 @@ int xp_fp8_rows_f32(int32_t rows, int32_t n, int32_t k, const float* x, const ui
 /* ------------------------------------------------------ measurement probe */
 
 /* Bandwidth probe (not part of the layer): read every byte of the packed
- * weights of the experts ids[0 .. n_ids-1] (device int32, each in
- * [0, n_experts), with non-NULL table entries) once -- the codes and scales of
- * gate, up and down, hidden * inter * 3 * (1/2 + 1/32) bytes per expert -- with
- * the decode kernels' 16-byte non-temporal loads and no arithmetic on the
- * weights. Its duration is the time the memory system needs to deliver the
- * weight bytes a decode layer streams (each distinct expert once), the
- * attainable ceiling that layer's weight stream is measured against. sink:
- * one device uint32, written only if a folded word equals a fixed constant.
- * n_ids == 0 enqueues nothing; n_ids outside [0, n_experts] is XP_ERR_SHAPE. */
+ * weights of the matrices named in `parts` (bit 0 gate, bit 1 up, bit 2 down;
+ * 1..7) of the experts ids[0 .. n_ids-1] (device int32, each in [0, n_experts),
+ * with non-NULL table entries) once -- codes and scales, hidden * inter *
+ * (1/2 + 1/32) bytes per matrix -- with the decode kernels' 16-byte
+ * non-temporal loads and no arithmetic on the weights, in one launch of many
+ * small workgroups. Its duration is the time the memory system needs to
+ * deliver those bytes in one launch: the attainable ceiling a decode launch
+ * streaming them (each distinct expert once) is measured against. sink: one
+ * device uint32, written only if a folded word equals a fixed constant.
+ * n_ids == 0 enqueues nothing; n_ids outside [0, n_experts] or parts outside
+ * 1..7 is XP_ERR_SHAPE. */
 int xp_stream_weights(const xp_dims* dims, const xp_expert* experts, const int32_t* ids, int32_t n_ids,
-                      uint32_t* sink, void* stream);
+                      int32_t parts, uint32_t* sink, void* stream);
 
 /* ------------------------------------------------------------ pass sizes */
 

@@ -191,10 +191,12 @@ def test_stream_probe_argument_checks():
     L = xp.lib()
     d = xp.dims(256, 128, 8, 2)
     P = ctypes.c_void_p(0x1000)
-    assert L.xp_stream_weights(ctypes.byref(d), None, None, 0, None, None) == xp.XP_OK   # nothing to read
-    assert L.xp_stream_weights(ctypes.byref(d), P, P, -1, P, None) == xp.XP_ERR_SHAPE
-    assert L.xp_stream_weights(ctypes.byref(d), P, P, 9, P, None) == xp.XP_ERR_SHAPE    # more ids than experts
-    assert L.xp_stream_weights(ctypes.byref(d), None, P, 2, P, None) == xp.XP_ERR_NULL
-    assert L.xp_stream_weights(ctypes.byref(d), P, P, 2, None, None) == xp.XP_ERR_NULL
+    assert L.xp_stream_weights(ctypes.byref(d), None, None, 0, 7, None, None) == xp.XP_OK   # nothing to read
+    assert L.xp_stream_weights(ctypes.byref(d), P, P, -1, 7, P, None) == xp.XP_ERR_SHAPE
+    assert L.xp_stream_weights(ctypes.byref(d), P, P, 9, 7, P, None) == xp.XP_ERR_SHAPE    # more ids than experts
+    for parts in (0, 8, -1):
+        assert L.xp_stream_weights(ctypes.byref(d), P, P, 2, parts, P, None) == xp.XP_ERR_SHAPE
+    assert L.xp_stream_weights(ctypes.byref(d), None, P, 2, 7, P, None) == xp.XP_ERR_NULL
+    assert L.xp_stream_weights(ctypes.byref(d), P, P, 2, 3, None, None) == xp.XP_ERR_NULL
     bad = xp.dims(100, 128, 8, 2)
-    assert L.xp_stream_weights(ctypes.byref(bad), P, P, 2, P, None) == xp.XP_ERR_SHAPE
+    assert L.xp_stream_weights(ctypes.byref(bad), P, P, 2, 7, P, None) == xp.XP_ERR_SHAPE

@@ -25,7 +25,7 @@ def test_device_generator_matches_host():
         assert np.array_equal(s.cpu().numpy(), synth.scales(seed, layer, e, t + 1, N, K, -6, 0))
 
 
-@pytest.mark.parametrize("N,K", [(64, 32), (128, 256), (256, 128), (2048, 4096)])
+@pytest.mark.parametrize("N,K", [(64, 32), (128, 256), (256, 128), (64, 192), (128, 320), (64, 544), (2048, 4096)])
 def test_pack_layout(N, K):
     rng = np.random.default_rng(N + K)
     codes = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
@@ -96,6 +96,7 @@ def test_stream_probe_reads_and_writes_nothing():
     layer = DeviceLayer(synth.CONFIGS["tiny"], 0)
     ids = torch.arange(layer.cfg.E, dtype=torch.int32, device="cuda")
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
-    xp.xp_stream_weights(layer.d, layer.table, ids, sink)
+    for parts in (7, 3, 4, 1):
+        xp.xp_stream_weights(layer.d, layer.table, ids, sink, parts)
     torch.cuda.synchronize()
     assert int(sink.item()) in (0, 0x9E3779B9 - (1 << 32))
