@@ -50,6 +50,12 @@ def lib():
         L.or_e4m3fn.restype = f64
         L.or_bf16.argtypes = [ctypes.c_uint16]
         L.or_bf16.restype = f64
+        L.or_e8m0.argtypes = [u]
+        L.or_e8m0.restype = f64
+        L.or_dequant_coded.argtypes = [i32, P, P, P]
+        L.or_dequant_coded.restype = None
+        L.or_layer_coded.argtypes = [i32] * 5 + [P] * 14
+        L.or_layer_coded.restype = i32
         L.or_round_bf16.argtypes = [f64]
         L.or_round_bf16.restype = f64
         L.or_route.argtypes = [i32, i32, i32, P, P, P]
@@ -104,6 +110,24 @@ def e4m3fn(byte: int) -> float:
 
 def bf16(bits: int) -> float:
     return lib().or_bf16(int(bits))
+
+
+def e8m0(byte: int) -> float:
+    return lib().or_e8m0(int(byte))
+
+
+def dequant_coded(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """float64 activations from E4M3FN codes [..][H] and E8M0 scales [..][H/32] (one per 32)."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    H = codes.shape[-1]
+    rows = codes.reshape(-1, H)
+    sc = scales.reshape(-1, H // 32)
+    assert sc.shape[0] == rows.shape[0]
+    out = np.zeros(rows.shape, dtype=np.float64)
+    for r in range(rows.shape[0]):
+        lib().or_dequant_coded(H, _p(rows[r]), _p(sc[r]), _p(out[r]))
+    return out.reshape(codes.shape)
 
 
 def decode_matrix(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
@@ -238,6 +262,38 @@ def layer(x_bf16: np.ndarray, logits: np.ndarray, experts: dict, H: int, I: int,
         raise KeyError("oracle.layer: experts %s are routed but not given" % sorted(missing))
     threads = lib().or_layer(H, I, E, k, R, _p(x_bf16), _p(logits), *tables,
                              _p(topk_id), _p(topk_w), _p(act), _p(out), _p(y), 1 if act_bf16 else 0)
+    return dict(topk_id=topk_id, topk_w=topk_w, act=act, out=out, y=y, threads=threads)
+
+
+def layer_coded(x_codes: np.ndarray, x_scales: np.ndarray, logits: np.ndarray, experts: dict, H: int, I: int,
+                E: int, k: int):
+    """float64 layer over R rows whose activations are coded: x_codes [R][H] E4M3FN,
+    x_scales [R][H/32] E8M0 (x = e4m3fn(code) * 2^(scale - 127)); otherwise as layer()."""
+    x_codes = _c(x_codes, np.uint8)
+    x_scales = _c(x_scales, np.uint8)
+    logits = _c(logits, np.float32)
+    R = x_codes.shape[0]
+    assert x_codes.shape == (R, H) and x_scales.shape == (R, H // 32) and logits.shape == (R, E)
+    names = ("gate_codes", "gate_scales", "up_codes", "up_scales", "down_codes", "down_scales")
+    keep, tables = [], []
+    for nm in names:
+        arr = (ctypes.c_void_p * E)()
+        for e, ex in experts.items():
+            a = _c(ex[nm], np.uint8)
+            keep.append(a)
+            arr[e] = a.ctypes.data
+        tables.append(arr)
+    ids_chk, _ = route(logits, k)
+    missing = set(int(e) for e in np.unique(ids_chk)) - set(experts)
+    if missing:
+        raise KeyError("oracle.layer_coded: experts %s are routed but not given" % sorted(missing))
+    topk_id = np.zeros((R, k), dtype=np.int32)
+    topk_w = np.zeros((R, k), dtype=np.float64)
+    act = np.zeros((R, k, I), dtype=np.float64)
+    out = np.zeros((R, k, H), dtype=np.float64)
+    y = np.zeros((R, H), dtype=np.float64)
+    threads = lib().or_layer_coded(H, I, E, k, R, _p(x_codes), _p(x_scales), _p(logits), *tables,
+                                   _p(topk_id), _p(topk_w), _p(act), _p(out), _p(y))
     return dict(topk_id=topk_id, topk_w=topk_w, act=act, out=out, y=y, threads=threads)
 
 

@@ -53,6 +53,24 @@ double or_e4m3fn(unsigned byte) {
     return sign ? -mag : mag;
 }
 
+/* E8M0 (the OCP MX scale format): an unsigned biased exponent, value
+ * 2^(byte - 127); 0xFF is NaN. Reading for coded activations: the pages name a
+ * gate/up path over E4M3 activation codes ("32 fp4 by E4M3 (or bf16)
+ * products") but give no activation scale; we read one power-of-two scale per
+ * 32 activations, stored as E8M0 like an MX block scale. [#2983, "What this
+ * changes"; commit list: the gate/up coded kernels] */
+double or_e8m0(unsigned byte) {
+    byte &= 255u;
+    if (byte == 255u) return NAN;
+    return ldexp(1.0, (int)byte - 127);
+}
+
+/* Coded activations to float64: x[i] = e4m3fn(code[i]) * e8m0(scale[i / 32]),
+ * exact (a 4-significant-bit value times a power of two). */
+void or_dequant_coded(int n, const uint8_t* codes, const uint8_t* scales, double* x) {
+    for (int i = 0; i < n; ++i) x[i] = or_e4m3fn(codes[i]) * or_e8m0(scales[i / 32]);
+}
+
 /* bf16: the high half of an IEEE binary32. */
 double or_bf16(uint16_t bits) {
     uint32_t u = (uint32_t)bits << 16;
@@ -257,12 +275,12 @@ void or_set_threads(int n) {
 #endif
 }
 
-int or_layer(int H, int I, int E, int k, int R, const uint16_t* x_bf16, const float* logits,
-             const uint8_t* const* gate_codes, const uint8_t* const* gate_scales,
-             const uint8_t* const* up_codes, const uint8_t* const* up_scales,
-             const uint8_t* const* down_codes, const uint8_t* const* down_scales,
-             int32_t* topk_id, double* topk_w, double* act, double* out, double* y, int act_bf16) {
-    (void)E;
+/* The layer over R rows whose activations are given in float64 (xr: [R][H]). */
+static int layer_rows(int H, int I, int E, int k, int R, const double* xr, const float* logits,
+                      const uint8_t* const* gate_codes, const uint8_t* const* gate_scales,
+                      const uint8_t* const* up_codes, const uint8_t* const* up_scales,
+                      const uint8_t* const* down_codes, const uint8_t* const* down_scales,
+                      int32_t* topk_id, double* topk_w, double* act, double* out, double* y, int act_bf16) {
     or_route(R, E, k, logits, topk_id, topk_w);
     int used = 1;
 #ifdef _OPENMP
@@ -279,22 +297,49 @@ int or_layer(int H, int I, int E, int k, int R, const uint16_t* x_bf16, const fl
     for (int p = 0; p < pairs; ++p) {
         int r = p / k;
         int e = topk_id[p];
-        double* x = (double*)malloc(sizeof(double) * (size_t)H);
+        const double* x = xr + (size_t)r * H;
         double* g = (double*)malloc(sizeof(double) * (size_t)I);
         double* u = (double*)malloc(sizeof(double) * (size_t)I);
-        for (int i = 0; i < H; ++i) x[i] = or_bf16(x_bf16[(size_t)r * H + i]);
         or_matvec(I, H, gate_codes[e], gate_scales[e], x, g);
         or_matvec(I, H, up_codes[e], up_scales[e], x, u);
         or_swiglu(I, g, u, act + (size_t)p * I);
         if (act_bf16)
             for (int i = 0; i < I; ++i) act[(size_t)p * I + i] = or_round_bf16(act[(size_t)p * I + i]);
         or_matvec(H, I, down_codes[e], down_scales[e], act + (size_t)p * I, out + (size_t)p * H);
-        free(x);
         free(g);
         free(u);
     }
     for (int r = 0; r < R; ++r)
         or_combine(k, H, topk_w + (size_t)r * k, out + (size_t)r * k * H, y + (size_t)r * H);
+    return used;
+}
+
+int or_layer(int H, int I, int E, int k, int R, const uint16_t* x_bf16, const float* logits,
+             const uint8_t* const* gate_codes, const uint8_t* const* gate_scales,
+             const uint8_t* const* up_codes, const uint8_t* const* up_scales,
+             const uint8_t* const* down_codes, const uint8_t* const* down_scales,
+             int32_t* topk_id, double* topk_w, double* act, double* out, double* y, int act_bf16) {
+    double* xr = (double*)malloc(sizeof(double) * (size_t)R * H);
+    for (size_t i = 0; i < (size_t)R * H; ++i) xr[i] = or_bf16(x_bf16[i]);
+    int used = layer_rows(H, I, E, k, R, xr, logits, gate_codes, gate_scales, up_codes, up_scales, down_codes,
+                          down_scales, topk_id, topk_w, act, out, y, act_bf16);
+    free(xr);
+    return used;
+}
+
+/* The layer with coded activations: row r's x is or_dequant_coded of its H
+ * E4M3FN codes and H/32 E8M0 scales; everything after is or_layer's. */
+int or_layer_coded(int H, int I, int E, int k, int R, const uint8_t* x_codes, const uint8_t* x_scales,
+                   const float* logits, const uint8_t* const* gate_codes, const uint8_t* const* gate_scales,
+                   const uint8_t* const* up_codes, const uint8_t* const* up_scales,
+                   const uint8_t* const* down_codes, const uint8_t* const* down_scales,
+                   int32_t* topk_id, double* topk_w, double* act, double* out, double* y) {
+    double* xr = (double*)malloc(sizeof(double) * (size_t)R * H);
+    for (int r = 0; r < R; ++r)
+        or_dequant_coded(H, x_codes + (size_t)r * H, x_scales + (size_t)r * (H / 32), xr + (size_t)r * H);
+    int used = layer_rows(H, I, E, k, R, xr, logits, gate_codes, gate_scales, up_codes, up_scales, down_codes,
+                          down_scales, topk_id, topk_w, act, out, y, 0);
+    free(xr);
     return used;
 }
 

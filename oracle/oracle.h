@@ -27,6 +27,8 @@ extern "C" {
 double or_e2m1(unsigned code);
 double or_e4m3fn(unsigned byte);
 double or_bf16(uint16_t bits);
+double or_e8m0(unsigned byte);
+void or_dequant_coded(int n, const uint8_t* codes, const uint8_t* scales, double* x);
 /* float64 -> nearest bf16 value (ties to even, one rounding), as a double */
 double or_round_bf16(double v);
 
@@ -62,6 +64,12 @@ int or_layer(int H, int I, int E, int k, int R, const uint16_t* x_bf16, const fl
              const uint8_t* const* up_codes, const uint8_t* const* up_scales,
              const uint8_t* const* down_codes, const uint8_t* const* down_scales,
              int32_t* topk_id, double* topk_w, double* act, double* out, double* y, int act_bf16);
+/* or_layer with coded activations: x_codes [R][H] E4M3FN, x_scales [R][H/32] E8M0. */
+int or_layer_coded(int H, int I, int E, int k, int R, const uint8_t* x_codes, const uint8_t* x_scales,
+                   const float* logits, const uint8_t* const* gate_codes, const uint8_t* const* gate_scales,
+                   const uint8_t* const* up_codes, const uint8_t* const* up_scales,
+                   const uint8_t* const* down_codes, const uint8_t* const* down_scales,
+                   int32_t* topk_id, double* topk_w, double* act, double* out, double* y);
 
 /* fp32 replay of the per-row arithmetic (chain, scaled fma, eight-leaf tree),
  * for x given as float: y[n] for n in [0, N). */

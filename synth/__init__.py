@@ -30,6 +30,7 @@ M2 = 0x94D049BB133111EB
 GATE_CODES, GATE_SCALES, UP_CODES, UP_SCALES, DOWN_CODES, DOWN_SCALES = 1, 2, 3, 4, 5, 6
 X, LOGITS, BIAS, PLANT = 7, 8, 9, 10
 FP8_WEIGHTS, FP8_SCALES = 11, 12
+X_CODES, X_SCALES = 13, 14
 MATRICES = {
     "gate": (GATE_CODES, GATE_SCALES),
     "up": (UP_CODES, UP_SCALES),
@@ -174,6 +175,19 @@ def activations(seed: int, layer: int, R: int, H: int) -> np.ndarray:
     """bf16 N(0,1) activations [R][H] as uint16 bit patterns."""
     z = normals(stream_key(seed, layer, X), 0, R * H).astype(np.float32)
     return f32_to_bf16_bits(z).reshape(R, H)
+
+
+def coded_activations(seed: int, layer: int, R: int, H: int, emin: int = -6, emax: int = -2):
+    """Coded activations: E4M3FN codes [R][H] uniform over the 254 non-NaN bytes
+    (0x7F and 0xFF skipped) and one E8M0 scale byte per 32, 127 + e with e
+    uniform on {emin..emax}: [R][H/32]. Returns (codes, scales), uint8."""
+    w = stream(stream_key(seed, layer, X_CODES), 0, R * H)
+    b = ((w >> np.uint64(32)) * np.uint64(254)) >> np.uint64(32)
+    b = np.where(b >= np.uint64(0x7F), b + np.uint64(1), b)
+    n = np.uint64(emax - emin + 1)
+    ws = stream(stream_key(seed, layer, X_SCALES), 0, R * (H // 32))
+    e = (((ws >> np.uint64(32)) * n) >> np.uint64(32)).astype(np.int64) + emin
+    return b.astype(np.uint8).reshape(R, H), (e + 127).astype(np.uint8).reshape(R, H // 32)
 
 
 def logits(seed: int, layer: int, R: int, E: int, bias_sigma: float = 0.0) -> np.ndarray:
