@@ -79,14 +79,26 @@ struct DnDepth {
 
 // ------------------------------------------------------------------ gate/up
 
+// An E8M0 byte (an OCP MX scale) as fp32: 2^(b - 127), exact; 0 is 2^-127 (a
+// subnormal), 0xFF NaN.
+__device__ __forceinline__ float e8m0(uint32_t b) {
+    if (b == 255u) return __builtin_nanf("");
+    return b == 0u ? __uint_as_float(0x00400000u) : __uint_as_float(b << 23);
+}
+
 // One leaf of one matrix (gate or up) for one (pass, tile): returns the P leaf
 // values of this lane's column. The leaf's groups are g = leaf, leaf+8, ...;
 // every leaf walks ceil(G/8) of them so the loop body has no branches (the
 // ring's wait counts then follow it exactly): a group past the end re-reads
 // group G-1 and its product is discarded by a select.
-template <int P>
-__device__ __forceinline__ void gu_leaf(gcodes_t cc, gbytes_t ss, const uint32_t* const (&xr)[P], int leaf, int G,
-                                        int lane, float (&acc)[P]) {
+// Activations: bf16 rows (xr[r] = the row's 16-bit pairs), or, when CODED,
+// E4M3FN codes (xr[r] = the row's code bytes, read as pairs) with one E8M0
+// scale per group (sr[r] = the row's scale bytes); a coded value enters the
+// chain as e4m3(code) * 2^(scale - 127), computed exactly in fp32, so the chain
+// is the bf16 path's on those values.
+template <int P, bool CODED>
+__device__ __forceinline__ void gu_leaf(gcodes_t cc, gbytes_t ss, const uint32_t* const (&xr)[P],
+                                        const uint8_t* const (&sr)[P], int leaf, int G, int lane, float (&acc)[P]) {
     constexpr int D = GuDepth<P>::value;
     const int xl = lane & 15;
     const int ng = (G + 7) >> 3;
@@ -95,12 +107,20 @@ __device__ __forceinline__ void gu_leaf(gcodes_t cc, gbytes_t ss, const uint32_t
     u32x4 bc[D];
     uint32_t bs[D];
     uint32_t bx[D][P];
+    uint32_t bsx[D][P];
     auto load = [&](int s, int i) {
         const int g = min(leaf + 8 * i, G - 1);
         bc[s] = load_codes(cc + (size_t)g * kTile);
         bs[s] = ss[(size_t)g * kTile];
 #pragma unroll
-        for (int r = 0; r < P; ++r) bx[s][r] = xr[r][16 * g + xl];
+        for (int r = 0; r < P; ++r) {
+            if constexpr (CODED) {
+                bx[s][r] = ((const uint16_t*)xr[r])[16 * g + xl];
+                bsx[s][r] = sr[r][g];
+            } else {
+                bx[s][r] = xr[r][16 * g + xl];
+            }
+        }
     };
 #pragma unroll
     for (int s = 0; s < D; ++s) load(s, s);
@@ -109,13 +129,25 @@ __device__ __forceinline__ void gu_leaf(gcodes_t cc, gbytes_t ss, const uint32_t
         for (int s = 0; s < D; ++s) {
             const int i = i0 + s;
             const float sc = e4m3(bs[s]);
-            uint32_t xc[P];
-#pragma unroll
-            for (int r = 0; r < P; ++r) xc[r] = bx[s][r];
-            const u32x4 cw = bc[s];
-            load(s, i + D);
             float p[P], xa[P], xb[P];
-            { float w[8]; decode8(cw[0], w); Chain<P>::head_bf16(w, xc, xa, xb, p); }
+            const u32x4 cw = bc[s];
+            if constexpr (CODED) {
+#pragma unroll
+                for (int r = 0; r < P; ++r) {
+                    const f32x2 v = __builtin_amdgcn_cvt_pk_f32_fp8((int)bx[s][r], false);
+                    const float sx = e8m0(bsx[s][r]);
+                    xa[r] = v.x * sx;
+                    xb[r] = v.y * sx;
+                }
+                load(s, i + D);
+                { float w[8]; decode8(cw[0], w); Chain<P>::head_f32(w, xa, xb, p); }
+            } else {
+                uint32_t xc[P];
+#pragma unroll
+                for (int r = 0; r < P; ++r) xc[r] = bx[s][r];
+                load(s, i + D);
+                { float w[8]; decode8(cw[0], w); Chain<P>::head_bf16(w, xc, xa, xb, p); }
+            }
             { float w[8]; decode8(cw[1], w); Chain<P>::tail1(w, xa, xb, p); }
             { float w[8]; decode8(cw[2], w); Chain<P>::tail2(w, xa, xb, p); }
             { float w[8]; decode8(cw[3], w); Chain<P>::tail3(w, xa, xb, p); }
@@ -132,10 +164,11 @@ __device__ __forceinline__ void gu_leaf(gcodes_t cc, gbytes_t ss, const uint32_t
 // Gate/up outputs: act in fp32, g and u in fp32 (split), or act stored as bf16.
 enum GuOut { kActF32 = 0, kSplit = 1, kActBf16 = 2 };
 
-template <int P, int OUT>
-__device__ __forceinline__ void gu_item(const xp_expert* __restrict__ experts, const uint16_t* __restrict__ x,
-                        const int32_t* __restrict__ entry, int4 ps, int tile, int H, int I, int k,
-                        float* __restrict__ out0, float* __restrict__ out1, float* red) {
+// x: bf16 rows [R][H], or, when CODED, E4M3FN code rows [R][H] with E8M0 scales xs [R][H/32].
+template <int P, int OUT, bool CODED = false>
+__device__ __forceinline__ void gu_item(const xp_expert* __restrict__ experts, const void* __restrict__ x,
+                        const uint8_t* __restrict__ xs, const int32_t* __restrict__ entry, int4 ps, int tile,
+                        int H, int I, int k, float* __restrict__ out0, float* __restrict__ out1, float* red) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int leaf = wave & 7, up = wave >> 3;
@@ -148,13 +181,20 @@ __device__ __forceinline__ void gu_item(const xp_expert* __restrict__ experts, c
     const gbytes_t ss = (gbytes_t)(up ? ex.up_scales : ex.gate_scales) + tile_chunks + lane;
 
     const uint32_t* xr[P];
+    const uint8_t* sr[P];
 #pragma unroll
     for (int r = 0; r < P; ++r) {
-        const int ent = entry[first + (r < real ? r : real - 1)];
-        xr[r] = (const uint32_t*)(x + (size_t)(ent / k) * H);
+        const size_t row = (size_t)(entry[first + (r < real ? r : real - 1)] / k);
+        if constexpr (CODED) {
+            xr[r] = (const uint32_t*)((const uint8_t*)x + row * H);
+            sr[r] = xs + row * (H >> 5);
+        } else {
+            xr[r] = (const uint32_t*)((const uint16_t*)x + row * H);
+            sr[r] = nullptr;
+        }
     }
     float acc[P];
-    gu_leaf<P>(cc, ss, xr, leaf, G, lane, acc);
+    gu_leaf<P, CODED>(cc, ss, xr, sr, leaf, G, lane, acc);
 
     // leaves -> LDS: red[wave][row][lane], gate leaves in waves 0-7, up in 8-15
 #pragma unroll

@@ -28,9 +28,9 @@
 namespace xp {
 
 // Gate/up passes over the plan in the workspace: work item = (pass, tile).
-template <int OUT>
+template <int OUT, bool CODED = false>
 __global__ __launch_bounds__(1024) void gateup_kernel(const xp_expert* __restrict__ experts,
-                                                      const uint16_t* __restrict__ x,
+                                                      const void* __restrict__ x, const uint8_t* __restrict__ xs,
                                                       const int32_t* __restrict__ hdr,
                                                       const int32_t* __restrict__ entry,
                                                       const int4* __restrict__ passes, int E, int H, int I,
@@ -44,14 +44,14 @@ __global__ __launch_bounds__(1024) void gateup_kernel(const xp_expert* __restric
         const int tile = item - pass * n_tiles;
         const int4 ps = passes[pass];
         switch (ps.w) {
-            case 1: gu_item<1, OUT>(tab, x, entry, ps, tile, H, I, k, out0, out1, red); break;
-            case 2: gu_item<2, OUT>(tab, x, entry, ps, tile, H, I, k, out0, out1, red); break;
-            case 3: gu_item<3, OUT>(tab, x, entry, ps, tile, H, I, k, out0, out1, red); break;
-            case 4: gu_item<4, OUT>(tab, x, entry, ps, tile, H, I, k, out0, out1, red); break;
-            case 5: gu_item<5, OUT>(tab, x, entry, ps, tile, H, I, k, out0, out1, red); break;
-            case 6: gu_item<6, OUT>(tab, x, entry, ps, tile, H, I, k, out0, out1, red); break;
-            case 7: gu_item<7, OUT>(tab, x, entry, ps, tile, H, I, k, out0, out1, red); break;
-            case 8: gu_item<8, OUT>(tab, x, entry, ps, tile, H, I, k, out0, out1, red); break;
+            case 1: gu_item<1, OUT, CODED>(tab, x, xs, entry, ps, tile, H, I, k, out0, out1, red); break;
+            case 2: gu_item<2, OUT, CODED>(tab, x, xs, entry, ps, tile, H, I, k, out0, out1, red); break;
+            case 3: gu_item<3, OUT, CODED>(tab, x, xs, entry, ps, tile, H, I, k, out0, out1, red); break;
+            case 4: gu_item<4, OUT, CODED>(tab, x, xs, entry, ps, tile, H, I, k, out0, out1, red); break;
+            case 5: gu_item<5, OUT, CODED>(tab, x, xs, entry, ps, tile, H, I, k, out0, out1, red); break;
+            case 6: gu_item<6, OUT, CODED>(tab, x, xs, entry, ps, tile, H, I, k, out0, out1, red); break;
+            case 7: gu_item<7, OUT, CODED>(tab, x, xs, entry, ps, tile, H, I, k, out0, out1, red); break;
+            case 8: gu_item<8, OUT, CODED>(tab, x, xs, entry, ps, tile, H, I, k, out0, out1, red); break;
             default: break;
         }
     }
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(1024) void gateup_one_row_kernel(const xp_expert* _
         if (publish) publish_one_row(ri, k, mo, mi);
     }
     __syncthreads();
-    gu_item<1, kActF32>(experts, x, s_entry, make_int4(s_pick, 0, 1, 1), tile, H, I, k, act, nullptr, red);
+    gu_item<1, kActF32>(experts, x, nullptr, s_entry, make_int4(s_pick, 0, 1, 1), tile, H, I, k, act, nullptr, red);
 }
 
 // A16: act is bf16 (the bf16-storage variant); its pairs reach the chain as
@@ -433,27 +433,36 @@ static int grid_for(int rows, int k, int n_tiles) {
     return (int)(items < kMaxItemsGrid ? items : kMaxItemsGrid);
 }
 
-static int gateup_common(const xp_dims* dims, int32_t rows, const uint16_t* x, const xp_expert* experts,
-                         const void* ws, size_t ws_bytes, float* o0, float* o1, int mode, void* stream) {
+// mode: a GuOut, or kCoded (act in fp32 from E4M3FN-coded activations with E8M0 scales xs).
+constexpr int kCoded = 16;
+
+static int gateup_common(const xp_dims* dims, int32_t rows, const void* x, const uint8_t* xs,
+                         const xp_expert* experts, const void* ws, size_t ws_bytes, float* o0, float* o1, int mode,
+                         void* stream) {
     int st = check_dims(dims);
     if (st != XP_OK) return st;
     if (rows < 0) return XP_ERR_SHAPE;
     if (rows == 0) return XP_OK;
-    if (!x || !experts || !ws || !o0 || (mode == kSplit && !o1)) return XP_ERR_NULL;
+    if (!x || !experts || !ws || !o0 || (mode == kSplit && !o1) || (mode == kCoded && !xs)) return XP_ERR_NULL;
     if (ws_bytes < ws_layout(dims, rows).total) return XP_ERR_WORKSPACE;
     Plan pl = plan_view(ws, dims, rows);
     const int grid = grid_for(rows, dims->top_k, dims->inter / kTile);
     hipStream_t s = (hipStream_t)stream;
+    const uint8_t* no_xs = nullptr;
     if (mode == kSplit)
-        hipLaunchKernelGGL((gateup_kernel<kSplit>), dim3(grid), dim3(1024), 0, s, experts, x, pl.hdr, pl.entry,
-                           pl.gu_pass, dims->n_experts, dims->hidden, dims->inter, dims->top_k, o0, o1);
+        hipLaunchKernelGGL((gateup_kernel<kSplit>), dim3(grid), dim3(1024), 0, s, experts, x, no_xs, pl.hdr,
+                           pl.entry, pl.gu_pass, dims->n_experts, dims->hidden, dims->inter, dims->top_k, o0, o1);
     else if (mode == kActBf16)
-        hipLaunchKernelGGL((gateup_kernel<kActBf16>), dim3(grid), dim3(1024), 0, s, experts, x, pl.hdr,
+        hipLaunchKernelGGL((gateup_kernel<kActBf16>), dim3(grid), dim3(1024), 0, s, experts, x, no_xs, pl.hdr,
+                           pl.entry, pl.gu_pass, dims->n_experts, dims->hidden, dims->inter, dims->top_k, o0,
+                           (float*)nullptr);
+    else if (mode == kCoded)
+        hipLaunchKernelGGL((gateup_kernel<kActF32, true>), dim3(grid), dim3(1024), 0, s, experts, x, xs, pl.hdr,
                            pl.entry, pl.gu_pass, dims->n_experts, dims->hidden, dims->inter, dims->top_k, o0,
                            (float*)nullptr);
     else
-        hipLaunchKernelGGL((gateup_kernel<kActF32>), dim3(grid), dim3(1024), 0, s, experts, x, pl.hdr, pl.entry,
-                           pl.gu_pass, dims->n_experts, dims->hidden, dims->inter, dims->top_k, o0,
+        hipLaunchKernelGGL((gateup_kernel<kActF32>), dim3(grid), dim3(1024), 0, s, experts, x, no_xs, pl.hdr,
+                           pl.entry, pl.gu_pass, dims->n_experts, dims->hidden, dims->inter, dims->top_k, o0,
                            (float*)nullptr);
     return launch_status();
 }
@@ -464,17 +473,24 @@ using namespace xp;
 
 XP_API int xp_gateup_rows(const xp_dims* dims, int32_t rows, const uint16_t* x, const xp_expert* experts,
                           const void* workspace, size_t ws_bytes, float* act, void* stream) {
-    return gateup_common(dims, rows, x, experts, workspace, ws_bytes, act, nullptr, kActF32, stream);
+    return gateup_common(dims, rows, x, nullptr, experts, workspace, ws_bytes, act, nullptr, kActF32, stream);
 }
 
 XP_API int xp_gateup_rows_split(const xp_dims* dims, int32_t rows, const uint16_t* x, const xp_expert* experts,
                                 const void* workspace, size_t ws_bytes, float* g, float* u, void* stream) {
-    return gateup_common(dims, rows, x, experts, workspace, ws_bytes, g, u, kSplit, stream);
+    return gateup_common(dims, rows, x, nullptr, experts, workspace, ws_bytes, g, u, kSplit, stream);
 }
 
 XP_API int xp_gateup_rows_act16(const xp_dims* dims, int32_t rows, const uint16_t* x, const xp_expert* experts,
                                 const void* workspace, size_t ws_bytes, uint16_t* act16, void* stream) {
-    return gateup_common(dims, rows, x, experts, workspace, ws_bytes, (float*)act16, nullptr, kActBf16, stream);
+    return gateup_common(dims, rows, x, nullptr, experts, workspace, ws_bytes, (float*)act16, nullptr, kActBf16,
+                         stream);
+}
+
+XP_API int xp_gateup_rows_coded(const xp_dims* dims, int32_t rows, const uint8_t* x_codes, const uint8_t* x_scales,
+                                const xp_expert* experts, const void* workspace, size_t ws_bytes, float* act,
+                                void* stream) {
+    return gateup_common(dims, rows, x_codes, x_scales, experts, workspace, ws_bytes, act, nullptr, kCoded, stream);
 }
 
 static int down_common(const xp_dims* dims, int32_t rows, const void* act, const xp_expert* experts,

@@ -24,7 +24,7 @@ EXPORTS = (
     "xp_set_tiers", "xp_get_tiers", "xp_status_string", "xp_route_gateup", "xp_down_combine",
     "xp_prefill_gateup", "xp_prefill_down", "xp_fp8_packed_bytes", "xp_fp8_pack", "xp_fp8_rows",
     "xp_gateup_rows_act16", "xp_down_rows_act16", "xp_combine_y16", "xp_fp8_rows_f32", "xp_stream_weights",
-    "xp_decode_static",
+    "xp_decode_static", "xp_gateup_rows_coded",
 )
 
 
@@ -83,6 +83,7 @@ def lib():
         L.xp_fp8_rows_f32.argtypes = [i32, i32, i32, P, P, P, P, i32, P]
         L.xp_stream_weights.argtypes = [D, P, P, i32, i32, P, P]
         L.xp_decode_static.argtypes = [D, i32, P, P, P, P, P, P, P, P, P]
+        L.xp_gateup_rows_coded.argtypes = [D, i32, P, P, P, P, sz, P, P]
         L.xp_set_tiers.argtypes = [P, i32, P, i32]
         L.xp_get_tiers.argtypes = [P, P, P, P]
         L.xp_status_string.argtypes = [ctypes.c_int]
@@ -91,7 +92,8 @@ def lib():
                      "xp_gateup_rows_split", "xp_down_rows", "xp_combine", "xp_set_tiers", "xp_get_tiers",
                      "xp_route_gateup", "xp_down_combine", "xp_prefill_gateup", "xp_prefill_down",
                      "xp_fp8_pack", "xp_fp8_rows", "xp_gateup_rows_act16", "xp_down_rows_act16",
-                     "xp_combine_y16", "xp_fp8_rows_f32", "xp_stream_weights", "xp_decode_static"):
+                     "xp_combine_y16", "xp_fp8_rows_f32", "xp_stream_weights", "xp_decode_static",
+                     "xp_gateup_rows_coded"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
         try:
@@ -325,6 +327,18 @@ def xp_prefill_down(d: xp_dims, rows: int, act, experts, workspace, out, stream=
     nbytes = workspace.numel() if workspace is not None else 0
     _check(lib().xp_prefill_down(ctypes.byref(d), int(rows), _ptr(act), _ptr(experts), _ptr(workspace), nbytes,
                                  _ptr(out), _stream(stream)), "xp_prefill_down")
+
+
+def xp_gateup_rows_coded(d: xp_dims, rows: int, x_codes, x_scales, experts, workspace, act, stream=None) -> None:
+    """Gate/up over E4M3FN-coded activations with one E8M0 scale per 32 (see xp.h)."""
+    if rows > 0:
+        _dev(x_codes, torch.uint8, "x_codes", rows * d.hidden)
+        _dev(x_scales, torch.uint8, "x_scales", rows * (d.hidden // 32))
+        _dev(experts, torch.int64, "experts", d.n_experts * 6)
+        _dev(act, torch.float32, "act", rows * d.top_k * d.inter)
+    nbytes = workspace.numel() if workspace is not None else 0
+    _check(lib().xp_gateup_rows_coded(ctypes.byref(d), int(rows), _ptr(x_codes), _ptr(x_scales), _ptr(experts),
+                                      _ptr(workspace), nbytes, _ptr(act), _stream(stream)), "xp_gateup_rows_coded")
 
 
 def _dev_u16(t: torch.Tensor, name: str, numel: int) -> None:

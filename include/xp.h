@@ -236,6 +236,23 @@ int xp_down_rows_act16(const xp_dims* dims, int32_t rows, const uint16_t* act16,
 int xp_combine_y16(const xp_dims* dims, int32_t rows, const float* out, const float* topk_w, uint16_t* y16,
                    void* stream);
 
+/* ------------------------------------------------- coded activations
+ * Gate/up over activations given as E4M3FN codes [#2983, "What this changes":
+ * the chain's 32 products are fp4 weights by E4M3 (or bf16) activations; the
+ * commit list registers gate/up kernels over coded activations]. The pages give
+ * no activation scale; here each row carries one E8M0 scale per 32 activations
+ * (the OCP MX block-scale convention): x[row][k] = e4m3(x_codes[row][k]) *
+ * 2^(x_scales[row][k/32] - 127) (scale byte 0xFF is NaN). That value is formed
+ * exactly in fp32 and enters the same per-row chain, scaled fma, tree and
+ * epilogue as xp_gateup_rows, so the result is bit-equal to xp_gateup_rows on
+ * the bf16 activations holding those values (whenever they are bf16 values,
+ * i.e. always except below bf16's subnormal range). x_codes: [rows][H] bytes;
+ * x_scales: [rows][H/32] bytes. Same plan, workspace, act and errors as
+ * xp_gateup_rows. */
+int xp_gateup_rows_coded(const xp_dims* dims, int32_t rows, const uint8_t* x_codes, const uint8_t* x_scales,
+                         const xp_expert* experts, const void* workspace, size_t ws_bytes, float* act,
+                         void* stream);
+
 /* ------------------------------------------------- dense FP8 projections
  * The decode layer's other weight stream: y = x W^T for a dense projection
  * whose weights are E4M3FN bytes with one fp32 scale per 128 x 128 block

@@ -200,3 +200,17 @@ def test_stream_probe_argument_checks():
     assert L.xp_stream_weights(ctypes.byref(d), P, P, 2, 3, None, None) == xp.XP_ERR_NULL
     bad = xp.dims(100, 128, 8, 2)
     assert L.xp_stream_weights(ctypes.byref(bad), P, P, 2, 7, P, None) == xp.XP_ERR_SHAPE
+
+
+def test_coded_argument_checks():
+    L = xp.lib()
+    d = xp.dims(256, 128, 8, 2)
+    P = ctypes.c_void_p(0x1000)
+    need = xp.xp_workspace_bytes(d, 4)
+    assert L.xp_gateup_rows_coded(ctypes.byref(d), 0, None, None, None, None, 0, None, None) == xp.XP_OK
+    assert L.xp_gateup_rows_coded(ctypes.byref(d), 4, P, None, P, P, need, P, None) == xp.XP_ERR_NULL
+    assert L.xp_gateup_rows_coded(ctypes.byref(d), 4, None, P, P, P, need, P, None) == xp.XP_ERR_NULL
+    assert L.xp_gateup_rows_coded(ctypes.byref(d), 4, P, P, P, P, need - 1, P, None) == xp.XP_ERR_WORKSPACE
+    assert L.xp_gateup_rows_coded(ctypes.byref(d), -1, P, P, P, P, need, P, None) == xp.XP_ERR_SHAPE
+    bad = xp.dims(4000, 128, 8, 2)
+    assert L.xp_gateup_rows_coded(ctypes.byref(bad), 4, P, P, P, P, need, P, None) == xp.XP_ERR_SHAPE
