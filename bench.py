@@ -440,6 +440,7 @@ class Fp8Cell:
         self.x = torch.from_numpy(xb.view(np.int16).copy()).cuda()
         self.xf = torch.from_numpy(synth.bf16_bits_to_f32(xb) + np.float32(1.0 / 3.0)).cuda()  # full fp32 values
         self.y = torch.empty((rmax, nmax), dtype=torch.float32, device="cuda")
+        self.ys = [torch.empty((rmax, N), dtype=torch.float32, device="cuda") for N, _ in FP8_SHAPES]
         self.set_bytes = sum(N * K + ((N + 127) // 128) * (K // 128) * 4 for N, K in FP8_SHAPES)
         torch.cuda.synchronize()
 
@@ -470,6 +471,25 @@ def time_fp8(cell: Fp8Cell, steps: int, warmup: int) -> dict:
         torch.cuda.synchronize()
         ms = _replay_ms(g, steps)
         del g
+        # the same round with one launch per layer for the projections that share x (same K)
+        by_k = {}
+        for i, (N, K) in enumerate(FP8_SHAPES):
+            by_k.setdefault(K, []).append(i)
+
+        def rnd_multi():
+            from fp4_routed_expert_xp_amd import xp
+            for l in range(cell.layers):
+                for K, idx in by_k.items():
+                    mats = [(cell.mats[l][i][0], cell.mats[l][i][1], cell.ys[i]) for i in idx]
+                    xp.xp_fp8_rows_multi(R, K, xs[K], mats)
+        rnd_multi()
+        torch.cuda.synchronize()
+        g = _graph(rnd_multi)
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        ms_multi = _replay_ms(g, steps)
+        del g
         xfs = {K: cell.xf[:R, :K].contiguous() for _, K in FP8_SHAPES}
 
         def run_f32(i, l):
@@ -487,9 +507,15 @@ def time_fp8(cell: Fp8Cell, steps: int, warmup: int) -> dict:
                 dst["%dx%d" % (N, K)] = round(_replay_ms(gk, 5) * 1e3 / cell.layers, 3)
                 del gk
         layer_us = ms * 1e3 / cell.layers
+        multi_us = ms_multi * 1e3 / cell.layers
         out[R] = dict(rows=R, round_ms=round(ms, 4), layer_us=round(layer_us, 3),
                       weight_gbps=round(cell.set_bytes / (layer_us * 1e-6) / 1e9, 1),
                       pct_hbm_peak=round(100 * cell.set_bytes / (layer_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 2),
+                      multi=dict(launches_per_layer=len(by_k), round_ms=round(ms_multi, 4),
+                                 layer_us=round(multi_us, 3),
+                                 weight_gbps=round(cell.set_bytes / (multi_us * 1e-6) / 1e9, 1),
+                                 pct_hbm_peak=round(100 * cell.set_bytes / (multi_us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                                                    2)),
                       kernel_us=per, kernel_us_f32_rows=per_f32)
     return out
 

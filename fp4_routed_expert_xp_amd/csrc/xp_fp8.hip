@@ -171,19 +171,41 @@ struct Run<RUN, F32, 1> {
     }
 };
 
-// One workgroup: 16 columns [16t, 16t + 16), all rows. RUN = blocks per slice;
-// F32: rows of x are fp32 (else bf16).
+// Matrices that share x and K, run by one launch: matrix i owns the
+// workgroups [tile0[i], tile0[i+1]), one per 16 of its n[i] columns.
+constexpr int kMaxMats = 8;
+struct MatSet {
+    int count;
+    int tile0[kMaxMats + 1];
+    int n[kMaxMats];
+    const uint8_t* pw[kMaxMats];
+    const float* scale[kMaxMats];
+    float* y[kMaxMats];
+};
+
+// One workgroup: 16 columns [16t, 16t + 16), all rows, of one matrix of the
+// set. RUN = blocks per slice; F32: rows of x are fp32 (else bf16).
 template <int RUN, bool F32>
-__global__ __launch_bounds__(1024) void fp8_rows_kernel(int R, int N, int KB, const void* __restrict__ x,
-                                                        const uint8_t* __restrict__ pw,
-                                                        const float* __restrict__ scale, float* __restrict__ y) {
+__global__ __launch_bounds__(1024) void fp8_rows_kernel(int R, int KB, const void* __restrict__ x, MatSet ms) {
     __shared__ float red[kMaxSlices * 4 * 64];
     __shared__ u32x4v xsh[kMaxSlices * 16 * kXRow];
     const int S = blockDim.x >> 6;
     const int slice = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int c = lane & 15, q = lane >> 4;
-    const int t = blockIdx.x;
+    // this workgroup's matrix (selects with constant indices keep the set in scalar registers)
+    int m = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxMats; ++i)
+        if (i < ms.count && (int)blockIdx.x >= ms.tile0[i]) m = i;
+    int N = ms.n[0], t0 = ms.tile0[0];
+    const uint8_t* __restrict__ pw = ms.pw[0];
+    const float* __restrict__ scale = ms.scale[0];
+    float* __restrict__ y = ms.y[0];
+#pragma unroll
+    for (int i = 1; i < kMaxMats; ++i)
+        if (i == m) { N = ms.n[i]; t0 = ms.tile0[i]; pw = ms.pw[i]; scale = ms.scale[i]; y = ms.y[i]; }
+    const int t = (int)blockIdx.x - t0;
     const int K = KB * kBlock;
 
     Slice<RUN, F32> sl;
@@ -293,12 +315,30 @@ XP_API int xp_fp8_pack(int32_t n, int32_t k, const uint8_t* w, uint8_t* packed, 
     return launch_status();
 }
 
-static int fp8_rows_common(int32_t rows, int32_t n, int32_t k, const void* x, const uint8_t* packed,
-                           const float* scales, float* y, int32_t slices, bool f32, void* stream) {
-    if (!fp8_shape_ok(n, k) || rows < 0) return XP_ERR_SHAPE;
+static int fp8_rows_set(int32_t rows, int32_t k, const void* x, const xp_fp8_matrix* mats, int32_t count,
+                        int32_t slices, bool f32, void* stream) {
+    if (rows < 0 || k <= 0 || count < 1 || count > kMaxMats) return XP_ERR_SHAPE;
+    if (!mats) return XP_ERR_NULL;
+    MatSet ms{};
+    ms.count = count;
+    long long tiles = 0;
+    for (int i = 0; i < count; ++i) {
+        if (!fp8_shape_ok(mats[i].n, k)) return XP_ERR_SHAPE;
+        if (rows > 0 && (!mats[i].packed || !mats[i].scales || !mats[i].y)) return XP_ERR_NULL;
+        if (rows > 0 && (!aligned(mats[i].packed, 16) || !aligned(mats[i].scales, 4) || !aligned(mats[i].y, 4)))
+            return XP_ERR_SHAPE;
+        ms.tile0[i] = (int)tiles;
+        ms.n[i] = mats[i].n;
+        ms.pw[i] = mats[i].packed;
+        ms.scale[i] = mats[i].scales;
+        ms.y[i] = mats[i].y;
+        tiles += mats[i].n / kCols;
+    }
+    if (tiles > 0x7fffffffLL) return XP_ERR_SHAPE;
+    ms.tile0[count] = (int)tiles;
     if (rows == 0) return XP_OK;
-    if (!x || !packed || !scales || !y) return XP_ERR_NULL;
-    if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 4) || !aligned(y, 4)) return XP_ERR_SHAPE;
+    if (!x) return XP_ERR_NULL;
+    if (!aligned(x, 16)) return XP_ERR_SHAPE;
     const int KB = k / kBlock;
     const int P = next_pow2(KB);
     int S = slices;
@@ -307,9 +347,9 @@ static int fp8_rows_common(int32_t rows, int32_t n, int32_t k, const void* x, co
     const int run = P / S;
     if (run > kMaxRun) return XP_ERR_SHAPE;
     hipStream_t s = (hipStream_t)stream;
-    const dim3 grid(n / kCols), block(64 * S);
+    const dim3 grid((unsigned)tiles), block(64 * S);
 #define XP_FP8_LAUNCH(RUN_, F32_)                                                                            \
-    hipLaunchKernelGGL((fp8_rows_kernel<RUN_, F32_>), grid, block, 0, s, rows, n, KB, x, packed, scales, y)
+    hipLaunchKernelGGL((fp8_rows_kernel<RUN_, F32_>), grid, block, 0, s, rows, KB, x, ms)
     if (f32) {
         switch (run) {
             case 1: XP_FP8_LAUNCH(1, true); break;
@@ -329,12 +369,26 @@ static int fp8_rows_common(int32_t rows, int32_t n, int32_t k, const void* x, co
     return launch_status();
 }
 
+static int fp8_rows_one(int32_t rows, int32_t n, int32_t k, const void* x, const uint8_t* packed,
+                        const float* scales, float* y, int32_t slices, bool f32, void* stream) {
+    if (!fp8_shape_ok(n, k) || rows < 0) return XP_ERR_SHAPE;
+    if (rows == 0) return XP_OK;
+    if (!x || !packed || !scales || !y) return XP_ERR_NULL;
+    const xp_fp8_matrix m{n, packed, scales, y};
+    return fp8_rows_set(rows, k, x, &m, 1, slices, f32, stream);
+}
+
 XP_API int xp_fp8_rows(int32_t rows, int32_t n, int32_t k, const uint16_t* x, const uint8_t* packed,
                        const float* scales, float* y, int32_t slices, void* stream) {
-    return fp8_rows_common(rows, n, k, x, packed, scales, y, slices, false, stream);
+    return fp8_rows_one(rows, n, k, x, packed, scales, y, slices, false, stream);
 }
 
 XP_API int xp_fp8_rows_f32(int32_t rows, int32_t n, int32_t k, const float* x, const uint8_t* packed,
                            const float* scales, float* y, int32_t slices, void* stream) {
-    return fp8_rows_common(rows, n, k, x, packed, scales, y, slices, true, stream);
+    return fp8_rows_one(rows, n, k, x, packed, scales, y, slices, true, stream);
+}
+
+XP_API int xp_fp8_rows_multi(int32_t rows, int32_t k, const uint16_t* x, const xp_fp8_matrix* mats, int32_t count,
+                             int32_t slices, void* stream) {
+    return fp8_rows_set(rows, k, x, mats, count, slices, false, stream);
 }

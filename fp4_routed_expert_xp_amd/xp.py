@@ -24,8 +24,13 @@ EXPORTS = (
     "xp_set_tiers", "xp_get_tiers", "xp_status_string", "xp_route_gateup", "xp_down_combine",
     "xp_prefill_gateup", "xp_prefill_down", "xp_fp8_packed_bytes", "xp_fp8_pack", "xp_fp8_rows",
     "xp_gateup_rows_act16", "xp_down_rows_act16", "xp_combine_y16", "xp_fp8_rows_f32", "xp_stream_weights",
-    "xp_decode_static", "xp_gateup_rows_coded",
+    "xp_decode_static", "xp_gateup_rows_coded", "xp_fp8_rows_multi",
 )
+
+
+class xp_fp8_matrix(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int32), ("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("y", ctypes.c_void_p)]
 
 
 class XPError(RuntimeError):
@@ -84,6 +89,7 @@ def lib():
         L.xp_stream_weights.argtypes = [D, P, P, i32, i32, P, P]
         L.xp_decode_static.argtypes = [D, i32, P, P, P, P, P, P, P, P, P]
         L.xp_gateup_rows_coded.argtypes = [D, i32, P, P, P, P, sz, P, P]
+        L.xp_fp8_rows_multi.argtypes = [i32, i32, P, ctypes.POINTER(xp_fp8_matrix), i32, i32, P]
         L.xp_set_tiers.argtypes = [P, i32, P, i32]
         L.xp_get_tiers.argtypes = [P, P, P, P]
         L.xp_status_string.argtypes = [ctypes.c_int]
@@ -93,7 +99,7 @@ def lib():
                      "xp_route_gateup", "xp_down_combine", "xp_prefill_gateup", "xp_prefill_down",
                      "xp_fp8_pack", "xp_fp8_rows", "xp_gateup_rows_act16", "xp_down_rows_act16",
                      "xp_combine_y16", "xp_fp8_rows_f32", "xp_stream_weights", "xp_decode_static",
-                     "xp_gateup_rows_coded"):
+                     "xp_gateup_rows_coded", "xp_fp8_rows_multi"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
         try:
@@ -421,6 +427,23 @@ def xp_stream_weights(d: xp_dims, experts, ids, sink, parts: int = 7, stream=Non
         _dev(sink, torch.int32 if sink.dtype == torch.int32 else torch.uint32, "sink", 1)
     _check(lib().xp_stream_weights(ctypes.byref(d), _ptr(experts), _ptr(ids), int(n), int(parts), _ptr(sink),
                                    _stream(stream)), "xp_stream_weights")
+
+
+def xp_fp8_rows_multi(rows: int, k: int, x, mats, slices: int = 0, stream=None) -> None:
+    """One launch for several FP8 projections of the same rows: mats is a list of
+    (packed, scales, y) device tensors, y [rows][n] (see xp_fp8_rows_multi in xp.h)."""
+    arr = (xp_fp8_matrix * max(len(mats), 1))()
+    for i, (packed, scales, y) in enumerate(mats):
+        n = packed.numel() // k if k > 0 else 0
+        if rows > 0:
+            _dev(packed, torch.uint8, "packed", n * k)
+            _dev(scales, torch.float32, "scales", ((n + 127) // 128) * (k // 128))
+            _dev(y, torch.float32, "y", rows * n)
+        arr[i] = xp_fp8_matrix(n, _ptr(packed), _ptr(scales), _ptr(y))
+    if rows > 0:
+        _dev_bf16(x, "x", rows * k)
+    _check(lib().xp_fp8_rows_multi(int(rows), int(k), _ptr(x), arr, len(mats), int(slices), _stream(stream)),
+           "xp_fp8_rows_multi")
 
 
 # -------------------------------------------------------------- conveniences

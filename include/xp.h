@@ -304,6 +304,24 @@ int xp_fp8_rows(int32_t rows, int32_t n, int32_t k, const uint16_t* x, const uin
 int xp_fp8_rows_f32(int32_t rows, int32_t n, int32_t k, const float* x, const uint8_t* packed,
                     const float* scales, float* y, int32_t slices, void* stream);
 
+/* One launch for several projections that read the same rows x [rows][k]
+ * (bf16): matrix i has n = mats[i].n output columns, its packed weights,
+ * scales and output y [rows][n] as for xp_fp8_rows. Each matrix's y is bit for
+ * bit what xp_fp8_rows gives for it alone with the same `slices` (the form
+ * rule and limits of xp_fp8_rows, with k shared by all); the launch saves the
+ * fixed cost of one launch per matrix [#2983, commit list: the FP8 commit runs
+ * a decode step's dense FP8 projections]. mats: host array of count (1..8)
+ * descriptors; errors as xp_fp8_rows, XP_ERR_SHAPE for a count outside 1..8. */
+typedef struct {
+    int32_t n;
+    const uint8_t* packed;
+    const float* scales;
+    float* y;
+} xp_fp8_matrix;
+
+int xp_fp8_rows_multi(int32_t rows, int32_t k, const uint16_t* x, const xp_fp8_matrix* mats, int32_t count,
+                      int32_t slices, void* stream);
+
 /* ------------------------------------------------------ measurement probe */
 
 /* Bandwidth probe (not part of the layer): read every byte of the packed

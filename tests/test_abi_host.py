@@ -214,3 +214,21 @@ def test_coded_argument_checks():
     assert L.xp_gateup_rows_coded(ctypes.byref(d), -1, P, P, P, P, need, P, None) == xp.XP_ERR_SHAPE
     bad = xp.dims(4000, 128, 8, 2)
     assert L.xp_gateup_rows_coded(ctypes.byref(bad), 4, P, P, P, P, need, P, None) == xp.XP_ERR_SHAPE
+
+
+def test_fp8_multi_argument_checks():
+    L = xp.lib()
+    P = ctypes.c_void_p(16)
+    arr = (xp.xp_fp8_matrix * 2)(xp.xp_fp8_matrix(16, 16, 16, 16), xp.xp_fp8_matrix(48, 16, 16, 16))
+    assert L.xp_fp8_rows_multi(0, 128, None, arr, 2, 0, None) == xp.XP_OK
+    assert L.xp_fp8_rows_multi(1, 128, P, arr, 0, 0, None) == xp.XP_ERR_SHAPE
+    assert L.xp_fp8_rows_multi(1, 128, P, arr, 9, 0, None) == xp.XP_ERR_SHAPE
+    assert L.xp_fp8_rows_multi(1, 128, P, None, 2, 0, None) == xp.XP_ERR_NULL
+    assert L.xp_fp8_rows_multi(1, 100, P, arr, 2, 0, None) == xp.XP_ERR_SHAPE     # k not a multiple of 128
+    bad = (xp.xp_fp8_matrix * 1)(xp.xp_fp8_matrix(20, 16, 16, 16))                 # n not a multiple of 16
+    assert L.xp_fp8_rows_multi(1, 128, P, bad, 1, 0, None) == xp.XP_ERR_SHAPE
+    nul = (xp.xp_fp8_matrix * 1)(xp.xp_fp8_matrix(16, None, 16, 16))
+    assert L.xp_fp8_rows_multi(1, 128, P, nul, 1, 0, None) == xp.XP_ERR_NULL
+    odd = (xp.xp_fp8_matrix * 1)(xp.xp_fp8_matrix(16, 0x1008, 16, 16))
+    assert L.xp_fp8_rows_multi(1, 128, P, odd, 1, 0, None) == xp.XP_ERR_SHAPE
+    assert L.xp_fp8_rows_multi(1, 128, ctypes.c_void_p(0x1008), arr, 2, 0, None) == xp.XP_ERR_SHAPE

@@ -239,3 +239,39 @@ def test_fp8_f32_one_hot_rows_are_exact():
     for r, k in enumerate(ks):
         x[r, k] = 1.0
     assert np.array_equal(bits(m.run_f32(x)), bits(oracle.fp8_proj_f32(x, m.w, m.s).astype(np.float32)))
+
+
+@pytest.mark.parametrize("K,Ns", [(4096, (576, 1536, 4096)), (512, (16, 48, 304, 1024, 16, 32, 64, 128)),
+                                  (2048, (1024,))])
+def test_fp8_rows_multi_equals_separate_launches(K, Ns):
+    """One launch over several matrices that share x: each matrix's y bit-equal to
+    its own xp_fp8_rows launch, at row counts 1, 5, 16 and 33, with NaN and +Inf
+    planted in other rows, in the default form and in the form with the fewest
+    waves per workgroup (four blocks per wave)."""
+    mats = [Fp8Matrix(N, K, layer=i) for i, N in enumerate(Ns)]
+    P = 1
+    while P < K // 128:
+        P *= 2
+    for R in (1, 5, 16, 33):
+        x = synth.activations(SEED + 70 + R, 0, R, K)
+        if R >= 2:
+            x, _, _ = synth.plant_nan_inf(SEED + 70, R, x)
+        for slices in (0, max(1, P // 4)):
+            ys = [torch.full((R, m.N), float("nan"), dtype=torch.float32, device="cuda") for m in mats]
+            xp.xp_fp8_rows_multi(R, K, to_dev(x), [(m.packed, m.s_dev, y) for m, y in zip(mats, ys)], slices)
+            torch.cuda.synchronize()
+            for m, y in zip(mats, ys):
+                assert np.array_equal(bits(y.cpu().numpy()), bits(m.run(x, slices))), (K, m.N, R, slices)
+
+
+def test_fp8_rows_multi_refusals():
+    m = Fp8Matrix(16, 128)
+    x = to_dev(synth.activations(SEED, 0, 1, 128))
+    y = torch.empty((1, 16), dtype=torch.float32, device="cuda")
+    with pytest.raises(xp.XPError) as ei:
+        xp.xp_fp8_rows_multi(1, 128, x, [(m.packed, m.s_dev, y)] * 9)
+    assert ei.value.status == xp.XP_ERR_SHAPE
+    with pytest.raises(xp.XPError) as ei:
+        xp.xp_fp8_rows_multi(1, 128, x, [])
+    assert ei.value.status == xp.XP_ERR_SHAPE
+    xp.xp_fp8_rows_multi(0, 128, None, [(m.packed, m.s_dev, y)])   # no rows: nothing to do
