@@ -1,6 +1,6 @@
-// xp_pass_dev.h — device pieces of a decode pass shared by the pass kernels
-// (xp_rows.hip) and the one-launch layer (xp_layer.hip): weight decode, the
-// eight-leaf tree, the gate/up leaf walk and one gate/up work item.
+// xp_pass_dev.h — device pieces of a decode pass used by the pass kernels
+// (xp_rows.hip): weight decode, the eight-leaf tree, the gate/up leaf walks
+// and one gate/up work item.
 #pragma once
 
 #include "xp_chain_asm.h"
@@ -161,11 +161,96 @@ __device__ __forceinline__ void gu_leaf(gcodes_t cc, gbytes_t ss, const uint32_t
     }
 }
 
+// Both matrices of one leaf for one (pass, tile), in one wave: for each of the
+// leaf's groups the gate and up codes and scales are loaded together, the rows'
+// activations once, and the gate chain then the up chain run over the same
+// converted activations. Per matrix and row this is gu_leaf's arithmetic
+// exactly (the same chain, scaled fma and leaf), so the bits are gu_leaf's.
+template <int P, bool CODED>
+__device__ __forceinline__ void gu_leaf2(gcodes_t cg, gbytes_t sg, gcodes_t cu, gbytes_t su,
+                                         const uint32_t* const (&xr)[P], const uint8_t* const (&sr)[P], int leaf,
+                                         int G, int lane, float (&accg)[P], float (&accu)[P]) {
+    constexpr int D = GuDepth<P>::value;
+    const int xl = lane & 15;
+    const int ng = (G + 7) >> 3;
+#pragma unroll
+    for (int r = 0; r < P; ++r) accg[r] = accu[r] = 0.0f;
+    u32x4 bg[D], bu[D];
+    uint32_t bsg[D], bsu[D];
+    uint32_t bx[D][P];
+    uint32_t bsx[D][P];
+    auto load = [&](int s, int i) {
+        const int g = min(leaf + 8 * i, G - 1);
+        bg[s] = load_codes(cg + (size_t)g * kTile);
+        bu[s] = load_codes(cu + (size_t)g * kTile);
+        bsg[s] = sg[(size_t)g * kTile];
+        bsu[s] = su[(size_t)g * kTile];
+#pragma unroll
+        for (int r = 0; r < P; ++r) {
+            if constexpr (CODED) {
+                bx[s][r] = ((const uint16_t*)xr[r])[16 * g + xl];
+                bsx[s][r] = sr[r][g];
+            } else {
+                bx[s][r] = xr[r][16 * g + xl];
+            }
+        }
+    };
+#pragma unroll
+    for (int s = 0; s < D; ++s) load(s, s);
+    for (int i0 = 0; i0 < ng; i0 += D) {
+#pragma unroll
+        for (int s = 0; s < D; ++s) {
+            const int i = i0 + s;
+            const float scg = e4m3(bsg[s]), scu = e4m3(bsu[s]);
+            const u32x4 cwg = bg[s], cwu = bu[s];
+            float p[P], xa[P], xb[P];
+            if constexpr (CODED) {
+#pragma unroll
+                for (int r = 0; r < P; ++r) {
+                    const f32x2 v = __builtin_amdgcn_cvt_pk_f32_fp8((int)bx[s][r], false);
+                    const float sx = e8m0(bsx[s][r]);
+                    xa[r] = v.x * sx;
+                    xb[r] = v.y * sx;
+                }
+                load(s, i + D);
+                { float w[8]; decode8(cwg[0], w); Chain<P>::head_f32(w, xa, xb, p); }
+            } else {
+                uint32_t xc[P];
+#pragma unroll
+                for (int r = 0; r < P; ++r) xc[r] = bx[s][r];
+                load(s, i + D);
+                { float w[8]; decode8(cwg[0], w); Chain<P>::head_bf16(w, xc, xa, xb, p); }
+            }
+            { float w[8]; decode8(cwg[1], w); Chain<P>::tail1(w, xa, xb, p); }
+            { float w[8]; decode8(cwg[2], w); Chain<P>::tail2(w, xa, xb, p); }
+            { float w[8]; decode8(cwg[3], w); Chain<P>::tail3(w, xa, xb, p); }
+            const bool valid = leaf + 8 * i < G;
+#pragma unroll
+            for (int r = 0; r < P; ++r) {
+                const float v = __builtin_fmaf(p[r], scg, accg[r]);
+                accg[r] = valid ? v : accg[r];
+            }
+            { float w[8]; decode8(cwu[0], w); Chain<P>::head_f32(w, xa, xb, p); }
+            { float w[8]; decode8(cwu[1], w); Chain<P>::tail1(w, xa, xb, p); }
+            { float w[8]; decode8(cwu[2], w); Chain<P>::tail2(w, xa, xb, p); }
+            { float w[8]; decode8(cwu[3], w); Chain<P>::tail3(w, xa, xb, p); }
+#pragma unroll
+            for (int r = 0; r < P; ++r) {
+                const float v = __builtin_fmaf(p[r], scu, accu[r]);
+                accu[r] = valid ? v : accu[r];
+            }
+        }
+    }
+}
+
 // Gate/up outputs: act in fp32, g and u in fp32 (split), or act stored as bf16.
 enum GuOut { kActF32 = 0, kSplit = 1, kActBf16 = 2 };
 
 // x: bf16 rows [R][H], or, when CODED, E4M3FN code rows [R][H] with E8M0 scales xs [R][H/32].
-template <int P, int OUT, bool CODED = false>
+// WAVES = 16: waves 0-7 walk the gate leaves, 8-15 the up leaves (gu_leaf);
+// WAVES = 8: wave j walks leaf j of both matrices (gu_leaf2). The leaves land in
+// the same LDS slots either way, so the tree and epilogue are shared.
+template <int P, int OUT, bool CODED = false, int WAVES = 16>
 __device__ __forceinline__ void gu_item(const xp_expert* __restrict__ experts, const void* __restrict__ x,
                         const uint8_t* __restrict__ xs, const int32_t* __restrict__ entry, int4 ps, int tile,
                         int H, int I, int k, float* __restrict__ out0, float* __restrict__ out1, float* red) {
@@ -177,8 +262,6 @@ __device__ __forceinline__ void gu_item(const xp_expert* __restrict__ experts, c
 
     const xp_expert ex = experts[e];
     const size_t tile_chunks = (size_t)tile * G * kTile;
-    const gcodes_t cc = (gcodes_t)(up ? ex.up_codes : ex.gate_codes) + tile_chunks + lane;
-    const gbytes_t ss = (gbytes_t)(up ? ex.up_scales : ex.gate_scales) + tile_chunks + lane;
 
     const uint32_t* xr[P];
     const uint8_t* sr[P];
@@ -193,12 +276,25 @@ __device__ __forceinline__ void gu_item(const xp_expert* __restrict__ experts, c
             sr[r] = nullptr;
         }
     }
-    float acc[P];
-    gu_leaf<P, CODED>(cc, ss, xr, sr, leaf, G, lane, acc);
-
-    // leaves -> LDS: red[wave][row][lane], gate leaves in waves 0-7, up in 8-15
+    // leaves -> LDS: red[slot][row][lane], gate leaves in slots 0-7, up in 8-15
+    if constexpr (WAVES == 16) {
+        const gcodes_t cc = (gcodes_t)(up ? ex.up_codes : ex.gate_codes) + tile_chunks + lane;
+        const gbytes_t ss = (gbytes_t)(up ? ex.up_scales : ex.gate_scales) + tile_chunks + lane;
+        float acc[P];
+        gu_leaf<P, CODED>(cc, ss, xr, sr, leaf, G, lane, acc);
 #pragma unroll
-    for (int r = 0; r < P; ++r) red[(wave * P + r) * kTile + lane] = acc[r];
+        for (int r = 0; r < P; ++r) red[(wave * P + r) * kTile + lane] = acc[r];
+    } else {
+        float accg[P], accu[P];
+        gu_leaf2<P, CODED>((gcodes_t)ex.gate_codes + tile_chunks + lane, (gbytes_t)ex.gate_scales + tile_chunks + lane,
+                           (gcodes_t)ex.up_codes + tile_chunks + lane, (gbytes_t)ex.up_scales + tile_chunks + lane,
+                           xr, sr, leaf, G, lane, accg, accu);
+#pragma unroll
+        for (int r = 0; r < P; ++r) {
+            red[(leaf * P + r) * kTile + lane] = accg[r];
+            red[((8 + leaf) * P + r) * kTile + lane] = accu[r];
+        }
+    }
     __syncthreads();
     const int t = threadIdx.x;
     if (t < P * kTile) {

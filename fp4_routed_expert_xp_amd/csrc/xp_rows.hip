@@ -3,8 +3,9 @@
 // A work item is (pass, tile of 64 output columns). Lane c of a wave owns column
 // tile*64 + c; each wave owns one leaf j of the eight-leaf tree, i.e. the
 // 32-weight groups g = j, j+8, j+16, ... of the K axis, which it walks in
-// ascending order. Gate/up items run 16 waves (waves 0-7: the gate leaves, 8-15:
-// the up leaves); down items run 8 waves. For each of its groups a lane loads
+// ascending order. Gate/up items run 8 waves, each walking its leaf of both
+// matrices (or, for batches with no more items than CUs, 16 waves: 0-7 the gate
+// leaves, 8-15 the up leaves); down items run 8 waves. For each of its groups a lane loads
 // 16 bytes of codes (one coalesced 1 KiB read per wave in the packed layout) and
 // one scale byte, decodes the 32 weights once (v_cvt_scalef32_pk_f32_fp4 with
 // scale 1, exact; eight at a time, each dword just before its quarter of the
@@ -28,8 +29,13 @@
 namespace xp {
 
 // Gate/up passes over the plan in the workspace: work item = (pass, tile).
-template <int OUT, bool CODED = false>
-__global__ __launch_bounds__(1024) void gateup_kernel(const xp_expert* __restrict__ experts,
+// WAVES = 8: each wave walks one leaf of both matrices and two workgroups share
+// a CU, so that one streams weights while the other reduces and stores; the
+// host takes it when the batch can hold more items than there are CUs.
+// WAVES = 16: gate and up leaves in separate waves, one workgroup per CU (a
+// batch of at most as many items as CUs, e.g. one row).
+template <int OUT, bool CODED, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 16 / WAVES) void gateup_kernel(const xp_expert* __restrict__ experts,
                                                       const void* __restrict__ x, const uint8_t* __restrict__ xs,
                                                       const int32_t* __restrict__ hdr,
                                                       const int32_t* __restrict__ entry,
@@ -44,14 +50,14 @@ __global__ __launch_bounds__(1024) void gateup_kernel(const xp_expert* __restric
         const int tile = item - pass * n_tiles;
         const int4 ps = passes[pass];
         switch (ps.w) {
-            case 1: gu_item<1, OUT, CODED>(tab, x, xs, entry, ps, tile, H, I, k, out0, out1, red); break;
-            case 2: gu_item<2, OUT, CODED>(tab, x, xs, entry, ps, tile, H, I, k, out0, out1, red); break;
-            case 3: gu_item<3, OUT, CODED>(tab, x, xs, entry, ps, tile, H, I, k, out0, out1, red); break;
-            case 4: gu_item<4, OUT, CODED>(tab, x, xs, entry, ps, tile, H, I, k, out0, out1, red); break;
-            case 5: gu_item<5, OUT, CODED>(tab, x, xs, entry, ps, tile, H, I, k, out0, out1, red); break;
-            case 6: gu_item<6, OUT, CODED>(tab, x, xs, entry, ps, tile, H, I, k, out0, out1, red); break;
-            case 7: gu_item<7, OUT, CODED>(tab, x, xs, entry, ps, tile, H, I, k, out0, out1, red); break;
-            case 8: gu_item<8, OUT, CODED>(tab, x, xs, entry, ps, tile, H, I, k, out0, out1, red); break;
+            case 1: gu_item<1, OUT, CODED, WAVES>(tab, x, xs, entry, ps, tile, H, I, k, out0, out1, red); break;
+            case 2: gu_item<2, OUT, CODED, WAVES>(tab, x, xs, entry, ps, tile, H, I, k, out0, out1, red); break;
+            case 3: gu_item<3, OUT, CODED, WAVES>(tab, x, xs, entry, ps, tile, H, I, k, out0, out1, red); break;
+            case 4: gu_item<4, OUT, CODED, WAVES>(tab, x, xs, entry, ps, tile, H, I, k, out0, out1, red); break;
+            case 5: gu_item<5, OUT, CODED, WAVES>(tab, x, xs, entry, ps, tile, H, I, k, out0, out1, red); break;
+            case 6: gu_item<6, OUT, CODED, WAVES>(tab, x, xs, entry, ps, tile, H, I, k, out0, out1, red); break;
+            case 7: gu_item<7, OUT, CODED, WAVES>(tab, x, xs, entry, ps, tile, H, I, k, out0, out1, red); break;
+            case 8: gu_item<8, OUT, CODED, WAVES>(tab, x, xs, entry, ps, tile, H, I, k, out0, out1, red); break;
             default: break;
         }
     }
@@ -428,6 +434,9 @@ __global__ __launch_bounds__(1024) void down_combine_rows_kernel(
     }
 }
 
+// Gate/up batches of at most this many (pass, tile) items (one per CU) run 16-wave workgroups.
+constexpr long kWideItems = 256;
+
 static int grid_for(int rows, int k, int n_tiles) {
     long items = (long)rows * k * n_tiles;  // passes <= rows*k
     return (int)(items < kMaxItemsGrid ? items : kMaxItemsGrid);
@@ -446,24 +455,34 @@ static int gateup_common(const xp_dims* dims, int32_t rows, const void* x, const
     if (!x || !experts || !ws || !o0 || (mode == kSplit && !o1) || (mode == kCoded && !xs)) return XP_ERR_NULL;
     if (ws_bytes < ws_layout(dims, rows).total) return XP_ERR_WORKSPACE;
     Plan pl = plan_view(ws, dims, rows);
-    const int grid = grid_for(rows, dims->top_k, dims->inter / kTile);
+    const int n_tiles = dims->inter / kTile;
+    const int grid = grid_for(rows, dims->top_k, n_tiles);
+    const bool wide = (long)rows * dims->top_k * n_tiles <= kWideItems;
     hipStream_t s = (hipStream_t)stream;
+    const xp_expert* ex = experts;
+    const int32_t* hdr = pl.hdr;
+    const int32_t* ent = pl.entry;
+    const int4* gp = pl.gu_pass;
+    const int E = dims->n_experts, H = dims->hidden, I = dims->inter, k = dims->top_k;
     const uint8_t* no_xs = nullptr;
-    if (mode == kSplit)
-        hipLaunchKernelGGL((gateup_kernel<kSplit>), dim3(grid), dim3(1024), 0, s, experts, x, no_xs, pl.hdr,
-                           pl.entry, pl.gu_pass, dims->n_experts, dims->hidden, dims->inter, dims->top_k, o0, o1);
-    else if (mode == kActBf16)
-        hipLaunchKernelGGL((gateup_kernel<kActBf16>), dim3(grid), dim3(1024), 0, s, experts, x, no_xs, pl.hdr,
-                           pl.entry, pl.gu_pass, dims->n_experts, dims->hidden, dims->inter, dims->top_k, o0,
-                           (float*)nullptr);
-    else if (mode == kCoded)
-        hipLaunchKernelGGL((gateup_kernel<kActF32, true>), dim3(grid), dim3(1024), 0, s, experts, x, xs, pl.hdr,
-                           pl.entry, pl.gu_pass, dims->n_experts, dims->hidden, dims->inter, dims->top_k, o0,
-                           (float*)nullptr);
-    else
-        hipLaunchKernelGGL((gateup_kernel<kActF32>), dim3(grid), dim3(1024), 0, s, experts, x, no_xs, pl.hdr,
-                           pl.entry, pl.gu_pass, dims->n_experts, dims->hidden, dims->inter, dims->top_k, o0,
-                           (float*)nullptr);
+    float* no_o1 = nullptr;
+#define XP_GU_LAUNCH(OUT_, CODED_, XS_, O1_)                                                                   \
+    if (wide)                                                                                               \
+        hipLaunchKernelGGL((gateup_kernel<OUT_, CODED_, 16>), dim3(grid), dim3(1024), 0, s, ex, x, XS_, hdr, ent, \
+                           gp, E, H, I, k, o0, O1_);                                                         \
+    else                                                                                                    \
+        hipLaunchKernelGGL((gateup_kernel<OUT_, CODED_, 8>), dim3(grid), dim3(512), 0, s, ex, x, XS_, hdr, ent,   \
+                           gp, E, H, I, k, o0, O1_);
+    if (mode == kSplit) {
+        XP_GU_LAUNCH(kSplit, false, no_xs, o1)
+    } else if (mode == kActBf16) {
+        XP_GU_LAUNCH(kActBf16, false, no_xs, no_o1)
+    } else if (mode == kCoded) {
+        XP_GU_LAUNCH(kActF32, true, xs, no_o1)
+    } else {
+        XP_GU_LAUNCH(kActF32, false, no_xs, no_o1)
+    }
+#undef XP_GU_LAUNCH
     return launch_status();
 }
 
