@@ -98,7 +98,11 @@ __global__ __launch_bounds__(1024) void gateup_one_row_kernel(const xp_expert* _
 
 // A16: act is bf16 (the bf16-storage variant); its pairs reach the chain as
 // gate/up's x does (one dword of two bf16 per lane of each row of 16).
-template <int P, bool A16>
+// T: output tiles per item (1, or 2: tiles 2*tile and 2*tile+1). With two, each
+// wave walks its leaf of both tiles over one load of the rows' act values, so
+// twice the weight bytes are in flight per wave; per tile the chain, scaled
+// fma, leaf order and tree are the one-tile item's.
+template <int P, bool A16, int T>
 __device__ __forceinline__ void dn_item(const xp_expert* __restrict__ experts, const void* __restrict__ act,
                         const int32_t* __restrict__ entry, int4 ps, int tile, int H, int I,
                         float* __restrict__ out, float* red) {
@@ -108,9 +112,11 @@ __device__ __forceinline__ void dn_item(const xp_expert* __restrict__ experts, c
     const int e = ps.x, first = ps.y, real = ps.z;
     const int G = I >> 5;
     const int xl = 2 * (lane & 15);
+    const int tile0 = tile * T;
 
     const xp_expert ex = experts[e];
-    const size_t tile_chunks = (size_t)tile * G * kTile;
+    const size_t tile_chunks = (size_t)tile0 * G * kTile;
+    const size_t tile_step = (size_t)G * kTile;     // chunks from one tile to the next
     const gcodes_t cc = (gcodes_t)ex.down_codes + tile_chunks + lane;
     const gbytes_t ss = (gbytes_t)ex.down_scales + tile_chunks + lane;
 
@@ -125,17 +131,22 @@ __device__ __forceinline__ void dn_item(const xp_expert* __restrict__ experts, c
 
     // Branch-free ring over ceil(G/8) groups per leaf, as in gu_leaf.
     const int ng = (G + 7) >> 3;
-    float acc[P];
+    float acc[T][P];
 #pragma unroll
-    for (int r = 0; r < P; ++r) acc[r] = 0.0f;
-    u32x4 bc[D];
-    uint32_t bs[D];
+    for (int q = 0; q < T; ++q)
+#pragma unroll
+        for (int r = 0; r < P; ++r) acc[q][r] = 0.0f;
+    u32x4 bc[D][T];
+    uint32_t bs[D][T];
     float2 bx[D][P];
     uint32_t bx16[D][P];
     auto load = [&](int s, int i) {
         const int g = min(leaf + 8 * i, G - 1);
-        bc[s] = load_codes(cc + (size_t)g * kTile);
-        bs[s] = ss[(size_t)g * kTile];
+#pragma unroll
+        for (int q = 0; q < T; ++q) {
+            bc[s][q] = load_codes(cc + q * tile_step + (size_t)g * kTile);
+            bs[s][q] = ss[q * tile_step + (size_t)g * kTile];
+        }
 #pragma unroll
         for (int r = 0; r < P; ++r) {
             if constexpr (A16)
@@ -150,71 +161,84 @@ __device__ __forceinline__ void dn_item(const xp_expert* __restrict__ experts, c
 #pragma unroll
         for (int s = 0; s < D; ++s) {
             const int i = i0 + s;
-            const float sc = e4m3(bs[s]);
-            const u32x4 cw = bc[s];
+            float sc[T];
+            u32x4 cw[T];
+#pragma unroll
+            for (int q = 0; q < T; ++q) { sc[q] = e4m3(bs[s][q]); cw[q] = bc[s][q]; }
             float p[P], xa[P], xb[P];
             if constexpr (A16) {
                 uint32_t xc[P];
 #pragma unroll
                 for (int r = 0; r < P; ++r) xc[r] = bx16[s][r];
                 load(s, i + D);
-                { float w[8]; decode8(cw[0], w); Chain<P>::head_bf16(w, xc, xa, xb, p); }
+                { float w[8]; decode8(cw[0][0], w); Chain<P>::head_bf16(w, xc, xa, xb, p); }
             } else {
 #pragma unroll
                 for (int r = 0; r < P; ++r) { xa[r] = bx[s][r].x; xb[r] = bx[s][r].y; }
                 load(s, i + D);
-                { float w[8]; decode8(cw[0], w); Chain<P>::head_f32(w, xa, xb, p); }
+                { float w[8]; decode8(cw[0][0], w); Chain<P>::head_f32(w, xa, xb, p); }
             }
-            { float w[8]; decode8(cw[1], w); Chain<P>::tail1(w, xa, xb, p); }
-            { float w[8]; decode8(cw[2], w); Chain<P>::tail2(w, xa, xb, p); }
-            { float w[8]; decode8(cw[3], w); Chain<P>::tail3(w, xa, xb, p); }
             const bool valid = leaf + 8 * i < G;
 #pragma unroll
-            for (int r = 0; r < P; ++r) {
-                const float v = __builtin_fmaf(p[r], sc, acc[r]);
-                acc[r] = valid ? v : acc[r];
+            for (int q = 0; q < T; ++q) {
+                if (q > 0) { float w[8]; decode8(cw[q][0], w); Chain<P>::head_f32(w, xa, xb, p); }
+                { float w[8]; decode8(cw[q][1], w); Chain<P>::tail1(w, xa, xb, p); }
+                { float w[8]; decode8(cw[q][2], w); Chain<P>::tail2(w, xa, xb, p); }
+                { float w[8]; decode8(cw[q][3], w); Chain<P>::tail3(w, xa, xb, p); }
+#pragma unroll
+                for (int r = 0; r < P; ++r) {
+                    const float v = __builtin_fmaf(p[r], sc[q], acc[q][r]);
+                    acc[q][r] = valid ? v : acc[q][r];
+                }
             }
         }
     }
 
+    // red[tile q][leaf][row][lane]
 #pragma unroll
-    for (int r = 0; r < P; ++r) red[(leaf * P + r) * kTile + lane] = acc[r];
+    for (int q = 0; q < T; ++q)
+#pragma unroll
+        for (int r = 0; r < P; ++r) red[((q * kLeaves + leaf) * P + r) * kTile + lane] = acc[q][r];
     __syncthreads();
     const int t = threadIdx.x;
-    if (t < P * kTile) {
-        const int r = t >> 6, c = t & 63;
-        if (r < real) {
-            const float v = tree8(red + r * kTile + c, P * kTile);
-            out[(size_t)entry[first + r] * H + (size_t)tile * kTile + c] = v;
+#pragma unroll
+    for (int q = 0; q < T; ++q) {
+        if (t < P * kTile) {
+            const int r = t >> 6, c = t & 63;
+            if (r < real) {
+                const float v = tree8(red + (q * kLeaves * P + r) * kTile + c, P * kTile);
+                out[(size_t)entry[first + r] * H + (size_t)(tile0 + q) * kTile + c] = v;
+            }
         }
     }
     __syncthreads();
 }
 
-template <bool A16>
+// Down passes: work item = (pass, T consecutive output tiles).
+template <bool A16, int T>
 __global__ __launch_bounds__(512, 4) void down_kernel(const xp_expert* __restrict__ experts,
                                                       const void* __restrict__ act,
                                                       const int32_t* __restrict__ hdr,
                                                       const int32_t* __restrict__ entry,
                                                       const int4* __restrict__ passes, int E, int H, int I,
                                                       float* __restrict__ out) {
-    __shared__ float red[kLeaves * kMaxPass * kTile];
+    __shared__ float red[T * kLeaves * kMaxPass * kTile];
     const xp_expert* tab = experts;
-    const int n_tiles = H / kTile;
-    const int n_items = hdr[1] * n_tiles;
+    const int n_items_pass = H / (kTile * T);
+    const int n_items = hdr[1] * n_items_pass;
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-        const int pass = item / n_tiles;
-        const int tile = item - pass * n_tiles;
+        const int pass = item / n_items_pass;
+        const int tile = item - pass * n_items_pass;
         const int4 ps = passes[pass];
         switch (ps.w) {
-            case 1: dn_item<1, A16>(tab, act, entry, ps, tile, H, I, out, red); break;
-            case 2: dn_item<2, A16>(tab, act, entry, ps, tile, H, I, out, red); break;
-            case 3: dn_item<3, A16>(tab, act, entry, ps, tile, H, I, out, red); break;
-            case 4: dn_item<4, A16>(tab, act, entry, ps, tile, H, I, out, red); break;
-            case 5: dn_item<5, A16>(tab, act, entry, ps, tile, H, I, out, red); break;
-            case 6: dn_item<6, A16>(tab, act, entry, ps, tile, H, I, out, red); break;
-            case 7: dn_item<7, A16>(tab, act, entry, ps, tile, H, I, out, red); break;
-            case 8: dn_item<8, A16>(tab, act, entry, ps, tile, H, I, out, red); break;
+            case 1: dn_item<1, A16, T>(tab, act, entry, ps, tile, H, I, out, red); break;
+            case 2: dn_item<2, A16, T>(tab, act, entry, ps, tile, H, I, out, red); break;
+            case 3: dn_item<3, A16, T>(tab, act, entry, ps, tile, H, I, out, red); break;
+            case 4: dn_item<4, A16, T>(tab, act, entry, ps, tile, H, I, out, red); break;
+            case 5: dn_item<5, A16, T>(tab, act, entry, ps, tile, H, I, out, red); break;
+            case 6: dn_item<6, A16, T>(tab, act, entry, ps, tile, H, I, out, red); break;
+            case 7: dn_item<7, A16, T>(tab, act, entry, ps, tile, H, I, out, red); break;
+            case 8: dn_item<8, A16, T>(tab, act, entry, ps, tile, H, I, out, red); break;
             default: break;
         }
     }
@@ -434,6 +458,12 @@ __global__ __launch_bounds__(1024) void down_combine_rows_kernel(
     }
 }
 
+#ifndef XP_DN_TILES
+#define XP_DN_TILES 2
+#endif
+// Down batches pair tiles when they can hold more than this many two-tile items (two per CU).
+constexpr long kPairItems = 512;
+
 // Gate/up batches of at most this many (pass, tile) items (one per CU) run 16-wave workgroups.
 constexpr long kWideItems = 256;
 
@@ -521,13 +551,25 @@ static int down_common(const xp_dims* dims, int32_t rows, const void* act, const
     if (!act || !experts || !workspace || !out) return XP_ERR_NULL;
     if (ws_bytes < ws_layout(dims, rows).total) return XP_ERR_WORKSPACE;
     Plan pl = plan_view(workspace, dims, rows);
-    const int grid = grid_for(rows, dims->top_k, dims->hidden / kTile);
-    if (a16)
-        hipLaunchKernelGGL(down_kernel<true>, dim3(grid), dim3(512), 0, (hipStream_t)stream, experts, act, pl.hdr,
-                           pl.entry, pl.dn_pass, dims->n_experts, dims->hidden, dims->inter, out);
+    const int n_tiles = dims->hidden / kTile;
+    const int grid = grid_for(rows, dims->top_k, n_tiles);
+    // two tiles per item where the tiles pair up and the pairs can still give
+    // every CU two workgroups (XP_DN_TILES=1 forces one tile)
+    const bool pair = XP_DN_TILES == 2 && n_tiles % 2 == 0 && (long)rows * dims->top_k * (n_tiles / 2) > kPairItems;
+    hipStream_t s = (hipStream_t)stream;
+    const int E = dims->n_experts, H = dims->hidden, I = dims->inter;
+    if (a16 && pair)
+        hipLaunchKernelGGL((down_kernel<true, 2>), dim3(grid), dim3(512), 0, s, experts, act, pl.hdr, pl.entry,
+                           pl.dn_pass, E, H, I, out);
+    else if (a16)
+        hipLaunchKernelGGL((down_kernel<true, 1>), dim3(grid), dim3(512), 0, s, experts, act, pl.hdr, pl.entry,
+                           pl.dn_pass, E, H, I, out);
+    else if (pair)
+        hipLaunchKernelGGL((down_kernel<false, 2>), dim3(grid), dim3(512), 0, s, experts, act, pl.hdr, pl.entry,
+                           pl.dn_pass, E, H, I, out);
     else
-        hipLaunchKernelGGL(down_kernel<false>, dim3(grid), dim3(512), 0, (hipStream_t)stream, experts, act, pl.hdr,
-                           pl.entry, pl.dn_pass, dims->n_experts, dims->hidden, dims->inter, out);
+        hipLaunchKernelGGL((down_kernel<false, 1>), dim3(grid), dim3(512), 0, s, experts, act, pl.hdr, pl.entry,
+                           pl.dn_pass, E, H, I, out);
     return launch_status();
 }
 
