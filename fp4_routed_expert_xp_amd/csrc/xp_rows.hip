@@ -96,6 +96,86 @@ __global__ __launch_bounds__(1024) void gateup_one_row_kernel(const xp_expert* _
     gu_item<1, kActF32>(experts, x, nullptr, s_entry, make_int4(s_pick, 0, 1, 1), tile, H, I, k, act, nullptr, red);
 }
 
+// ------------------------------------------------- few-row route + gate/up
+// Routing, plan and gate/up for 2..64 rows in one launch. Every workgroup
+// routes the whole batch itself (topk_row per row, then plan_block, the
+// routing kernel's routines) into LDS and runs its (pass, tile) items from
+// that plan, so no workgroup waits on another; workgroup 0 also publishes what
+// xp_route_bucket writes: top-k ids and weights, counts, offsets, entries, both
+// pass lists and the header. The plan is a pure function of the logits, so
+// every workgroup's copy is the same. The routing scratch (masks, picks,
+// counts, offsets) lives in the leaf buffer, which is free until the items
+// start. Needs E <= 64 * WAVES (one thread per expert in plan_block).
+constexpr int kRouteFusedEntries = kSmallRows * kMaxTopK;   // rows * k
+// Every workgroup routes the batch before its first item, which delays every
+// item when all workgroups have one: sixteen release-width rows (4096
+// workgroups) took 200 us this way against 157 us with the routing launch; four
+// (1024) gained 1.4 us. So the launch is kept to batches whose grid (one
+// workgroup per possible item) stays this small.
+#ifndef XP_ROUTE_FUSED_GRID
+#define XP_ROUTE_FUSED_GRID 1024
+#endif
+
+template <int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 16 / WAVES) void route_gateup_rows_kernel(
+    const xp_expert* __restrict__ experts, const uint16_t* __restrict__ x, RouteIn ri, int R, int H, int I, int k,
+    Tiers T, float* __restrict__ act) {
+    __shared__ __align__(16) float red[2 * kLeaves * kMaxPass * kTile];
+    __shared__ int4 sgu[kRouteFusedEntries];
+    __shared__ int32_t sentry[kRouteFusedEntries];
+    __shared__ int wsum[48];
+    __shared__ int s_ngu;
+    // routing scratch inside red: masks, picks, counts, offsets (20 KiB of 32)
+    unsigned long long* smask = (unsigned long long*)red;                 // [kMaxExperts]
+    int32_t* sid = (int32_t*)(smask + kMaxExperts);                       // [kSmallRows][kMaxTopK]
+    int32_t* scnt = sid + kSmallRows * kMaxTopK;                          // [kMaxExperts]
+    int32_t* soff = scnt + kMaxExperts;                                   // [kMaxExperts + 1]
+    const int E = ri.E;
+    const bool pub = blockIdx.x == 0;
+    const int t = threadIdx.x;
+    for (int e = t; e < E; e += blockDim.x) smask[e] = 0ull;
+    __syncthreads();
+    const int wave = t >> 6;
+    for (int r = wave; r < R; r += WAVES)
+        topk_row(ri.logits, E, k, r, r, pub ? ri.topk_id : nullptr, ri.topk_w, sid + r * kMaxTopK, smask);
+    __syncthreads();
+    for (int e = t; e < E; e += blockDim.x) scnt[e] = __popcll(smask[e]);
+    __syncthreads();
+    plan_block(E, scnt, T, soff, sgu, pub ? ri.w.dn_pass : nullptr, pub ? ri.w.count : nullptr,
+               pub ? ri.w.offset : nullptr, pub ? ri.w.hdr : nullptr, &s_ngu, wsum);
+    __syncthreads();
+    for (int i = t; i < R * k; i += blockDim.x) {
+        const int r = i / k, j = i - r * k;
+        const int e = sid[r * kMaxTopK + j];
+        const unsigned long long below = (r == 0) ? 0ull : (smask[e] & ((1ull << r) - 1ull));
+        const int at = soff[e] + __popcll(below);
+        sentry[at] = i;
+        if (pub) ri.w.entry[at] = i;
+    }
+    const int n_gu = s_ngu;
+    if (pub)
+        for (int i = t; i < n_gu; i += blockDim.x) ri.w.gu_pass[i] = sgu[i];
+    __syncthreads();   // the plan is complete; red is the leaf buffer from here on
+    const int n_tiles = I / kTile;
+    const int n_items = n_gu * n_tiles;
+    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+        const int pass = item / n_tiles;
+        const int tile = item - pass * n_tiles;
+        const int4 ps = sgu[pass];
+        switch (ps.w) {
+            case 1: gu_item<1, kActF32, false, WAVES>(experts, x, nullptr, sentry, ps, tile, H, I, k, act, nullptr, red); break;
+            case 2: gu_item<2, kActF32, false, WAVES>(experts, x, nullptr, sentry, ps, tile, H, I, k, act, nullptr, red); break;
+            case 3: gu_item<3, kActF32, false, WAVES>(experts, x, nullptr, sentry, ps, tile, H, I, k, act, nullptr, red); break;
+            case 4: gu_item<4, kActF32, false, WAVES>(experts, x, nullptr, sentry, ps, tile, H, I, k, act, nullptr, red); break;
+            case 5: gu_item<5, kActF32, false, WAVES>(experts, x, nullptr, sentry, ps, tile, H, I, k, act, nullptr, red); break;
+            case 6: gu_item<6, kActF32, false, WAVES>(experts, x, nullptr, sentry, ps, tile, H, I, k, act, nullptr, red); break;
+            case 7: gu_item<7, kActF32, false, WAVES>(experts, x, nullptr, sentry, ps, tile, H, I, k, act, nullptr, red); break;
+            case 8: gu_item<8, kActF32, false, WAVES>(experts, x, nullptr, sentry, ps, tile, H, I, k, act, nullptr, red); break;
+            default: break;
+        }
+    }
+}
+
 // A16: act is bf16 (the bf16-storage variant); its pairs reach the chain as
 // gate/up's x does (one dword of two bf16 per lane of each row of 16).
 // T: output tiles per item (1, or 2: tiles 2*tile and 2*tile+1). With two, each
@@ -592,14 +672,29 @@ XP_API int xp_route_gateup(const xp_dims* dims, int32_t rows, const float* logit
     if (rows == 0) return XP_OK;
     if (!logits || !x || !experts || !topk_id || !topk_w || !workspace || !act) return XP_ERR_NULL;
     if (ws_bytes < ws_layout(dims, rows).total) return XP_ERR_WORKSPACE;
+    WsPtrs w = ws_ptrs(workspace, dims, rows);
+    RouteIn ri{logits, dims->n_experts, topk_id, topk_w, w};
     if (rows > 1) {
+        const int n_tiles = dims->inter / kTile;
+        const bool wide = (long)rows * dims->top_k * n_tiles <= kWideItems;
+        const int threads = wide ? 1024 : 512;
+        const int grid = grid_for(rows, dims->top_k, n_tiles);
+        if (rows <= kSmallRows && dims->n_experts <= threads && grid <= XP_ROUTE_FUSED_GRID) {
+            // routing inside the gate/up launch
+            const Tiers T = current_tiers();
+            if (wide)
+                hipLaunchKernelGGL(route_gateup_rows_kernel<16>, dim3(grid), dim3(1024), 0, (hipStream_t)stream,
+                                   experts, x, ri, rows, dims->hidden, dims->inter, dims->top_k, T, act);
+            else
+                hipLaunchKernelGGL(route_gateup_rows_kernel<8>, dim3(grid), dim3(512), 0, (hipStream_t)stream,
+                                   experts, x, ri, rows, dims->hidden, dims->inter, dims->top_k, T, act);
+            return launch_status();
+        }
         // the routing launch, then gate/up over the published plan
         st = xp_route_bucket(dims, rows, logits, topk_id, topk_w, workspace, ws_bytes, stream);
         if (st != XP_OK) return st;
         return xp_gateup_rows(dims, rows, x, experts, workspace, ws_bytes, act, stream);
     }
-    WsPtrs w = ws_ptrs(workspace, dims, rows);
-    RouteIn ri{logits, dims->n_experts, topk_id, topk_w, w};
     const int grid = dims->top_k * (dims->inter / kTile);
     hipLaunchKernelGGL(gateup_one_row_kernel, dim3(grid), dim3(1024), 0, (hipStream_t)stream, experts, x, ri,
                        dims->hidden, dims->inter, dims->top_k, act);

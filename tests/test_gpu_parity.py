@@ -19,7 +19,7 @@ import oracle
 import synth
 from fp4_routed_expert_xp_amd import xp
 
-from gpu_helpers import DeviceLayer, bits, log, rel_err_rows, run_fused, run_path, same_class, to_dev
+from gpu_helpers import DeviceLayer, bits, log, read_plan, rel_err_rows, run_fused, run_path, same_class, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -233,11 +233,13 @@ def maxed_layer():
     return DeviceLayer(MAXED, 0)
 
 
-@pytest.mark.parametrize("R", [1, 5, 70])
+@pytest.mark.parametrize("R", [1, 5, 64, 70])
 def test_largest_experts_and_topk(maxed_layer, R):
     """E = 1024 and k = 16 (the ABI's limits), H = 128 (leaves 4-7 of gate/up hold
     no group and contribute +0), through both the single-workgroup (R <= 64) and
-    the block routing (R > 64); the two-call path gives the same bits."""
+    the block routing (R > 64); the two-call path gives the same bits and
+    publishes the same plan (R = 64: 1024 entries, the most that the routing
+    inside the gate/up launch holds)."""
     log("maxed R=%d" % R)
     x = synth.activations(MAXED.seed, R, R, MAXED.H)
     lg = synth.logits(MAXED.seed, R, R, MAXED.E)
@@ -248,6 +250,10 @@ def test_largest_experts_and_topk(maxed_layer, R):
     fused = run_fused(maxed_layer, x, lg)
     for n in ("topk_w", "act", "out", "y"):
         assert np.array_equal(bits(res[n]), bits(fused[n])), n
+    assert np.array_equal(res["topk_id"], fused["topk_id"])
+    pa, pb = read_plan(maxed_layer.d, R, res["ws"]), read_plan(maxed_layer.d, R, fused["ws"])
+    for n in ("n_gu", "n_dn", "count", "offset", "entry", "gu", "dn"):
+        assert np.array_equal(pa[n], pb[n]), n
 
 
 @pytest.mark.parametrize("R", [1, 5, 16])
