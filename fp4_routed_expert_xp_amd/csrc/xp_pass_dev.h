@@ -88,9 +88,10 @@ __device__ __forceinline__ float e8m0(uint32_t b) {
 
 // One leaf of one matrix (gate or up) for one (pass, tile): returns the P leaf
 // values of this lane's column. The leaf's groups are g = leaf, leaf+8, ...;
-// every leaf walks ceil(G/8) of them so the loop body has no branches (the
-// ring's wait counts then follow it exactly): a group past the end re-reads
-// group G-1 and its product is discarded by a select.
+// every leaf walks ceil(G/8) of them, rounded up to whole loop trips of 2*D
+// groups, so the loop body has no branches (the ring's wait counts then follow
+// it exactly): a group past the end re-reads group G-1 and its product is
+// discarded by a select.
 // Activations: bf16 rows (xr[r] = the row's 16-bit pairs), or, when CODED,
 // E4M3FN codes (xr[r] = the row's code bytes, read as pairs) with one E8M0
 // scale per group (sr[r] = the row's scale bytes); a coded value enters the
@@ -104,48 +105,47 @@ __device__ __forceinline__ void gu_leaf(gcodes_t cc, gbytes_t ss, const uint32_t
     const int ng = (G + 7) >> 3;
 #pragma unroll
     for (int r = 0; r < P; ++r) acc[r] = 0.0f;
-    u32x4 bc[D];
-    uint32_t bs[D];
-    uint32_t bx[D][P];
-    uint32_t bsx[D][P];
-    auto load = [&](int s, int i) {
+    // Two register sets of D groups (see gu_leaf2).
+    u32x4 bc[2][D];
+    uint32_t bs[2][D];
+    uint32_t bx[2][D][P];
+    uint32_t bsx[2][D][P];
+    auto load = [&](int set, int s, int i) {
         const int g = min(leaf + 8 * i, G - 1);
-        bc[s] = load_codes(cc + (size_t)g * kTile);
-        bs[s] = ss[(size_t)g * kTile];
+        bc[set][s] = load_codes(cc + (size_t)g * kTile);
+        bs[set][s] = ss[(size_t)g * kTile];
 #pragma unroll
         for (int r = 0; r < P; ++r) {
             if constexpr (CODED) {
-                bx[s][r] = ((const uint16_t*)xr[r])[16 * g + xl];
-                bsx[s][r] = sr[r][g];
+                bx[set][s][r] = ((const uint16_t*)xr[r])[16 * g + xl];
+                bsx[set][s][r] = sr[r][g];
             } else {
-                bx[s][r] = xr[r][16 * g + xl];
+                bx[set][s][r] = xr[r][16 * g + xl];
             }
         }
     };
-#pragma unroll
-    for (int s = 0; s < D; ++s) load(s, s);
-    for (int i0 = 0; i0 < ng; i0 += D) {
+    auto half = [&](int set, int i0) {
 #pragma unroll
         for (int s = 0; s < D; ++s) {
             const int i = i0 + s;
-            const float sc = e4m3(bs[s]);
+            const float sc = e4m3(bs[set][s]);
             float p[P], xa[P], xb[P];
-            const u32x4 cw = bc[s];
+            const u32x4 cw = bc[set][s];
             if constexpr (CODED) {
 #pragma unroll
                 for (int r = 0; r < P; ++r) {
-                    const f32x2 v = __builtin_amdgcn_cvt_pk_f32_fp8((int)bx[s][r], false);
-                    const float sx = e8m0(bsx[s][r]);
+                    const f32x2 v = __builtin_amdgcn_cvt_pk_f32_fp8((int)bx[set][s][r], false);
+                    const float sx = e8m0(bsx[set][s][r]);
                     xa[r] = v.x * sx;
                     xb[r] = v.y * sx;
                 }
-                load(s, i + D);
+                load(set ^ 1, s, i + D);
                 { float w[8]; decode8(cw[0], w); Chain<P>::head_f32(w, xa, xb, p); }
             } else {
                 uint32_t xc[P];
 #pragma unroll
-                for (int r = 0; r < P; ++r) xc[r] = bx[s][r];
-                load(s, i + D);
+                for (int r = 0; r < P; ++r) xc[r] = bx[set][s][r];
+                load(set ^ 1, s, i + D);
                 { float w[8]; decode8(cw[0], w); Chain<P>::head_bf16(w, xc, xa, xb, p); }
             }
             { float w[8]; decode8(cw[1], w); Chain<P>::tail1(w, xa, xb, p); }
@@ -158,6 +158,12 @@ __device__ __forceinline__ void gu_leaf(gcodes_t cc, gbytes_t ss, const uint32_t
                 acc[r] = valid ? v : acc[r];
             }
         }
+    };
+#pragma unroll
+    for (int s = 0; s < D; ++s) load(0, s, s);
+    for (int i0 = 0; i0 < ng; i0 += 2 * D) {
+        half(0, i0);
+        half(1, i0 + D);
     }
 }
 
@@ -175,50 +181,53 @@ __device__ __forceinline__ void gu_leaf2(gcodes_t cg, gbytes_t sg, gcodes_t cu, 
     const int ng = (G + 7) >> 3;
 #pragma unroll
     for (int r = 0; r < P; ++r) accg[r] = accu[r] = 0.0f;
-    u32x4 bg[D], bu[D];
-    uint32_t bsg[D], bsu[D];
-    uint32_t bx[D][P];
-    uint32_t bsx[D][P];
-    auto load = [&](int s, int i) {
+    // Two register sets of D groups: while the groups of one set are consumed,
+    // the loads of the next D groups fill the other, so a load never targets a
+    // register still in use and nothing is copied (or waited for) at the loop's
+    // back edge; D groups stay in flight throughout.
+    u32x4 bg[2][D], bu[2][D];
+    uint32_t bsg[2][D], bsu[2][D];
+    uint32_t bx[2][D][P];
+    uint32_t bsx[2][D][P];
+    auto load = [&](int set, int s, int i) {
         const int g = min(leaf + 8 * i, G - 1);
-        bg[s] = load_codes(cg + (size_t)g * kTile);
-        bu[s] = load_codes(cu + (size_t)g * kTile);
-        bsg[s] = sg[(size_t)g * kTile];
-        bsu[s] = su[(size_t)g * kTile];
+        bg[set][s] = load_codes(cg + (size_t)g * kTile);
+        bu[set][s] = load_codes(cu + (size_t)g * kTile);
+        bsg[set][s] = sg[(size_t)g * kTile];
+        bsu[set][s] = su[(size_t)g * kTile];
 #pragma unroll
         for (int r = 0; r < P; ++r) {
             if constexpr (CODED) {
-                bx[s][r] = ((const uint16_t*)xr[r])[16 * g + xl];
-                bsx[s][r] = sr[r][g];
+                bx[set][s][r] = ((const uint16_t*)xr[r])[16 * g + xl];
+                bsx[set][s][r] = sr[r][g];
             } else {
-                bx[s][r] = xr[r][16 * g + xl];
+                bx[set][s][r] = xr[r][16 * g + xl];
             }
         }
     };
-#pragma unroll
-    for (int s = 0; s < D; ++s) load(s, s);
-    for (int i0 = 0; i0 < ng; i0 += D) {
+    // Consume set `set` (groups i0 .. i0+D-1), loading groups i0+D .. into the other.
+    auto half = [&](int set, int i0) {
 #pragma unroll
         for (int s = 0; s < D; ++s) {
             const int i = i0 + s;
-            const float scg = e4m3(bsg[s]), scu = e4m3(bsu[s]);
-            const u32x4 cwg = bg[s], cwu = bu[s];
+            const float scg = e4m3(bsg[set][s]), scu = e4m3(bsu[set][s]);
+            const u32x4 cwg = bg[set][s], cwu = bu[set][s];
             float p[P], xa[P], xb[P];
             if constexpr (CODED) {
 #pragma unroll
                 for (int r = 0; r < P; ++r) {
-                    const f32x2 v = __builtin_amdgcn_cvt_pk_f32_fp8((int)bx[s][r], false);
-                    const float sx = e8m0(bsx[s][r]);
+                    const f32x2 v = __builtin_amdgcn_cvt_pk_f32_fp8((int)bx[set][s][r], false);
+                    const float sx = e8m0(bsx[set][s][r]);
                     xa[r] = v.x * sx;
                     xb[r] = v.y * sx;
                 }
-                load(s, i + D);
+                load(set ^ 1, s, i + D);
                 { float w[8]; decode8(cwg[0], w); Chain<P>::head_f32(w, xa, xb, p); }
             } else {
                 uint32_t xc[P];
 #pragma unroll
-                for (int r = 0; r < P; ++r) xc[r] = bx[s][r];
-                load(s, i + D);
+                for (int r = 0; r < P; ++r) xc[r] = bx[set][s][r];
+                load(set ^ 1, s, i + D);
                 { float w[8]; decode8(cwg[0], w); Chain<P>::head_bf16(w, xc, xa, xb, p); }
             }
             { float w[8]; decode8(cwg[1], w); Chain<P>::tail1(w, xa, xb, p); }
@@ -240,6 +249,12 @@ __device__ __forceinline__ void gu_leaf2(gcodes_t cg, gbytes_t sg, gcodes_t cu, 
                 accu[r] = valid ? v : accu[r];
             }
         }
+    };
+#pragma unroll
+    for (int s = 0; s < D; ++s) load(0, s, s);
+    for (int i0 = 0; i0 < ng; i0 += 2 * D) {
+        half(0, i0);
+        half(1, i0 + D);
     }
 }
 

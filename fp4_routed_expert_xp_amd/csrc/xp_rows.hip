@@ -216,46 +216,45 @@ __device__ __forceinline__ void dn_item(const xp_expert* __restrict__ experts, c
     for (int q = 0; q < T; ++q)
 #pragma unroll
         for (int r = 0; r < P; ++r) acc[q][r] = 0.0f;
-    u32x4 bc[D][T];
-    uint32_t bs[D][T];
-    float2 bx[D][P];
-    uint32_t bx16[D][P];
-    auto load = [&](int s, int i) {
+    // Two register sets of D groups (see gu_leaf2).
+    u32x4 bc[2][D][T];
+    uint32_t bs[2][D][T];
+    float2 bx[2][D][P];
+    uint32_t bx16[2][D][P];
+    auto load = [&](int set, int s, int i) {
         const int g = min(leaf + 8 * i, G - 1);
 #pragma unroll
         for (int q = 0; q < T; ++q) {
-            bc[s][q] = load_codes(cc + q * tile_step + (size_t)g * kTile);
-            bs[s][q] = ss[q * tile_step + (size_t)g * kTile];
+            bc[set][s][q] = load_codes(cc + q * tile_step + (size_t)g * kTile);
+            bs[set][s][q] = ss[q * tile_step + (size_t)g * kTile];
         }
 #pragma unroll
         for (int r = 0; r < P; ++r) {
             if constexpr (A16)
-                bx16[s][r] = ar16[r][16 * g + (lane & 15)];
+                bx16[set][s][r] = ar16[r][16 * g + (lane & 15)];
             else
-                bx[s][r] = *(const float2*)(ar[r] + 32 * g + xl);
+                bx[set][s][r] = *(const float2*)(ar[r] + 32 * g + xl);
         }
     };
-#pragma unroll
-    for (int s = 0; s < D; ++s) load(s, s);
-    for (int i0 = 0; i0 < ng; i0 += D) {
+    auto half = [&](int set, int i0) {
 #pragma unroll
         for (int s = 0; s < D; ++s) {
             const int i = i0 + s;
             float sc[T];
             u32x4 cw[T];
 #pragma unroll
-            for (int q = 0; q < T; ++q) { sc[q] = e4m3(bs[s][q]); cw[q] = bc[s][q]; }
+            for (int q = 0; q < T; ++q) { sc[q] = e4m3(bs[set][s][q]); cw[q] = bc[set][s][q]; }
             float p[P], xa[P], xb[P];
             if constexpr (A16) {
                 uint32_t xc[P];
 #pragma unroll
-                for (int r = 0; r < P; ++r) xc[r] = bx16[s][r];
-                load(s, i + D);
+                for (int r = 0; r < P; ++r) xc[r] = bx16[set][s][r];
+                load(set ^ 1, s, i + D);
                 { float w[8]; decode8(cw[0][0], w); Chain<P>::head_bf16(w, xc, xa, xb, p); }
             } else {
 #pragma unroll
-                for (int r = 0; r < P; ++r) { xa[r] = bx[s][r].x; xb[r] = bx[s][r].y; }
-                load(s, i + D);
+                for (int r = 0; r < P; ++r) { xa[r] = bx[set][s][r].x; xb[r] = bx[set][s][r].y; }
+                load(set ^ 1, s, i + D);
                 { float w[8]; decode8(cw[0][0], w); Chain<P>::head_f32(w, xa, xb, p); }
             }
             const bool valid = leaf + 8 * i < G;
@@ -272,6 +271,12 @@ __device__ __forceinline__ void dn_item(const xp_expert* __restrict__ experts, c
                 }
             }
         }
+    };
+#pragma unroll
+    for (int s = 0; s < D; ++s) load(0, s, s);
+    for (int i0 = 0; i0 < ng; i0 += 2 * D) {
+        half(0, i0);
+        half(1, i0 + D);
     }
 
     // red[tile q][leaf][row][lane]
@@ -364,25 +369,24 @@ __global__ __launch_bounds__(1024) void down_combine_one_row_kernel(
 
     const int ng = (G + 7) >> 3;
     float acc = 0.0f;
-    u32x4 bc[D];
-    uint32_t bs[D];
-    float2 bx[D];
-    auto load = [&](int s, int i) {
+    // Two register sets of D groups (see gu_leaf2).
+    u32x4 bc[2][D];
+    uint32_t bs[2][D];
+    float2 bx[2][D];
+    auto load = [&](int set, int s, int i) {
         const int g = min(leaf + 8 * i, G - 1);
-        bc[s] = load_codes(cc + (size_t)g * kTile);
-        bs[s] = ss[(size_t)g * kTile];
-        bx[s] = *(const float2*)(ar + 32 * g);
+        bc[set][s] = load_codes(cc + (size_t)g * kTile);
+        bs[set][s] = ss[(size_t)g * kTile];
+        bx[set][s] = *(const float2*)(ar + 32 * g);
     };
-#pragma unroll
-    for (int s = 0; s < D; ++s) load(s, s);
-    for (int i0 = 0; i0 < ng; i0 += D) {
+    auto half = [&](int set, int i0) {
 #pragma unroll
         for (int s = 0; s < D; ++s) {
             const int i = i0 + s;
-            const float sc = e4m3(bs[s]);
-            const u32x4 cw = bc[s];
-            float p[1], xa[1] = {bx[s].x}, xb[1] = {bx[s].y};
-            load(s, i + D);
+            const float sc = e4m3(bs[set][s]);
+            const u32x4 cw = bc[set][s];
+            float p[1], xa[1] = {bx[set][s].x}, xb[1] = {bx[set][s].y};
+            load(set ^ 1, s, i + D);
             { float w[8]; decode8(cw[0], w); Chain<1>::head_f32(w, xa, xb, p); }
             { float w[8]; decode8(cw[1], w); Chain<1>::tail1(w, xa, xb, p); }
             { float w[8]; decode8(cw[2], w); Chain<1>::tail2(w, xa, xb, p); }
@@ -390,6 +394,12 @@ __global__ __launch_bounds__(1024) void down_combine_one_row_kernel(
             const float v = __builtin_fmaf(p[0], sc, acc);
             acc = (leaf + 8 * i < G) ? v : acc;
         }
+    };
+#pragma unroll
+    for (int s = 0; s < D; ++s) load(0, s, s);
+    for (int i0 = 0; i0 < ng; i0 += 2 * D) {
+        half(0, i0);
+        half(1, i0 + D);
     }
     red[wave][lane] = acc;
     __syncthreads();
@@ -444,28 +454,27 @@ __device__ __forceinline__ void dc_pass_leaf(const xp_expert* __restrict__ exper
     float acc[P];
 #pragma unroll
     for (int r = 0; r < P; ++r) acc[r] = 0.0f;
-    u32x4 bc[D];
-    uint32_t bs[D];
-    float2 bx[D][P];
-    auto load = [&](int s, int i) {
+    // Two register sets of D groups (see gu_leaf2).
+    u32x4 bc[2][D];
+    uint32_t bs[2][D];
+    float2 bx[2][D][P];
+    auto load = [&](int set, int s, int i) {
         const int g = min(leaf + 8 * i, G - 1);
-        bc[s] = load_codes(cc + (size_t)g * kTile);
-        bs[s] = ss[(size_t)g * kTile];
+        bc[set][s] = load_codes(cc + (size_t)g * kTile);
+        bs[set][s] = ss[(size_t)g * kTile];
 #pragma unroll
-        for (int r = 0; r < P; ++r) bx[s][r] = *(const float2*)(ar[r] + 32 * g);
+        for (int r = 0; r < P; ++r) bx[set][s][r] = *(const float2*)(ar[r] + 32 * g);
     };
-#pragma unroll
-    for (int s = 0; s < D; ++s) load(s, s);
-    for (int i0 = 0; i0 < ng; i0 += D) {
+    auto half = [&](int set, int i0) {
 #pragma unroll
         for (int s = 0; s < D; ++s) {
             const int i = i0 + s;
-            const float sc = e4m3(bs[s]);
-            const u32x4 cw = bc[s];
+            const float sc = e4m3(bs[set][s]);
+            const u32x4 cw = bc[set][s];
             float p[P], xa[P], xb[P];
 #pragma unroll
-            for (int r = 0; r < P; ++r) { xa[r] = bx[s][r].x; xb[r] = bx[s][r].y; }
-            load(s, i + D);
+            for (int r = 0; r < P; ++r) { xa[r] = bx[set][s][r].x; xb[r] = bx[set][s][r].y; }
+            load(set ^ 1, s, i + D);
             { float w[8]; decode8(cw[0], w); Chain<P>::head_f32(w, xa, xb, p); }
             { float w[8]; decode8(cw[1], w); Chain<P>::tail1(w, xa, xb, p); }
             { float w[8]; decode8(cw[2], w); Chain<P>::tail2(w, xa, xb, p); }
@@ -477,6 +486,12 @@ __device__ __forceinline__ void dc_pass_leaf(const xp_expert* __restrict__ exper
                 acc[r] = valid ? v : acc[r];
             }
         }
+    };
+#pragma unroll
+    for (int s = 0; s < D; ++s) load(0, s, s);
+    for (int i0 = 0; i0 < ng; i0 += 2 * D) {
+        half(0, i0);
+        half(1, i0 + D);
     }
 #pragma unroll
     for (int r = 0; r < P; ++r) red_wave[r * kTile + lane] = acc[r];
