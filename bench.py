@@ -34,17 +34,17 @@ CSRC = os.path.join(ROOT, "fp4_routed_expert_xp_amd", "csrc")
 # workload), from two rocprofv3 --pmc runs: FETCH_SIZE, then WRITE_SIZE, in KiB per
 # dispatch (mean over the dispatches of that workload). Each is scaled by what the
 # same counter read for a plain 2 GiB device-to-device copy: FETCH_SIZE read
-# 1,048,590 KiB for 2,097,152 KiB fetched, WRITE_SIZE read exactly 2,097,152 KiB.
+# 1,048,614.1 KiB for 2,097,152 KiB fetched, WRITE_SIZE read exactly 2,097,152 KiB.
 # The figure belongs to the sources the kernel is built from (their digest below);
 # after any change to them the bench reports traffic as null.
-TRAFFIC = dict(sources="7a76f4fa", fetch_kib=34964.6, write_kib=66.4,
-               fetch_factor=2097152 / 1048590.0, write_factor=1.0)
+TRAFFIC = dict(sources="7b102cd9", fetch_kib=34990.7, write_kib=66.4,
+               fetch_factor=2097152 / 1048614.1, write_factor=1.0)
 ROOFLINE_SOURCES = ("xp_rows.hip", "xp_pass_dev.h", "xp_common.h", "xp_route_dev.h", "xp_chain_asm.h")
 # The same counters for the one-row down + combine launch (down_combine_one_row_kernel).
-DOWN_TRAFFIC = dict(sources="7a76f4fa", fetch_kib=17712.6, write_kib=144.0)
+DOWN_TRAFFIC = dict(sources="7b102cd9", fetch_kib=17725.4, write_kib=144.0)
 # The same for the dense FP8 projection kernel at 4096 x 4096 (grid of 256
 # workgroups; mean over its launches at 1, 8 and 16 rows), tied to xp_fp8.hip.
-FP8_TRAFFIC = dict(sources="fe07a71a", fetch_kib=8525.4, write_kib=133.3)
+FP8_TRAFFIC = dict(sources="15929da9", fetch_kib=8532.4, write_kib=133.3)
 FP8_SOURCES = ("xp_fp8.hip", "xp_common.h")
 
 
