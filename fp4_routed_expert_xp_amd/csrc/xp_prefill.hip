@@ -39,6 +39,21 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4v;
 
 typedef const uint32_t __attribute__((address_space(1)))* gwords_t;
 typedef const uint8_t __attribute__((address_space(1)))* gbytes1_t;
+typedef const void __attribute__((address_space(1)))* gvoid_t;
+typedef void __attribute__((address_space(3)))* lvoid_t;
+
+// Keeps the compiler from moving memory operations across this point, so the
+// vector-memory counts below follow the program order.
+__device__ __forceinline__ void mem_fence_compiler() { asm volatile("" ::: "memory"); }
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt N (bits 3:0 and 15:14), expcnt
+// and, unless LGKM0, lgkmcnt left at their maxima. Issued through the builtin
+// so that the compiler's own wait bookkeeping sees it.
+template <int N, bool LGKM0>
+constexpr int waitcnt_imm() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    return (N & 15) | ((N >> 4) << 14) | (7 << 4) | ((LGKM0 ? 0 : 15) << 8);
+}
 
 // Item bookkeeping shared by both kernels: per-expert blocks of 128 rows and
 // their prefix, rebuilt by each workgroup from the plan's counts.
@@ -180,7 +195,7 @@ __device__ __forceinline__ Deal deal(int total) {
 #define XP_PF_GU_WAVES 2
 #endif
 #ifndef XP_PF_GU_DMAX
-#define XP_PF_GU_DMAX 2
+#define XP_PF_GU_DMAX 4
 #endif
 #ifndef XP_PF_GU_DA
 #define XP_PF_GU_DA 2
@@ -202,17 +217,80 @@ struct GuArgs {
     int k, H, I, G;
 };
 
-template <int NS, int D, int kDA>
-__device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint16_t (*sA)[kPM * kAStride],
-                                        const int* sEntry) {
-    static_assert(kDA % 2 == 0 && D % kDA == 0, "rings hold whole steps of two groups");
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int G = a.G, H = a.H, I = a.I;
+// NS 16-byte LDS reads at addr + s * 1024 (s = 0 .. NS-1), waited for inside
+// the same asm block: the reads follow direct global-to-LDS loads whose
+// completion the kernel orders itself (vmcnt and a barrier), and the compiler,
+// which cannot tell the ring's buffers apart, would otherwise wait for every
+// load in flight before each read.
+template <int NS>
+__device__ __forceinline__ void lds_frags(uint32_t addr, bf16x8 (&af)[NS]) {
+    u32x4v r[8];
+    if constexpr (NS == 2)
+        asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:1024\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(r[0]), "=&v"(r[1]) : "v"(addr) : "memory");
+    else if constexpr (NS == 4)
+        asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:1024\n\t"
+                     "ds_read_b128 %2, %4 offset:2048\n\tds_read_b128 %3, %4 offset:3072\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]) : "v"(addr) : "memory");
+    else if constexpr (NS == 6)
+        asm volatile("ds_read_b128 %0, %6\n\tds_read_b128 %1, %6 offset:1024\n\t"
+                     "ds_read_b128 %2, %6 offset:2048\n\tds_read_b128 %3, %6 offset:3072\n\t"
+                     "ds_read_b128 %4, %6 offset:4096\n\tds_read_b128 %5, %6 offset:5120\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]) : "v"(addr)
+                     : "memory");
+    else
+        asm volatile("ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:1024\n\t"
+                     "ds_read_b128 %2, %8 offset:2048\n\tds_read_b128 %3, %8 offset:3072\n\t"
+                     "ds_read_b128 %4, %8 offset:4096\n\tds_read_b128 %5, %8 offset:5120\n\t"
+                     "ds_read_b128 %6, %8 offset:6144\n\tds_read_b128 %7, %8 offset:7168\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+                       "=&v"(r[7])
+                     : "v"(addr) : "memory");
+#pragma unroll
+    for (int s = 0; s < NS; ++s) af[s] = __builtin_bit_cast(bf16x8, r[s]);
+}
 
-    // Activation rows staged by all threads: row t/2, 16 bf16 at k offset (t&1)*16.
-    const int arow = t >> 1, acol = (t & 1) * 16;
-    const u32x4v* xrow = (const u32x4v*)(a.x + (size_t)(sEntry[arow] / a.k) * H + acol);
-    u32x4v ra[kDA][2];
+// Activation tiles of one 32-wide group: 128 rows x 64 B, no padding; the
+// four 16-byte chunks of row r sit at chunk position c ^ swz(r), swz(r) =
+// ((r >> 1) ^ (r >> 3)) & 3, so a fragment read (16 rows at one chunk) is free
+// of bank conflicts whether the LDS serves 8 lanes a cycle from 32 banks or 16
+// lanes from 64.
+__device__ __forceinline__ int x_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+constexpr int kXTile = kPM * 64;   // bytes per group
+#ifndef XP_PF_GU_NB
+#define XP_PF_GU_NB 4              // LDS activation buffers (groups staged ahead: NB - 1)
+#endif
+
+// The activations arrive by direct global-to-LDS loads: wave w fills rows
+// 32w .. 32w+31 of a group's tile with two 1 KiB loads; lane L of a load writes
+// LDS bytes 16L .. 16L+15 of its 1 KiB, i.e. row L/4 of the 16 and chunk
+// position L%4, so it reads the row's chunk (L%4) ^ swz(L/4).
+// Ordering: each wave issues, per group step, its two activation loads and
+// then its weight loads, with compiler fences between them, so the number of
+// vector-memory operations issued after a given activation load is a constant
+// (kAfter below); before the step's barrier each wave waits until its loads of
+// the next group's tile have landed, and the barrier publishes them.
+template <int NS, int D, int kDA>
+__device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint8_t* sX, const int* sEntry) {
+    constexpr int NB = XP_PF_GU_NB;
+    static_assert(NB >= 3 && NB <= 8, "activation ring");
+    // loads per group step and wave: 2 activation, 8 weight (4 code words, 4 scale bytes)
+    constexpr int kAfter = 8 + 10 * (NB - 2);   // issued after the activation loads of group g+1, at step g's wait
+    static_assert(kAfter <= 63, "vmcnt range");
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int G = a.G, I = a.I;
+
+    // this lane's two activation sources (rows 32w + L/4 and 32w + 16 + L/4)
+    const int lrow = lane >> 2;
+    const int lchunk = (lane & 3) ^ x_swz(lrow);
+    const uint16_t* xa0 = a.x + (size_t)(sEntry[32 * wave + lrow] / a.k) * a.H + lchunk * 8;
+    const uint16_t* xa1 = a.x + (size_t)(sEntry[32 * wave + 16 + lrow] / a.k) * a.H + lchunk * 8;
+    auto dma_x = [&](int g) {
+        const int gc = min(g, G - 1);
+        uint8_t* dst = sX + (size_t)(g % NB) * kXTile + wave * 2048;
+        __builtin_amdgcn_global_load_lds((gvoid_t)(xa0 + gc * 32), (lvoid_t)dst, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gvoid_t)(xa1 + gc * 32), (lvoid_t)(dst + 1024), 16, 0, 0);
+    };
 
     // This wave's columns: packed tile pt, columns c0 .. c0+31 of it. A wave past
     // the last tile (I not a multiple of 128) reads tile 0 and stores nothing.
@@ -239,16 +317,6 @@ __device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint16_
         bs[slot][2] = us[g * 64];
         bs[slot][3] = us[g * 64 + 16];
     };
-    auto load_a = [&](int slot, int g) {
-        g = min(g, G - 1);
-        ra[slot][0] = xrow[4 * g];
-        ra[slot][1] = xrow[4 * g + 1];
-    };
-    auto store_a = [&](int buf, int slot, int half) {  // half: which group of the buffer's two
-        u32x4v* q = (u32x4v*)(&sA[buf][arow * kAStride + half * 32 + acol]);
-        q[0] = ra[slot][0];
-        q[1] = ra[slot][1];
-    };
     bf16x8 bf[2][4];
     auto decode_b = [&](int buf, int slot) {
         if (wave_scales_pow2(bs[slot][0], bs[slot][1], bs[slot][2], bs[slot][3])) {
@@ -259,6 +327,9 @@ __device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint16_
             for (int q = 0; q < 4; ++q) bf[buf][q] = decode8(bc[slot][q], e4m3f(bs[slot][q]));
         }
     };
+    // fragment reads: row 16s + (lane & 15), chunk `word`, at its swizzled position
+    const int frag_off = (lane & 15) * 64 + ((word ^ x_swz(lane & 15)) * 16);
+    const uint32_t x_lds = (uint32_t)(size_t)(lvoid_t)sX + frag_off;   // LDS byte address
 
     f32x4 acc[NS][2][2];
 #pragma unroll
@@ -269,16 +340,19 @@ __device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint16_
             acc[s][c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 
+    // prologue: activation tiles of groups 0 .. NB-2, weights of groups 0 .. D-1
+#pragma unroll
+    for (int g = 0; g < NB - 1; ++g) {
+        dma_x(g);
+        mem_fence_compiler();
+    }
 #pragma unroll
     for (int u = 0; u < D; ++u) load_b(u, u);
-#pragma unroll
-    for (int u = 0; u < kDA; ++u) load_a(u, u);
-    store_a(0, 0, 0);
-    store_a(0, 1, 1);
-    load_a(0, kDA);
-    load_a(1, kDA + 1);
+    mem_fence_compiler();
     decode_b(0, 0);
     load_b(0, D);
+    mem_fence_compiler();
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm<0, true>());
     __syncthreads();
 
     for (int g0 = 0; g0 < G; g0 += D) {
@@ -286,11 +360,12 @@ __device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint16_
         for (int u = 0; u < D; ++u) {
             const int g = g0 + u;
             const int cur = u & 1;
-            const int buf = (g >> 1) & 1;  // LDS buffers hold two groups each
-            const uint16_t* a_lds = &sA[buf][(lane & 15) * kAStride + cur * 32 + word * 8];
+            // the tile of group g + NB - 1 into the buffer group g - 1 used (all
+            // waves finished reading it before the last barrier)
+            dma_x(g + NB - 1);
+            mem_fence_compiler();
             bf16x8 af[NS];
-#pragma unroll
-            for (int s = 0; s < NS; ++s) af[s] = *(const bf16x8*)(a_lds + s * 16 * kAStride);
+            lds_frags<NS>(x_lds + (uint32_t)((g % NB) * kXTile), af);
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
                 acc[s][0][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s], bf[cur][0], acc[s][0][0], 0, 0, 0);
@@ -301,18 +376,20 @@ __device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint16_
             // next group's weights: decode now (overlaps the matrix work), refill the ring
             const int nslot = (u + 1) % D;
             decode_b(cur ^ 1, nslot);
+            mem_fence_compiler();
             load_b(nslot, g + 1 + D);
-            if (u & 1) {
-                // the next two groups' activations into the other LDS buffer, refill the ring
-                const int s0 = (u + 1) % kDA, s1 = (u + 2) % kDA;
-                store_a(buf ^ 1, s0, 0);
-                store_a(buf ^ 1, s1, 1);
-                load_a(s0, g + 1 + kDA);
-                load_a(s1, g + 2 + kDA);
-                __syncthreads();
-            }
+            mem_fence_compiler();
+            // this wave's loads of group g+1's tile have landed and its reads of
+            // buffer g % NB are done; the barrier publishes every wave's. (A
+            // plain barrier: __syncthreads' release fence would wait for every
+            // load in flight.)
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm<kAfter, true>());
+            __builtin_amdgcn_s_barrier();
+            mem_fence_compiler();
         }
     }
+    // no load of this item may still be in flight into the buffers
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm<0, false>());
 
     if (live) {
 #pragma unroll
@@ -359,10 +436,10 @@ __device__ __forceinline__ void dispatch_item(int rows, int G, F&& f) {
 struct GuRun {
     const GuArgs& a;
     const Item& it;
-    uint16_t (*sA)[kPM * kAStride];
+    uint8_t* sX;
     const int* sEntry;
     template <int NS, int D>
-    __device__ __forceinline__ void run() const { gu_item<NS, D, XP_PF_GU_DA>(a, it, sA, sEntry); }
+    __device__ __forceinline__ void run() const { gu_item<NS, D, XP_PF_GU_DA>(a, it, sX, sEntry); }
 };
 
 // act[entry][n] = silu(g) * u for the item's rows and columns, where g and u
@@ -371,7 +448,7 @@ __global__ __launch_bounds__(kPThreads, XP_PF_GU_WAVES) void prefill_gateup_kern
     const xp_expert* __restrict__ experts, const uint16_t* __restrict__ x, const int32_t* __restrict__ count,
     const int32_t* __restrict__ offset, const int32_t* __restrict__ entry, int E, int k, int H, int I,
     float* __restrict__ act) {
-    __shared__ __attribute__((aligned(16))) uint16_t sA[2][kPM * kAStride];
+    __shared__ __attribute__((aligned(1024))) uint8_t sX[XP_PF_GU_NB * kXTile];
     __shared__ int sEntry[kPM];
     __shared__ int sP[kMaxExperts + 1];
     __shared__ int swave[4];
@@ -386,7 +463,7 @@ __global__ __launch_bounds__(kPThreads, XP_PF_GU_WAVES) void prefill_gateup_kern
         const Item it = item_at(i, n_tiles, sP, E, count);
         if (t < kPM) sEntry[t] = entry[offset[it.e] + it.m0 + min(t, it.rows - 1)];
         __syncthreads();
-        dispatch_item<XP_PF_GU_DMAX>(it.rows, a.G, GuRun{a, it, sA, sEntry});
+        dispatch_item<XP_PF_GU_DMAX>(it.rows, a.G, GuRun{a, it, sX, sEntry});
         __syncthreads();  // sEntry and sA are rewritten by the next item
     }
 }
