@@ -256,75 +256,96 @@ __device__ __forceinline__ void lds_frags(uint32_t addr, bf16x8 (&af)[NS]) {
 // of bank conflicts whether the LDS serves 8 lanes a cycle from 32 banks or 16
 // lanes from 64.
 __device__ __forceinline__ int x_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
-constexpr int kXTile = kPM * 64;   // bytes per group
+constexpr int kXTile = kPM * 64;   // activation bytes per group
+constexpr int kWTile = 4 * 1024;   // weight code bytes per group: (matrix, packed tile) x 64 columns x 16 B
+constexpr int kSTile = 4 * 64;     // scale bytes per group: (matrix, packed tile) x 64 columns
 #ifndef XP_PF_GU_NB
-#define XP_PF_GU_NB 4              // LDS activation buffers (groups staged ahead: NB - 1)
+#define XP_PF_GU_NB 4              // LDS buffers per ring (groups staged ahead: NB - 1)
 #endif
 
-// The activations arrive by direct global-to-LDS loads: wave w fills rows
-// 32w .. 32w+31 of a group's tile with two 1 KiB loads; lane L of a load writes
-// LDS bytes 16L .. 16L+15 of its 1 KiB, i.e. row L/4 of the 16 and chunk
-// position L%4, so it reads the row's chunk (L%4) ^ swz(L/4).
-// Ordering: each wave issues, per group step, its two activation loads and
-// then its weight loads, with compiler fences between them, so the number of
-// vector-memory operations issued after a given activation load is a constant
-// (kAfter below); before the step's barrier each wave waits until its loads of
-// the next group's tile have landed, and the barrier publishes them.
+// A wave's four weight words (gate tile 0, gate tile 1, up tile 0, up tile 1
+// of its columns) and their four scale bytes from the LDS ring, waited for
+// inside the asm block for the same reason as lds_frags.
+__device__ __forceinline__ void lds_weights(uint32_t waddr, uint32_t saddr, uint32_t (&bc)[4], uint32_t (&bs)[4]) {
+    asm volatile("ds_read_b32 %0, %8\n\tds_read_b32 %1, %8 offset:256\n\t"
+                 "ds_read_b32 %2, %8 offset:2048\n\tds_read_b32 %3, %8 offset:2304\n\t"
+                 "ds_read_u8 %4, %9\n\tds_read_u8 %5, %9 offset:16\n\t"
+                 "ds_read_u8 %6, %9 offset:128\n\tds_read_u8 %7, %9 offset:144\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(bc[0]), "=&v"(bc[1]), "=&v"(bc[2]), "=&v"(bc[3]), "=&v"(bs[0]), "=&v"(bs[1]), "=&v"(bs[2]),
+                   "=&v"(bs[3])
+                 : "v"(waddr), "v"(saddr) : "memory");
+}
+
+// Every operand of a group arrives by direct global-to-LDS loads, NB - 1
+// groups ahead, into a ring of NB buffers: per wave and group one 16-byte load
+// per lane for each of two 16-row halves of its 32 activation rows, one 16-byte
+// load per lane of weight codes (wave w fetches the 1 KiB of (matrix w/2,
+// packed tile w%2): 64 columns x 16 B) and one 4-byte load on lanes 0-15 of that
+// block's 64 scale bytes. Activation lane L of a 1 KiB load writes LDS bytes
+// 16L .. 16L+15 of it, i.e. row L/4 of the 16 and chunk position L%4, so it
+// reads the row's chunk (L%4) ^ swz(L/4).
+// Per group step a wave issues those four loads (compiler fences keep the
+// order), reads the group's activation fragments, runs its matrix
+// instructions, waits until its own loads of the next group have landed (a
+// fixed vmcnt: the loads issued after them), passes a barrier that publishes
+// every wave's, and reads and decodes the next group's weights while the
+// matrix work drains. A buffer is refilled only after the barrier that follows
+// every wave's last read of it.
 template <int NS, int D, int kDA>
-__device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint8_t* sX, const int* sEntry) {
+__device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint8_t* sX, uint8_t* sW, uint8_t* sS,
+                                        const int* sEntry) {
     constexpr int NB = XP_PF_GU_NB;
-    static_assert(NB >= 3 && NB <= 8, "activation ring");
-    // loads per group step and wave: 2 activation, 8 weight (4 code words, 4 scale bytes)
-    constexpr int kAfter = 8 + 10 * (NB - 2);   // issued after the activation loads of group g+1, at step g's wait
+    static_assert(NB >= 3 && NB <= 8, "ring");
+    constexpr int kPerStep = 4;                      // loads per wave per group
+    constexpr int kAfter = kPerStep * (NB - 2);      // issued after group g+1's, at step g's wait
     static_assert(kAfter <= 63, "vmcnt range");
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int G = a.G, I = a.I;
 
-    // this lane's two activation sources (rows 32w + L/4 and 32w + 16 + L/4)
+    // activation sources of this lane (rows 32w + L/4 and 32w + 16 + L/4)
     const int lrow = lane >> 2;
     const int lchunk = (lane & 3) ^ x_swz(lrow);
     const uint16_t* xa0 = a.x + (size_t)(sEntry[32 * wave + lrow] / a.k) * a.H + lchunk * 8;
     const uint16_t* xa1 = a.x + (size_t)(sEntry[32 * wave + 16 + lrow] / a.k) * a.H + lchunk * 8;
-    auto dma_x = [&](int g) {
+    // weight block fetched by this wave: matrix wave/2, packed tile it.nt*2 + wave%2
+    // (tile 0 when past the last tile: I not a multiple of 128; nothing is stored for it)
+    const xp_expert ex = a.experts[it.e];
+    const int fpt_raw = it.nt * 2 + (wave & 1);
+    const int fpt = fpt_raw * 64 < I ? fpt_raw : 0;
+    const uint8_t* wsrc = (wave >> 1 ? ex.up_codes : ex.gate_codes) + (size_t)fpt * G * 1024 + lane * 16;
+    const uint8_t* ssrc = (wave >> 1 ? ex.up_scales : ex.gate_scales) + (size_t)fpt * G * 64 + (lane & 15) * 4;
+    auto dma = [&](int g) {
         const int gc = min(g, G - 1);
-        uint8_t* dst = sX + (size_t)(g % NB) * kXTile + wave * 2048;
-        __builtin_amdgcn_global_load_lds((gvoid_t)(xa0 + gc * 32), (lvoid_t)dst, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((gvoid_t)(xa1 + gc * 32), (lvoid_t)(dst + 1024), 16, 0, 0);
+        const int buf = g % NB;
+        uint8_t* dx = sX + (size_t)buf * kXTile + wave * 2048;
+        __builtin_amdgcn_global_load_lds((gvoid_t)(xa0 + gc * 32), (lvoid_t)dx, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gvoid_t)(xa1 + gc * 32), (lvoid_t)(dx + 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gvoid_t)(wsrc + (size_t)gc * 1024),
+                                         (lvoid_t)(sW + (size_t)buf * kWTile + wave * 1024), 16, 0, 0);
+        if (lane < 16)
+            __builtin_amdgcn_global_load_lds((gvoid_t)(ssrc + (size_t)gc * 64),
+                                             (lvoid_t)(sS + (size_t)buf * kSTile + wave * 64), 4, 0, 0);
     };
 
     // This wave's columns: packed tile pt, columns c0 .. c0+31 of it. A wave past
-    // the last tile (I not a multiple of 128) reads tile 0 and stores nothing.
+    // the last tile (I not a multiple of 128) computes on tile 0 and stores nothing.
     const int pt_raw = it.nt * 2 + (wave >> 1);
     const bool live = pt_raw * 64 < I;
     const int pt = live ? pt_raw : 0;
     const int c0 = (wave & 1) * 32;
-    const xp_expert ex = a.experts[it.e];
-    const int col = c0 + (lane & 15);  // column of the first 16-column MFMA tile
     const int word = lane >> 4;        // which 8 k of the 32-group this lane decodes
-    gwords_t gc = (gwords_t)(ex.gate_codes) + (size_t)pt * G * 256 + col * 4 + word;
-    gwords_t uc = (gwords_t)(ex.up_codes) + (size_t)pt * G * 256 + col * 4 + word;
-    gbytes1_t gs = (gbytes1_t)(ex.gate_scales) + (size_t)pt * G * 64 + col;
-    gbytes1_t us = (gbytes1_t)(ex.up_scales) + (size_t)pt * G * 64 + col;
-    uint32_t bc[D][4], bs[D][4];
-    auto load_b = [&](int slot, int g) {
-        g = min(g, G - 1);
-        bc[slot][0] = gc[g * 256];
-        bc[slot][1] = gc[g * 256 + 64];  // 16 columns on: +64 words, +16 scale bytes
-        bc[slot][2] = uc[g * 256];
-        bc[slot][3] = uc[g * 256 + 64];
-        bs[slot][0] = gs[g * 64];
-        bs[slot][1] = gs[g * 64 + 16];
-        bs[slot][2] = us[g * 64];
-        bs[slot][3] = us[g * 64 + 16];
-    };
+    // its weights in the ring: block (matrix, wave/2), column c0 + t*16 + lane%16, word `word`
+    const uint32_t w_lds = (uint32_t)(size_t)(lvoid_t)sW + (wave >> 1) * 1024 + (c0 + (lane & 15)) * 16 + word * 4;
+    const uint32_t s_lds = (uint32_t)(size_t)(lvoid_t)sS + (wave >> 1) * 64 + c0 + (lane & 15);
+    uint32_t bc[4], bs[4];
     bf16x8 bf[2][4];
-    auto decode_b = [&](int buf, int slot) {
-        if (wave_scales_pow2(bs[slot][0], bs[slot][1], bs[slot][2], bs[slot][3])) {
+    auto decode_b = [&](int buf) {
+        if (wave_scales_pow2(bs[0], bs[1], bs[2], bs[3])) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) bf[buf][q] = decode8_pow2(bc[slot][q], e4m3f(bs[slot][q]));
+            for (int q = 0; q < 4; ++q) bf[buf][q] = decode8_pow2(bc[q], e4m3f(bs[q]));
         } else {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) bf[buf][q] = decode8(bc[slot][q], e4m3f(bs[slot][q]));
+            for (int q = 0; q < 4; ++q) bf[buf][q] = decode8(bc[q], e4m3f(bs[q]));
         }
     };
     // fragment reads: row 16s + (lane & 15), chunk `word`, at its swizzled position
@@ -340,29 +361,25 @@ __device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint8_t
             acc[s][c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 
-    // prologue: activation tiles of groups 0 .. NB-2, weights of groups 0 .. D-1
+    // prologue: groups 0 .. NB-2 into buffers 0 .. NB-2; decode group 0
 #pragma unroll
     for (int g = 0; g < NB - 1; ++g) {
-        dma_x(g);
+        dma(g);
         mem_fence_compiler();
     }
-#pragma unroll
-    for (int u = 0; u < D; ++u) load_b(u, u);
-    mem_fence_compiler();
-    decode_b(0, 0);
-    load_b(0, D);
-    mem_fence_compiler();
     __builtin_amdgcn_s_waitcnt(waitcnt_imm<0, true>());
     __syncthreads();
+    lds_weights(w_lds, s_lds, bc, bs);
+    decode_b(0);
 
     for (int g0 = 0; g0 < G; g0 += D) {
 #pragma unroll
         for (int u = 0; u < D; ++u) {
             const int g = g0 + u;
             const int cur = u & 1;
-            // the tile of group g + NB - 1 into the buffer group g - 1 used (all
-            // waves finished reading it before the last barrier)
-            dma_x(g + NB - 1);
+            // group g + NB - 1 into the buffers group g - 1 used (every wave
+            // finished reading them before the last barrier)
+            dma(g + NB - 1);
             mem_fence_compiler();
             bf16x8 af[NS];
             lds_frags<NS>(x_lds + (uint32_t)((g % NB) * kXTile), af);
@@ -373,19 +390,16 @@ __device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint8_t
                 acc[s][0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s], bf[cur][2], acc[s][0][1], 0, 0, 0);
                 acc[s][1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s], bf[cur][3], acc[s][1][1], 0, 0, 0);
             }
-            // next group's weights: decode now (overlaps the matrix work), refill the ring
-            const int nslot = (u + 1) % D;
-            decode_b(cur ^ 1, nslot);
+            // this wave's loads of group g+1 have landed; the barrier publishes
+            // every wave's (a plain barrier: __syncthreads' release fence would
+            // wait for every load in flight)
             mem_fence_compiler();
-            load_b(nslot, g + 1 + D);
-            mem_fence_compiler();
-            // this wave's loads of group g+1's tile have landed and its reads of
-            // buffer g % NB are done; the barrier publishes every wave's. (A
-            // plain barrier: __syncthreads' release fence would wait for every
-            // load in flight.)
             __builtin_amdgcn_s_waitcnt(waitcnt_imm<kAfter, true>());
             __builtin_amdgcn_s_barrier();
             mem_fence_compiler();
+            const uint32_t nb = (uint32_t)((g + 1) % NB);
+            lds_weights(w_lds + nb * kWTile, s_lds + nb * kSTile, bc, bs);
+            decode_b(cur ^ 1);
         }
     }
     // no load of this item may still be in flight into the buffers
@@ -437,9 +451,11 @@ struct GuRun {
     const GuArgs& a;
     const Item& it;
     uint8_t* sX;
+    uint8_t* sW;
+    uint8_t* sS;
     const int* sEntry;
     template <int NS, int D>
-    __device__ __forceinline__ void run() const { gu_item<NS, D, XP_PF_GU_DA>(a, it, sX, sEntry); }
+    __device__ __forceinline__ void run() const { gu_item<NS, D, XP_PF_GU_DA>(a, it, sX, sW, sS, sEntry); }
 };
 
 // act[entry][n] = silu(g) * u for the item's rows and columns, where g and u
@@ -449,6 +465,8 @@ __global__ __launch_bounds__(kPThreads, XP_PF_GU_WAVES) void prefill_gateup_kern
     const int32_t* __restrict__ offset, const int32_t* __restrict__ entry, int E, int k, int H, int I,
     float* __restrict__ act) {
     __shared__ __attribute__((aligned(1024))) uint8_t sX[XP_PF_GU_NB * kXTile];
+    __shared__ __attribute__((aligned(1024))) uint8_t sW[XP_PF_GU_NB * kWTile];
+    __shared__ __attribute__((aligned(256))) uint8_t sS[XP_PF_GU_NB * kSTile];
     __shared__ int sEntry[kPM];
     __shared__ int sP[kMaxExperts + 1];
     __shared__ int swave[4];
@@ -463,7 +481,7 @@ __global__ __launch_bounds__(kPThreads, XP_PF_GU_WAVES) void prefill_gateup_kern
         const Item it = item_at(i, n_tiles, sP, E, count);
         if (t < kPM) sEntry[t] = entry[offset[it.e] + it.m0 + min(t, it.rows - 1)];
         __syncthreads();
-        dispatch_item<XP_PF_GU_DMAX>(it.rows, a.G, GuRun{a, it, sX, sEntry});
+        dispatch_item<XP_PF_GU_DMAX>(it.rows, a.G, GuRun{a, it, sX, sW, sS, sEntry});
         __syncthreads();  // sEntry and sA are rewritten by the next item
     }
 }

@@ -2,7 +2,10 @@
 
 Both paths run the same per-row arithmetic, so every output must be bit-equal,
 the published plan must be the same, and repeated down+combine launches on one
-plan must keep giving the same y. xp_down_combine runs one of three forms: one
+plan must keep giving the same y. xp_route_gateup routes inside the gate/up
+launch for one row (gateup_one_row_kernel) and for 2..64 rows whose gate/up
+grid is at most 1024 workgroups (route_gateup_rows_kernel), and otherwise runs
+the routing launch first. xp_down_combine runs one of three forms: one
 row with top-k up to 8 in down_combine_one_row_kernel, at most 64 (row, slot)
 entries in down_combine_rows_kernel, and more entries as the two launches
 (down, then combine); each form is covered below, and the two-call path is
