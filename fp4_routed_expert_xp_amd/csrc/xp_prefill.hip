@@ -31,7 +31,6 @@ namespace xp {
 constexpr int kPM = 128;        // rows per item
 constexpr int kPN = 128;        // output columns per item (two packed 64-column tiles)
 constexpr int kPThreads = 256;  // four waves
-constexpr int kAStride = 72;    // bf16 per LDS activation row: two groups (64) + 8 padding (conflict-free 16-byte reads)
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
@@ -251,8 +250,8 @@ __device__ __forceinline__ void lds_frags(uint32_t addr, bf16x8 (&af)[NS]) {
 }
 
 // Activation tiles of one 32-wide group: 128 rows x 64 B, no padding; the
-// four 16-byte chunks of row r sit at chunk position c ^ swz(r), swz(r) =
-// ((r >> 1) ^ (r >> 3)) & 3, so a fragment read (16 rows at one chunk) is free
+// four 16-byte chunks of row r sit at chunk position c ^ swz(r % 16), swz(p) =
+// ((p >> 1) ^ (p >> 3)) & 3, so a fragment read (16 rows at one chunk) is free
 // of bank conflicts whether the LDS serves 8 lanes a cycle from 32 banks or 16
 // lanes from 64.
 __device__ __forceinline__ int x_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
@@ -504,8 +503,8 @@ struct DnArgs {
 };
 
 template <int NS, int D, int kDA>
-__device__ __forceinline__ void dn_item(const DnArgs& a, const Item& it, uint16_t (*sHi)[kPM * kAStride],
-                                        uint16_t (*sLo)[kPM * kAStride], const int* sEntry) {
+__device__ __forceinline__ void dn_item(const DnArgs& a, const Item& it, uint8_t* sHi, uint8_t* sLo,
+                                        const int* sEntry) {
     static_assert(kDA % 2 == 0 && D % kDA == 0, "rings hold whole steps of two groups");
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int G = a.G, H = a.H, I = a.I;
@@ -519,17 +518,21 @@ __device__ __forceinline__ void dn_item(const DnArgs& a, const Item& it, uint16_
 #pragma unroll
         for (int q = 0; q < 4; ++q) ra[slot][q] = arow_p[8 * g + q];
     };
+    // row arow's chunks 2*(t&1) and 2*(t&1)+1 of the group's 64-byte row, at
+    // their swizzled positions (the tile layout of the gate/up activations; the
+    // swizzle follows the row's place in its 16-row slab)
+    const int cpos0 = ((2 * (t & 1)) ^ x_swz(arow & 15)) * 16, cpos1 = ((2 * (t & 1) + 1) ^ x_swz(arow & 15)) * 16;
     auto store_a = [&](int buf, int slot, int half) {
         uint32_t hi[8], lo[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q)
             split_pair(ra[slot][q >> 1][(q & 1) * 2], ra[slot][q >> 1][(q & 1) * 2 + 1], hi[q], lo[q]);
-        u32x4v* qh = (u32x4v*)(&sHi[buf][arow * kAStride + half * 32 + acol]);
-        u32x4v* ql = (u32x4v*)(&sLo[buf][arow * kAStride + half * 32 + acol]);
-        qh[0] = u32x4v{hi[0], hi[1], hi[2], hi[3]};
-        qh[1] = u32x4v{hi[4], hi[5], hi[6], hi[7]};
-        ql[0] = u32x4v{lo[0], lo[1], lo[2], lo[3]};
-        ql[1] = u32x4v{lo[4], lo[5], lo[6], lo[7]};
+        uint8_t* th = (uint8_t*)sHi + (size_t)(buf * 2 + half) * kXTile + arow * 64;
+        uint8_t* tl = (uint8_t*)sLo + (size_t)(buf * 2 + half) * kXTile + arow * 64;
+        *(u32x4v*)(th + cpos0) = u32x4v{hi[0], hi[1], hi[2], hi[3]};
+        *(u32x4v*)(th + cpos1) = u32x4v{hi[4], hi[5], hi[6], hi[7]};
+        *(u32x4v*)(tl + cpos0) = u32x4v{lo[0], lo[1], lo[2], lo[3]};
+        *(u32x4v*)(tl + cpos1) = u32x4v{lo[4], lo[5], lo[6], lo[7]};
     };
 
     const int pt_raw = it.nt * 2 + (wave >> 1);
@@ -539,6 +542,7 @@ __device__ __forceinline__ void dn_item(const DnArgs& a, const Item& it, uint16_
     const xp_expert ex = a.experts[it.e];
     const int col = c0 + (lane & 15);
     const int word = lane >> 4;
+    const int frag_off = (lane & 15) * 64 + ((word ^ x_swz(lane & 15)) * 16);
     gwords_t dc = (gwords_t)(ex.down_codes) + (size_t)pt * G * 256 + col * 4 + word;
     gbytes1_t ds = (gbytes1_t)(ex.down_scales) + (size_t)pt * G * 64 + col;
     uint32_t bc[D][2], bs[D][2];
@@ -585,12 +589,12 @@ __device__ __forceinline__ void dn_item(const DnArgs& a, const Item& it, uint16_
             const int g = g0 + u;
             const int cur = u & 1;
             const int buf = (g >> 1) & 1;  // LDS buffers hold two groups each
-            const int off = (lane & 15) * kAStride + cur * 32 + word * 8;
+            const size_t off = (size_t)(buf * 2 + cur) * kXTile + frag_off;
             bf16x8 ah[NS], al[NS];
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-                ah[s] = *(const bf16x8*)(&sHi[buf][off + s * 16 * kAStride]);
-                al[s] = *(const bf16x8*)(&sLo[buf][off + s * 16 * kAStride]);
+                ah[s] = *(const bf16x8*)((const uint8_t*)sHi + off + s * 1024);
+                al[s] = *(const bf16x8*)((const uint8_t*)sLo + off + s * 1024);
             }
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
@@ -635,8 +639,8 @@ __device__ __forceinline__ void dn_item(const DnArgs& a, const Item& it, uint16_
 struct DnRun {
     const DnArgs& a;
     const Item& it;
-    uint16_t (*sHi)[kPM * kAStride];
-    uint16_t (*sLo)[kPM * kAStride];
+    uint8_t* sHi;
+    uint8_t* sLo;
     const int* sEntry;
     template <int NS, int D>
     __device__ __forceinline__ void run() const { dn_item<NS, D, XP_PF_DN_DA>(a, it, sHi, sLo, sEntry); }
@@ -647,8 +651,9 @@ __global__ __launch_bounds__(kPThreads, XP_PF_DN_WAVES) void prefill_down_kernel
     const xp_expert* __restrict__ experts, const float* __restrict__ act, const int32_t* __restrict__ count,
     const int32_t* __restrict__ offset, const int32_t* __restrict__ entry, int E, int H, int I,
     float* __restrict__ out) {
-    __shared__ __attribute__((aligned(16))) uint16_t sHi[2][kPM * kAStride];
-    __shared__ __attribute__((aligned(16))) uint16_t sLo[2][kPM * kAStride];
+    // act halves, two LDS buffers of two groups each: [buffer][group][128 rows x 64 B], swizzled
+    __shared__ __attribute__((aligned(1024))) uint8_t sHi[2 * 2 * kXTile];
+    __shared__ __attribute__((aligned(1024))) uint8_t sLo[2 * 2 * kXTile];
     __shared__ int sEntry[kPM];
     __shared__ int sP[kMaxExperts + 1];
     __shared__ int swave[4];
