@@ -40,6 +40,11 @@ typedef const uint32_t __attribute__((address_space(1)))* gwords_t;
 typedef const uint8_t __attribute__((address_space(1)))* gbytes1_t;
 typedef const void __attribute__((address_space(1)))* gvoid_t;
 typedef void __attribute__((address_space(3)))* lvoid_t;
+}  // namespace xp
+
+#include "xp_prefill_asm.h"
+
+namespace xp {
 
 // Keeps the compiler from moving memory operations across this point, so the
 // vector-memory counts below follow the program order.
@@ -216,39 +221,6 @@ struct GuArgs {
     int k, H, I, G;
 };
 
-// NS 16-byte LDS reads at addr + s * 1024 (s = 0 .. NS-1), waited for inside
-// the same asm block: the reads follow direct global-to-LDS loads whose
-// completion the kernel orders itself (vmcnt and a barrier), and the compiler,
-// which cannot tell the ring's buffers apart, would otherwise wait for every
-// load in flight before each read.
-template <int NS>
-__device__ __forceinline__ void lds_frags(uint32_t addr, bf16x8 (&af)[NS]) {
-    u32x4v r[8];
-    if constexpr (NS == 2)
-        asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:1024\n\ts_waitcnt lgkmcnt(0)"
-                     : "=&v"(r[0]), "=&v"(r[1]) : "v"(addr) : "memory");
-    else if constexpr (NS == 4)
-        asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:1024\n\t"
-                     "ds_read_b128 %2, %4 offset:2048\n\tds_read_b128 %3, %4 offset:3072\n\ts_waitcnt lgkmcnt(0)"
-                     : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]) : "v"(addr) : "memory");
-    else if constexpr (NS == 6)
-        asm volatile("ds_read_b128 %0, %6\n\tds_read_b128 %1, %6 offset:1024\n\t"
-                     "ds_read_b128 %2, %6 offset:2048\n\tds_read_b128 %3, %6 offset:3072\n\t"
-                     "ds_read_b128 %4, %6 offset:4096\n\tds_read_b128 %5, %6 offset:5120\n\ts_waitcnt lgkmcnt(0)"
-                     : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]) : "v"(addr)
-                     : "memory");
-    else
-        asm volatile("ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:1024\n\t"
-                     "ds_read_b128 %2, %8 offset:2048\n\tds_read_b128 %3, %8 offset:3072\n\t"
-                     "ds_read_b128 %4, %8 offset:4096\n\tds_read_b128 %5, %8 offset:5120\n\t"
-                     "ds_read_b128 %6, %8 offset:6144\n\tds_read_b128 %7, %8 offset:7168\n\ts_waitcnt lgkmcnt(0)"
-                     : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
-                       "=&v"(r[7])
-                     : "v"(addr) : "memory");
-#pragma unroll
-    for (int s = 0; s < NS; ++s) af[s] = __builtin_bit_cast(bf16x8, r[s]);
-}
-
 // Activation tiles of one 32-wide group: 128 rows x 64 B, no padding; the
 // four 16-byte chunks of row r sit at chunk position c ^ swz(r % 16), swz(p) =
 // ((p >> 1) ^ (p >> 3)) & 3, so a fragment read (16 rows at one chunk) is free
@@ -264,7 +236,11 @@ constexpr int kSTile = 4 * 64;     // scale bytes per group: (matrix, packed til
 
 // A wave's four weight words (gate tile 0, gate tile 1, up tile 0, up tile 1
 // of its columns) and their four scale bytes from the LDS ring, waited for
-// inside the asm block for the same reason as lds_frags.
+// inside the asm block: the reads follow direct global-to-LDS loads whose
+// completion the kernel orders itself (vmcnt and a barrier), and the compiler,
+// which cannot tell the ring's buffers apart, would otherwise wait for every
+// load in flight before each read. The activation fragments are read the same
+// way, inside the generated group bodies.
 __device__ __forceinline__ void lds_weights(uint32_t waddr, uint32_t saddr, uint32_t (&bc)[4], uint32_t (&bs)[4]) {
     asm volatile("ds_read_b32 %0, %8\n\tds_read_b32 %1, %8 offset:256\n\t"
                  "ds_read_b32 %2, %8 offset:2048\n\tds_read_b32 %3, %8 offset:2304\n\t"
@@ -380,15 +356,7 @@ __device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint8_t
             // finished reading them before the last barrier)
             dma(g + NB - 1);
             mem_fence_compiler();
-            bf16x8 af[NS];
-            lds_frags<NS>(x_lds + (uint32_t)((g % NB) * kXTile), af);
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                acc[s][0][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s], bf[cur][0], acc[s][0][0], 0, 0, 0);
-                acc[s][1][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s], bf[cur][1], acc[s][1][0], 0, 0, 0);
-                acc[s][0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s], bf[cur][2], acc[s][0][1], 0, 0, 0);
-                acc[s][1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s], bf[cur][3], acc[s][1][1], 0, 0, 0);
-            }
+            PfGroup<NS>::gateup(acc, bf[cur], x_lds + (uint32_t)((g % NB) * kXTile));
             // this wave's loads of group g+1 have landed; the barrier publishes
             // every wave's (a plain barrier: __syncthreads' release fence would
             // wait for every load in flight)
@@ -403,6 +371,7 @@ __device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint8_t
     }
     // no load of this item may still be in flight into the buffers
     __builtin_amdgcn_s_waitcnt(waitcnt_imm<0, false>());
+    PfGroup<NS>::drain(acc);
 
     if (live) {
 #pragma unroll
@@ -509,30 +478,38 @@ __device__ __forceinline__ void dn_item(const DnArgs& a, const Item& it, uint8_t
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int G = a.G, H = a.H, I = a.I;
 
-    // act rows staged by all threads: row t/2, 16 floats at k offset (t&1)*16.
-    const int arow = t >> 1, acol = (t & 1) * 16;
-    const u32x4v* arow_p = (const u32x4v*)(a.act + (size_t)sEntry[arow] * I + acol);
+    // act staging: thread (wave w, lane L) moves floats 4c .. 4c+3 (c = L % 8) of
+    // the group for rows 32w + 8q + L/8, q = 0..3, so the eight lanes of a row
+    // read its 128 bytes together and each load instruction touches eight rows'
+    // lines. Each 16 bytes become 8 bytes of hi and 8 of lo at the row's chunk
+    // c/2 (at its swizzled position, the tile layout of the gate/up activations;
+    // the swizzle follows the row's place in its 16-row slab), half c % 2.
+    const int c8 = lane & 7;
+    const float* arow_q[4];
+    uint32_t soff_q[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int r = 32 * wave + 8 * q + (lane >> 3);
+        arow_q[q] = a.act + (size_t)sEntry[r] * I + 4 * c8;
+        soff_q[q] = (uint32_t)(r * 64 + (((c8 >> 1) ^ x_swz(r & 15)) * 16) + (c8 & 1) * 8);
+    }
     u32x4v ra[kDA][4];
     auto load_a = [&](int slot, int g) {
         g = min(g, G - 1);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) ra[slot][q] = arow_p[8 * g + q];
+        for (int q = 0; q < 4; ++q) ra[slot][q] = *(const u32x4v*)(arow_q[q] + 32 * g);
     };
-    // row arow's chunks 2*(t&1) and 2*(t&1)+1 of the group's 64-byte row, at
-    // their swizzled positions (the tile layout of the gate/up activations; the
-    // swizzle follows the row's place in its 16-row slab)
-    const int cpos0 = ((2 * (t & 1)) ^ x_swz(arow & 15)) * 16, cpos1 = ((2 * (t & 1) + 1) ^ x_swz(arow & 15)) * 16;
     auto store_a = [&](int buf, int slot, int half) {
-        uint32_t hi[8], lo[8];
+        uint8_t* th = (uint8_t*)sHi + (size_t)(buf * 2 + half) * kXTile;
+        uint8_t* tl = (uint8_t*)sLo + (size_t)(buf * 2 + half) * kXTile;
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-            split_pair(ra[slot][q >> 1][(q & 1) * 2], ra[slot][q >> 1][(q & 1) * 2 + 1], hi[q], lo[q]);
-        uint8_t* th = (uint8_t*)sHi + (size_t)(buf * 2 + half) * kXTile + arow * 64;
-        uint8_t* tl = (uint8_t*)sLo + (size_t)(buf * 2 + half) * kXTile + arow * 64;
-        *(u32x4v*)(th + cpos0) = u32x4v{hi[0], hi[1], hi[2], hi[3]};
-        *(u32x4v*)(th + cpos1) = u32x4v{hi[4], hi[5], hi[6], hi[7]};
-        *(u32x4v*)(tl + cpos0) = u32x4v{lo[0], lo[1], lo[2], lo[3]};
-        *(u32x4v*)(tl + cpos1) = u32x4v{lo[4], lo[5], lo[6], lo[7]};
+        for (int q = 0; q < 4; ++q) {
+            uint32_t h0, h1, l0, l1;
+            split_pair(ra[slot][q][0], ra[slot][q][1], h0, l0);
+            split_pair(ra[slot][q][2], ra[slot][q][3], h1, l1);
+            *(uint2*)(th + soff_q[q]) = make_uint2(h0, h1);
+            *(uint2*)(tl + soff_q[q]) = make_uint2(l0, l1);
+        }
     };
 
     const int pt_raw = it.nt * 2 + (wave >> 1);
@@ -564,6 +541,8 @@ __device__ __forceinline__ void dn_item(const DnArgs& a, const Item& it, uint8_t
         }
     };
 
+    // LDS byte addresses of the two act halves
+    const uint32_t hi_lds = (uint32_t)(size_t)(lvoid_t)sHi, lo_lds = (uint32_t)(size_t)(lvoid_t)sLo;
     f32x4 acc[NS][2];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -589,23 +568,8 @@ __device__ __forceinline__ void dn_item(const DnArgs& a, const Item& it, uint8_t
             const int g = g0 + u;
             const int cur = u & 1;
             const int buf = (g >> 1) & 1;  // LDS buffers hold two groups each
-            const size_t off = (size_t)(buf * 2 + cur) * kXTile + frag_off;
-            bf16x8 ah[NS], al[NS];
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                ah[s] = *(const bf16x8*)((const uint8_t*)sHi + off + s * 1024);
-                al[s] = *(const bf16x8*)((const uint8_t*)sLo + off + s * 1024);
-            }
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                acc[s][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[s], bf[cur][0], acc[s][0], 0, 0, 0);
-                acc[s][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[s], bf[cur][1], acc[s][1], 0, 0, 0);
-            }
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                acc[s][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[s], bf[cur][0], acc[s][0], 0, 0, 0);
-                acc[s][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[s], bf[cur][1], acc[s][1], 0, 0, 0);
-            }
+            const uint32_t off = (uint32_t)((buf * 2 + cur) * kXTile + frag_off);
+            PfGroup<NS>::down(acc, bf[cur], hi_lds + off, lo_lds + off);
             const int nslot = (u + 1) % D;
             decode_b(cur ^ 1, nslot);
             load_b(nslot, g + 1 + D);
@@ -620,6 +584,7 @@ __device__ __forceinline__ void dn_item(const DnArgs& a, const Item& it, uint8_t
         }
     }
 
+    PfGroup<NS>::drain(acc);
     if (live) {
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
