@@ -29,7 +29,7 @@
 namespace xp {
 
 constexpr int kPM = 128;        // rows per item
-constexpr int kPN = 128;        // output columns per item (two packed 64-column tiles)
+constexpr int kPN = 128;        // output columns per gate/up item (two packed 64-column tiles)
 constexpr int kPThreads = 256;  // four waves
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
@@ -62,9 +62,11 @@ constexpr int waitcnt_imm() {
 // Item bookkeeping shared by both kernels: per-expert blocks of 128 rows and
 // their prefix, rebuilt by each workgroup from the plan's counts.
 // sP[e] = row blocks of experts before e (sP[E] = all); all threads call.
+template <int NT>
 __device__ __forceinline__ int block_prefix(const int32_t* __restrict__ count, int E, int* sP, int* swave) {
+    static_assert(NT >= 256, "E <= 1024 experts at most four per thread");
     const int t = threadIdx.x;
-    const int per = (E + kPThreads - 1) / kPThreads;  // experts per thread (E <= 1024 -> <= 4)
+    const int per = (E + NT - 1) / NT;  // experts per thread
     int loc[4];
     int sum = 0;
 #pragma unroll
@@ -86,7 +88,7 @@ __device__ __forceinline__ int block_prefix(const int32_t* __restrict__ count, i
         if (j < per && e < E) sP[e] = run;
         run += loc[j];
     }
-    if (t == kPThreads - 1) sP[E] = run;
+    if (t == NT - 1) sP[E] = run;
     __syncthreads();
     return sP[E];
 }
@@ -204,9 +206,19 @@ __device__ __forceinline__ Deal deal(int total) {
 #ifndef XP_PF_GU_DA
 #define XP_PF_GU_DA 2
 #endif
-#ifndef XP_PF_DN_WAVES
-#define XP_PF_DN_WAVES 2
+// Down runs one workgroup of XP_PF_DN_WG_WAVES waves per CU when that is 8
+// (items of 256 columns: every act tile staged once serves twice the columns),
+// else two of four waves (items of 128 columns).
+#ifndef XP_PF_DN_WG_WAVES
+#define XP_PF_DN_WG_WAVES 8
 #endif
+#define XP_PF_DN_WAVES (8 / XP_PF_DN_WG_WAVES)
+constexpr int kDnWaves = XP_PF_DN_WG_WAVES;
+constexpr int kDnThreads = 64 * kDnWaves;
+constexpr int kDnCols = 32 * kDnWaves;     // output columns per down item
+constexpr int kDnRowsPerWave = kPM / kDnWaves;
+constexpr int kAQ = kDnRowsPerWave / 8;    // act loads per thread and group
+static_assert(kDnWaves == 4 || kDnWaves == 8, "down workgroup of four or eight waves");
 #ifndef XP_PF_DN_DMAX
 #define XP_PF_DN_DMAX 4
 #endif
@@ -441,7 +453,7 @@ __global__ __launch_bounds__(kPThreads, XP_PF_GU_WAVES) void prefill_gateup_kern
 
     const int t = threadIdx.x;
     const int n_tiles = (I + kPN - 1) / kPN;
-    const int total = block_prefix(count, E, sP, swave) * n_tiles;
+    const int total = block_prefix<kPThreads>(count, E, sP, swave) * n_tiles;
     const GuArgs a{x, experts, act, k, H, I, H / 32};
     const Deal dl = deal(total);
 
@@ -479,31 +491,32 @@ __device__ __forceinline__ void dn_item(const DnArgs& a, const Item& it, uint8_t
     const int G = a.G, H = a.H, I = a.I;
 
     // act staging: thread (wave w, lane L) moves floats 4c .. 4c+3 (c = L % 8) of
-    // the group for rows 32w + 8q + L/8, q = 0..3, so the eight lanes of a row
-    // read its 128 bytes together and each load instruction touches eight rows'
-    // lines. Each 16 bytes become 8 bytes of hi and 8 of lo at the row's chunk
-    // c/2 (at its swizzled position, the tile layout of the gate/up activations;
-    // the swizzle follows the row's place in its 16-row slab), half c % 2.
+    // the group for rows R w + 8q + L/8, q = 0 .. R/8 - 1 (R = 128 / waves), so
+    // the eight lanes of a row read its 128 bytes together and each load
+    // instruction touches eight rows' lines. Each 16 bytes become 8 bytes of hi
+    // and 8 of lo at the row's chunk c/2 (at its swizzled position, the tile
+    // layout of the gate/up activations; the swizzle follows the row's place in
+    // its 16-row slab), half c % 2.
     const int c8 = lane & 7;
-    const float* arow_q[4];
-    uint32_t soff_q[4];
+    const float* arow_q[kAQ];
+    uint32_t soff_q[kAQ];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int r = 32 * wave + 8 * q + (lane >> 3);
+    for (int q = 0; q < kAQ; ++q) {
+        const int r = kDnRowsPerWave * wave + 8 * q + (lane >> 3);
         arow_q[q] = a.act + (size_t)sEntry[r] * I + 4 * c8;
         soff_q[q] = (uint32_t)(r * 64 + (((c8 >> 1) ^ x_swz(r & 15)) * 16) + (c8 & 1) * 8);
     }
-    u32x4v ra[kDA][4];
+    u32x4v ra[kDA][kAQ];
     auto load_a = [&](int slot, int g) {
         g = min(g, G - 1);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) ra[slot][q] = *(const u32x4v*)(arow_q[q] + 32 * g);
+        for (int q = 0; q < kAQ; ++q) ra[slot][q] = *(const u32x4v*)(arow_q[q] + 32 * g);
     };
     auto store_a = [&](int buf, int slot, int half) {
         uint8_t* th = (uint8_t*)sHi + (size_t)(buf * 2 + half) * kXTile;
         uint8_t* tl = (uint8_t*)sLo + (size_t)(buf * 2 + half) * kXTile;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < kAQ; ++q) {
             uint32_t h0, h1, l0, l1;
             split_pair(ra[slot][q][0], ra[slot][q][1], h0, l0);
             split_pair(ra[slot][q][2], ra[slot][q][3], h1, l1);
@@ -512,7 +525,7 @@ __device__ __forceinline__ void dn_item(const DnArgs& a, const Item& it, uint8_t
         }
     };
 
-    const int pt_raw = it.nt * 2 + (wave >> 1);
+    const int pt_raw = it.nt * (kDnWaves / 2) + (wave >> 1);
     const bool live = pt_raw * 64 < H;
     const int pt = live ? pt_raw : 0;
     const int c0 = (wave & 1) * 32;
@@ -612,7 +625,7 @@ struct DnRun {
 };
 
 // out[entry][n] = the rows' act (fp32, as bf16 hi + lo) times down (K = inter).
-__global__ __launch_bounds__(kPThreads, XP_PF_DN_WAVES) void prefill_down_kernel(
+__global__ __launch_bounds__(kDnThreads, XP_PF_DN_WAVES) void prefill_down_kernel(
     const xp_expert* __restrict__ experts, const float* __restrict__ act, const int32_t* __restrict__ count,
     const int32_t* __restrict__ offset, const int32_t* __restrict__ entry, int E, int H, int I,
     float* __restrict__ out) {
@@ -621,11 +634,11 @@ __global__ __launch_bounds__(kPThreads, XP_PF_DN_WAVES) void prefill_down_kernel
     __shared__ __attribute__((aligned(1024))) uint8_t sLo[2 * 2 * kXTile];
     __shared__ int sEntry[kPM];
     __shared__ int sP[kMaxExperts + 1];
-    __shared__ int swave[4];
+    __shared__ int swave[kDnWaves];
 
     const int t = threadIdx.x;
-    const int n_tiles = (H + kPN - 1) / kPN;
-    const int total = block_prefix(count, E, sP, swave) * n_tiles;
+    const int n_tiles = (H + kDnCols - 1) / kDnCols;
+    const int total = block_prefix<kDnThreads>(count, E, sP, swave) * n_tiles;
     const DnArgs a{act, experts, out, H, I, I / 32};
     const Deal dl = deal(total);
 
@@ -686,9 +699,9 @@ XP_API int xp_prefill_down(const xp_dims* dims, int32_t rows, const float* act, 
     if (!act || !experts || !workspace || !out) return XP_ERR_NULL;
     if (ws_bytes < ws_layout(dims, rows).total) return XP_ERR_WORKSPACE;
     WsPtrs w = ws_ptrs(const_cast<void*>(workspace), dims, rows);
-    const int n_tiles = (dims->hidden + kPN - 1) / kPN;
+    const int n_tiles = (dims->hidden + kDnCols - 1) / kDnCols;
     const int grid = prefill_grid(rows, dims->top_k, dims->n_experts, n_tiles, XP_PF_DN_WAVES);
-    hipLaunchKernelGGL(prefill_down_kernel, dim3(grid), dim3(kPThreads), 0, (hipStream_t)stream, experts, act,
+    hipLaunchKernelGGL(prefill_down_kernel, dim3(grid), dim3(kDnThreads), 0, (hipStream_t)stream, experts, act,
                        w.count, w.offset, w.entry, dims->n_experts, dims->hidden, dims->inter, out);
     return launch_status();
 }
