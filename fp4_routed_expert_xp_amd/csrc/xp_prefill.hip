@@ -14,14 +14,18 @@
 // layer math; the prefill chunk of 4,096 rows is the prompt step's default size
 // on the same site's serving page]
 //
-// Work items are (expert, block of 128 of its rows, block of 128 output
-// columns). A workgroup of four waves takes one item: wave w owns 32 columns
-// (two 16-column MFMA tiles) for all 128 rows (eight 16-row slabs), so each wave
-// decodes only its own columns' weights, and the rows' activations are staged
-// once per workgroup in LDS (double-buffered along K, two 32-wide groups per
-// step and barrier). The grid is persistent (two workgroups per CU); items are
-// laid out expert-major and dealt to the eight XCDs in contiguous ranges so the
-// workgroups sharing an expert's rows and weights share one L2.
+// Work items are (expert, block of 128 of its rows, block of output columns).
+// Every wave owns 32 columns (two 16-column MFMA tiles) for all 128 rows (eight
+// 16-row slabs), so each wave decodes only its own columns' weights, and the
+// rows' activations are staged once per workgroup in LDS. Gate/up: workgroups
+// of four waves (128 columns of both matrices), two per CU. Down: workgroups of
+// eight waves (256 columns), one per CU, so each staged act tile serves twice
+// the columns; its act is four bytes per element against x's two. The grid is
+// persistent; items are laid out expert-major and dealt to the eight XCDs in
+// contiguous ranges so the workgroups sharing an expert's rows and weights
+// share one L2. Each group's matrix work runs in a generated asm body that
+// reads the next two slabs' activation fragments while the current two slabs'
+// matrix instructions issue (xp_prefill_asm.h).
 #include "xp_common.h"
 
 #include <algorithm>
@@ -182,21 +186,19 @@ __device__ __forceinline__ Deal deal(int total) {
 }
 
 // ------------------------------------------------------------------ gate/up
-// The K loop is software-pipelined over 32-wide groups: each wave keeps the
-// weight words and scale bytes of the next D groups in flight (a register
-// ring), each thread keeps the activations of the next kDA groups in flight and
-// stages the next two groups in LDS at every other group (one barrier per two
-// groups), and the weights of group g+1 are decoded while group g's matrix
-// instructions run. The loop body has no branches (D divides
-// the group count; refills past the end re-read the last group), so the
-// compiler's wait counts follow the ring exactly. NS = 16-row slabs computed:
-// the item's rows rounded up to 2, 4, 6 or 8 slabs.
+// The K loops are software-pipelined over 32-wide groups. Gate/up stages every
+// operand by direct global-to-LDS loads into a ring of NB groups (below). Down
+// keeps the weight words and scale bytes of the next D groups in flight in a
+// register ring, each thread keeps the act of the next kDA groups in flight and
+// stages the next two groups (as bf16 hi and lo) in LDS at every other group
+// (one barrier per two groups). Both decode group g+1's weights while group
+// g's matrix instructions drain. The loop bodies have no branches (D divides
+// the group count; refills past the end re-read the last group), so the wait
+// counts follow the rings exactly. NS = 16-row slabs computed: the item's rows
+// rounded up to 2, 4, 6 or 8 slabs.
 //
-// Per kernel: waves per SIMD (= resident workgroups per CU), the deepest weight
-// ring and the activation ring. Two resident workgroups per CU let one's
-// decode, LDS and barrier time overlap the other's matrix work (measured: both
-// kernels faster than with one workgroup and deeper rings); the rings are sized
-// so the 128 (gate/up) or 64 (down) accumulators per lane still fit.
+// Per kernel: resident workgroups per CU (gate/up; down's follows from its
+// workgroup size), the deepest weight ring and down's activation ring.
 #ifndef XP_PF_GU_WAVES
 #define XP_PF_GU_WAVES 2
 #endif
