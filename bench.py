@@ -34,18 +34,23 @@ CSRC = os.path.join(ROOT, "fp4_routed_expert_xp_amd", "csrc")
 # workload), from two rocprofv3 --pmc runs: FETCH_SIZE, then WRITE_SIZE, in KiB per
 # dispatch (mean over the dispatches of that workload). Each is scaled by what the
 # same counter read for a plain 2 GiB device-to-device copy: FETCH_SIZE read
-# 1,048,614.1 KiB for 2,097,152 KiB fetched, WRITE_SIZE read exactly 2,097,152 KiB.
+# 1,048,611.8 KiB for 2,097,152 KiB fetched, WRITE_SIZE read exactly 2,097,152 KiB.
 # The figure belongs to the sources the kernel is built from (their digest below);
 # after any change to them the bench reports traffic as null.
-TRAFFIC = dict(sources="7b102cd9", fetch_kib=34990.7, write_kib=66.4,
-               fetch_factor=2097152 / 1048614.1, write_factor=1.0)
+TRAFFIC = dict(sources="7aa0b2f7", fetch_kib=34992.6, write_kib=66.4,
+               fetch_factor=2097152 / 1048611.8, write_factor=1.0)
 ROOFLINE_SOURCES = ("xp_rows.hip", "xp_pass_dev.h", "xp_common.h", "xp_route_dev.h", "xp_chain_asm.h")
 # The same counters for the one-row down + combine launch (down_combine_one_row_kernel).
-DOWN_TRAFFIC = dict(sources="7b102cd9", fetch_kib=17725.4, write_kib=144.0)
+DOWN_TRAFFIC = dict(sources="7aa0b2f7", fetch_kib=17729.7, write_kib=144.0)
 # The same for the dense FP8 projection kernel at 4096 x 4096 (grid of 256
 # workgroups; mean over its launches at 1, 8 and 16 rows), tied to xp_fp8.hip.
 FP8_TRAFFIC = dict(sources="15929da9", fetch_kib=8532.4, write_kib=133.3)
 FP8_SOURCES = ("xp_fp8.hip", "xp_common.h")
+# The same for the two prefill kernels on the 4,096-row chunk (mean over 4 seeded
+# layers), tied to xp_prefill.hip and its headers.
+PF_GU_TRAFFIC = dict(sources="ea021dc9", fetch_kib=1780229.6, write_kib=262174.4)
+PF_DN_TRAFFIC = dict(sources="ea021dc9", fetch_kib=973971.3, write_kib=524300.5)
+PREFILL_SOURCES = ("xp_prefill.hip", "xp_prefill_asm.h", "xp_common.h")
 
 
 def csrc_digest(sources=ROOFLINE_SOURCES) -> str:
@@ -724,7 +729,14 @@ def main():
             "kernel": "prefill_gateup_kernel (xp_prefill_gateup)", "bound": "mfma",
             "achieved": pf["gateup_tflops"], "flops_per_launch": 4 * cfg.H * cfg.I * cfg.R * cfg.k,
             "launch_us": pf["kernel_us"]["prefill_gateup"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(pf["gateup_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+            "frac": round(pf["gateup_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": measured_traffic(PF_GU_TRAFFIC, PREFILL_SOURCES)}
+        line["prefill_roofline_down"] = {
+            "kernel": "prefill_down_kernel (xp_prefill_down)", "bound": "mfma",
+            "achieved": pf["down_tflops"], "flops_per_launch": 2 * cfg.H * cfg.I * cfg.R * cfg.k,
+            "launch_us": pf["kernel_us"]["prefill_down"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(pf["down_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": measured_traffic(PF_DN_TRAFFIC, PREFILL_SOURCES)}
     fp8 = [reports[k] for k in ("fp8_rows/1", "fp8_rows/16") if k in reports]
     if fp8:
         N, K = 4096, 4096

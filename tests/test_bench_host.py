@@ -31,6 +31,15 @@ def test_traffic_is_tied_to_the_kernel_sources():
         assert 0.99 * alg < f < 1.1 * alg
     else:
         assert f is None
+    # prefill chunk (4,096 rows): at least the algorithmic bytes of the seeded layers
+    # (about 2.58 GB gate/up, 1.94 GB down: each routed expert's weights once plus
+    # the activations in and out), at most twice that
+    for tr, alg in ((bench.PF_GU_TRAFFIC, 2.579e9), (bench.PF_DN_TRAFFIC, 1.944e9)):
+        v = bench.measured_traffic(tr, bench.PREFILL_SOURCES)
+        if bench.csrc_digest(bench.PREFILL_SOURCES) == tr["sources"]:
+            assert 0.99 * alg < v < 2.0 * alg
+        else:
+            assert v is None
 
 
 def test_sweep_sets_are_valid_pass_sizes():
