@@ -28,6 +28,10 @@ TINY = synth.CONFIGS["tiny"]
 # 384 intermediate columns: three 128-column blocks for gate/up, the last one half empty.
 MID = dataclasses.replace(TINY, name="mid", H=512, I=384, E=16, k=4, seed=1101, weight_seed=1101)
 PREFILL = synth.CONFIGS["prefill"]
+# Widths that are multiples of 64 only: gate/up's second 128-column item has one
+# live 64-column tile, down's second 256-column item one live tile of four, and
+# the group counts (10 and 6) take the shallow weight ring.
+ODD = dataclasses.replace(TINY, name="odd", H=320, I=192, E=8, k=3, seed=1111, weight_seed=1111)
 
 
 def run_prefill(layer: DeviceLayer, x_bits, logits) -> dict:
@@ -99,6 +103,18 @@ def test_mid_prefill_matches_oracle(mid_layer, R):
     lg = synth.logits(MID.seed, R, R, MID.E, bias_sigma=0.5)
     res = run_prefill(mid_layer, x, lg)
     ref = oracle_rows(mid_layer, x, lg)
+    worst = check_rows(res, ref)
+    log("  worst per-row relative error %.2e" % worst)
+
+
+@pytest.mark.parametrize("R", [5, 300])
+def test_odd_widths_prefill_matches_oracle(R):
+    layer = DeviceLayer(ODD, 0)
+    log("prefill odd widths H=%d I=%d R=%d" % (ODD.H, ODD.I, R))
+    x = synth.activations(ODD.seed, R, R, ODD.H)
+    lg = synth.logits(ODD.seed, R, R, ODD.E, bias_sigma=0.5)
+    res = run_prefill(layer, x, lg)
+    ref = oracle_rows(layer, x, lg)
     worst = check_rows(res, ref)
     log("  worst per-row relative error %.2e" % worst)
 
