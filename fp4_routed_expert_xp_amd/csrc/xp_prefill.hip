@@ -169,20 +169,30 @@ __device__ __forceinline__ Item item_at(int i, int n_tiles, const int* sP, int E
     return it;
 }
 
-// The workgroup's range of items: the eight XCDs take contiguous eighths of
-// the item list (workgroup b runs on XCD b % 8), each spread over its workgroups.
-struct Deal {
-    int first, end, step;
-};
+// Item dealing. The eight XCDs own contiguous eighths of the item list
+// (workgroup b runs on XCD b % 8), so the workgroups that share an expert's
+// rows and weights share an L2. Items differ up to fourfold in cost (2 to 8
+// slabs), so a workgroup takes its next item from its XCD's counter and, once
+// that range is done, from the other XCDs' in turn. The counters are int32
+// slots of the workspace header, zeroed by pf_counters_zero before each launch.
+constexpr int kPfCtrGateUp = 32;   // header slots 32 .. 39
+constexpr int kPfCtrDown = 40;     // header slots 40 .. 47
 
-__device__ __forceinline__ Deal deal(int total) {
-    const int g8 = gridDim.x >> 3;
-    const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
-    Deal d;
-    d.first = (int)(((long long)total * x) >> 3) + j;
-    d.end = (int)(((long long)total * (x + 1)) >> 3);
-    d.step = g8;
-    return d;
+__global__ void pf_counters_zero(int32_t* __restrict__ ctr) {
+    if (threadIdx.x < 8) ctr[threadIdx.x] = 0;
+}
+
+// Next item of this workgroup, or -1 once every range is done (one thread).
+__device__ __forceinline__ int next_item(int32_t* ctr, int total) {
+    const int x0 = blockIdx.x & 7;
+    for (int j = 0; j < 8; ++j) {
+        const int x = (x0 + j) & 7;
+        const int lo = (int)(((long long)total * x) >> 3), hi = (int)(((long long)total * (x + 1)) >> 3);
+        if (lo >= hi) continue;
+        const int v = lo + atomicAdd(&ctr[x], 1);
+        if (v < hi) return v;
+    }
+    return -1;
 }
 
 // ------------------------------------------------------------------ gate/up
@@ -445,7 +455,7 @@ struct GuRun {
 __global__ __launch_bounds__(kPThreads, XP_PF_GU_WAVES) void prefill_gateup_kernel(
     const xp_expert* __restrict__ experts, const uint16_t* __restrict__ x, const int32_t* __restrict__ count,
     const int32_t* __restrict__ offset, const int32_t* __restrict__ entry, int E, int k, int H, int I,
-    float* __restrict__ act) {
+    float* __restrict__ act, int32_t* __restrict__ ctr) {
     __shared__ __attribute__((aligned(1024))) uint8_t sX[XP_PF_GU_NB * kXTile];
     __shared__ __attribute__((aligned(1024))) uint8_t sW[XP_PF_GU_NB * kWTile];
     __shared__ __attribute__((aligned(256))) uint8_t sS[XP_PF_GU_NB * kSTile];
@@ -457,14 +467,18 @@ __global__ __launch_bounds__(kPThreads, XP_PF_GU_WAVES) void prefill_gateup_kern
     const int n_tiles = (I + kPN - 1) / kPN;
     const int total = block_prefix<kPThreads>(count, E, sP, swave) * n_tiles;
     const GuArgs a{x, experts, act, k, H, I, H / 32};
-    const Deal dl = deal(total);
+    __shared__ int sItem;
 
-    for (int i = dl.first; i < dl.end; i += dl.step) {
+    for (;;) {
+        if (t == 0) sItem = next_item(ctr, total);
+        __syncthreads();
+        const int i = sItem;
+        if (i < 0) break;
         const Item it = item_at(i, n_tiles, sP, E, count);
         if (t < kPM) sEntry[t] = entry[offset[it.e] + it.m0 + min(t, it.rows - 1)];
         __syncthreads();
         dispatch_item<XP_PF_GU_DMAX>(it.rows, a.G, GuRun{a, it, sX, sW, sS, sEntry});
-        __syncthreads();  // sEntry and sA are rewritten by the next item
+        __syncthreads();  // sItem, sEntry and the ring are rewritten by the next item
     }
 }
 
@@ -630,7 +644,7 @@ struct DnRun {
 __global__ __launch_bounds__(kDnThreads, XP_PF_DN_WAVES) void prefill_down_kernel(
     const xp_expert* __restrict__ experts, const float* __restrict__ act, const int32_t* __restrict__ count,
     const int32_t* __restrict__ offset, const int32_t* __restrict__ entry, int E, int H, int I,
-    float* __restrict__ out) {
+    float* __restrict__ out, int32_t* __restrict__ ctr) {
     // act halves, two LDS buffers of two groups each: [buffer][group][128 rows x 64 B], swizzled
     __shared__ __attribute__((aligned(1024))) uint8_t sHi[2 * 2 * kXTile];
     __shared__ __attribute__((aligned(1024))) uint8_t sLo[2 * 2 * kXTile];
@@ -642,9 +656,13 @@ __global__ __launch_bounds__(kDnThreads, XP_PF_DN_WAVES) void prefill_down_kerne
     const int n_tiles = (H + kDnCols - 1) / kDnCols;
     const int total = block_prefix<kDnThreads>(count, E, sP, swave) * n_tiles;
     const DnArgs a{act, experts, out, H, I, I / 32};
-    const Deal dl = deal(total);
+    __shared__ int sItem;
 
-    for (int i = dl.first; i < dl.end; i += dl.step) {
+    for (;;) {
+        if (t == 0) sItem = next_item(ctr, total);
+        __syncthreads();
+        const int i = sItem;
+        if (i < 0) break;
         const Item it = item_at(i, n_tiles, sP, E, count);
         if (t < kPM) sEntry[t] = entry[offset[it.e] + it.m0 + min(t, it.rows - 1)];
         __syncthreads();
@@ -677,33 +695,37 @@ static int prefill_grid(int rows, int k, int E, int n_tiles, int per_cu) {
 using namespace xp;
 
 XP_API int xp_prefill_gateup(const xp_dims* dims, int32_t rows, const uint16_t* x, const xp_expert* experts,
-                             const void* workspace, size_t ws_bytes, float* act, void* stream) {
+                             void* workspace, size_t ws_bytes, float* act, void* stream) {
     int st = check_dims(dims);
     if (st != XP_OK) return st;
     if (rows < 0) return XP_ERR_SHAPE;
     if (rows == 0) return XP_OK;
     if (!x || !experts || !workspace || !act) return XP_ERR_NULL;
     if (ws_bytes < ws_layout(dims, rows).total) return XP_ERR_WORKSPACE;
-    WsPtrs w = ws_ptrs(const_cast<void*>(workspace), dims, rows);
+    WsPtrs w = ws_ptrs(workspace, dims, rows);
     const int n_tiles = (dims->inter + kPN - 1) / kPN;
     const int grid = prefill_grid(rows, dims->top_k, dims->n_experts, n_tiles, XP_PF_GU_WAVES);
+    int32_t* ctr = w.hdr + kPfCtrGateUp;
+    hipLaunchKernelGGL(pf_counters_zero, dim3(1), dim3(64), 0, (hipStream_t)stream, ctr);
     hipLaunchKernelGGL(prefill_gateup_kernel, dim3(grid), dim3(kPThreads), 0, (hipStream_t)stream, experts, x,
-                       w.count, w.offset, w.entry, dims->n_experts, dims->top_k, dims->hidden, dims->inter, act);
+                       w.count, w.offset, w.entry, dims->n_experts, dims->top_k, dims->hidden, dims->inter, act, ctr);
     return launch_status();
 }
 
 XP_API int xp_prefill_down(const xp_dims* dims, int32_t rows, const float* act, const xp_expert* experts,
-                           const void* workspace, size_t ws_bytes, float* out, void* stream) {
+                           void* workspace, size_t ws_bytes, float* out, void* stream) {
     int st = check_dims(dims);
     if (st != XP_OK) return st;
     if (rows < 0) return XP_ERR_SHAPE;
     if (rows == 0) return XP_OK;
     if (!act || !experts || !workspace || !out) return XP_ERR_NULL;
     if (ws_bytes < ws_layout(dims, rows).total) return XP_ERR_WORKSPACE;
-    WsPtrs w = ws_ptrs(const_cast<void*>(workspace), dims, rows);
+    WsPtrs w = ws_ptrs(workspace, dims, rows);
     const int n_tiles = (dims->hidden + kDnCols - 1) / kDnCols;
     const int grid = prefill_grid(rows, dims->top_k, dims->n_experts, n_tiles, XP_PF_DN_WAVES);
+    int32_t* ctr = w.hdr + kPfCtrDown;
+    hipLaunchKernelGGL(pf_counters_zero, dim3(1), dim3(64), 0, (hipStream_t)stream, ctr);
     hipLaunchKernelGGL(prefill_down_kernel, dim3(grid), dim3(kDnThreads), 0, (hipStream_t)stream, experts, act,
-                       w.count, w.offset, w.entry, dims->n_experts, dims->hidden, dims->inter, out);
+                       w.count, w.offset, w.entry, dims->n_experts, dims->hidden, dims->inter, out, ctr);
     return launch_status();
 }

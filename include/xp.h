@@ -106,7 +106,8 @@ size_t xp_workspace_bytes(const xp_dims* dims, int32_t max_rows);
 /* Byte offsets of the fields of the plan for max_rows rows (host, pure), for
  * callers that read the plan back. A plan made for R rows uses the offsets for
  * R, so the calls that read one plan must pass the same row count:
- *   off[0] header: int32 [0] = gate/up passes, [1] = down passes
+ *   off[0] header: int32 [0] = gate/up passes, [1] = down passes,
+ *                  [32..47] work counters of the prefill calls
  *   off[1] count  int32 [E]          rows per expert
  *   off[2] offset int32 [E+1]        first entry of each expert
  *   off[3] entry  int32 [R*k]        row*k + slot, experts ascending, rows ascending
@@ -203,18 +204,22 @@ int xp_decode_static(const xp_dims* dims, int32_t rows, const float* logits, con
  * xp_gateup_rows / xp_down_rows, and meet the per-row tolerance (max |err| /
  * max |ref| <= 1e-3 against the float64 definition) instead. act must be
  * finite for xp_prefill_down (an infinite act gives NaN in out). Any row count
- * is accepted; xp_combine finishes the layer. [#2983, "What this changes" for
+ * is accepted; xp_combine finishes the layer. Each call launches a one-block
+ * kernel that zeroes its work counters in the workspace header (int32 slots
+ * 32..39 for gate/up, 40..47 for down; the plan is only read), then the
+ * contraction, whose workgroups take items from those counters: prefill calls
+ * that share a workspace must not overlap. [#2983, "What this changes" for
  * the layer math; the 4,096-row prompt chunk is the serving page's default] */
 
 /* act[row][slot][I] fp32 = silu(W_gate x_row) * (W_up x_row) for every entry of
  * the plan. x: [rows][H] bf16 bit patterns. Same buffers as xp_gateup_rows. */
 int xp_prefill_gateup(const xp_dims* dims, int32_t rows, const uint16_t* x, const xp_expert* experts,
-                      const void* workspace, size_t ws_bytes, float* act, void* stream);
+                      void* workspace, size_t ws_bytes, float* act, void* stream);
 
 /* out[row][slot][H] fp32 = W_down act[row][slot] for every entry of the plan.
  * Same buffers as xp_down_rows. */
 int xp_prefill_down(const xp_dims* dims, int32_t rows, const float* act, const xp_expert* experts,
-                    const void* workspace, size_t ws_bytes, float* out, void* stream);
+                    void* workspace, size_t ws_bytes, float* out, void* stream);
 
 /* ------------------------------------------------------ bf16 storage
  * Variants that store act or y as bf16 (the width x arrives in [#2983, "What

@@ -119,6 +119,31 @@ def test_odd_widths_prefill_matches_oracle(R):
     log("  worst per-row relative error %.2e" % worst)
 
 
+def test_prefill_repeated_on_one_plan(tiny_layer):
+    # Each call zeroes its work counters in the workspace header before its
+    # contraction, so calls repeated on one plan give the same bits.
+    R = 300
+    d = tiny_layer.d
+    x = to_dev(synth.activations(TINY.seed, 31, R, TINY.H))
+    lg = to_dev(synth.logits(TINY.seed, 31, R, TINY.E).astype(np.float32))
+    ws = torch.zeros(max(xp.xp_workspace_bytes(d, R), 256), dtype=torch.uint8, device="cuda")
+    topk_id = torch.empty((R, d.top_k), dtype=torch.int32, device="cuda")
+    topk_w = torch.empty((R, d.top_k), dtype=torch.float32, device="cuda")
+    xp.xp_route_bucket(d, R, lg, topk_id, topk_w, ws)
+    acts, outs = [], []
+    for _ in range(3):
+        act = torch.full((R, d.top_k, d.inter), float("nan"), dtype=torch.float32, device="cuda")
+        out = torch.full((R, d.top_k, d.hidden), float("nan"), dtype=torch.float32, device="cuda")
+        xp.xp_prefill_gateup(d, R, x, tiny_layer.table, ws, act)
+        xp.xp_prefill_down(d, R, act, tiny_layer.table, ws, out)
+        torch.cuda.synchronize()
+        acts.append(act.cpu().numpy().view(np.uint32))
+        outs.append(out.cpu().numpy().view(np.uint32))
+    for i in (1, 2):
+        assert np.array_equal(acts[i], acts[0]) and np.array_equal(outs[i], outs[0])
+    assert np.all(np.isfinite(acts[0].view(np.float32))) and np.all(np.isfinite(outs[0].view(np.float32)))
+
+
 def test_prefill_skewed_expert(tiny_layer):
     # Every row on experts 0 and 1 (one expert with all R rows in slot 0):
     # ten full blocks and a tail of 5.
