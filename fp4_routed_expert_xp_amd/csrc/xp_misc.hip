@@ -7,22 +7,37 @@ namespace xp {
 // y[r][n] = fma chain from +0 over slots j = 0..k-1 of w[r][j] * out[r][j][n];
 // Y16 stores it as bf16 (round to nearest even) instead of fp32.
 // [#2983, "Receipt": the combine output is the third tensor the probe holds equal]
-template <bool Y16>
+// Each thread takes V consecutive outputs of a row (V = 4: 16-byte loads of out
+// for large batches; V = 1 keeps enough workgroups in flight for small ones).
+// H is a multiple of 64, so a run of V never crosses a row.
+template <bool Y16, int V>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ out, const float* __restrict__ w,
                                                       int R, int H, int k, void* __restrict__ y) {
-    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    typedef __attribute__((ext_vector_type(V))) float fv;
+    const size_t idx = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * V;
     if (idx >= (size_t)R * H) return;
     const int r = (int)(idx / H);
     const int n = (int)(idx - (size_t)r * H);
     const float* o = out + (size_t)r * k * H + n;
     const float* wr = w + (size_t)r * k;
-    float s = 0.0f;
-    for (int j = 0; j < k; ++j) s = __builtin_fmaf(wr[j], o[(size_t)j * H], s);
-    if (Y16)
-        ((uint16_t*)y)[idx] = bf16_rne(s);
-    else
-        ((float*)y)[idx] = s;
+    fv s = (fv)0.0f;
+    for (int j = 0; j < k; ++j) {
+        const float wj = wr[j];
+        const fv v = *(const fv*)(o + (size_t)j * H);
+#pragma unroll
+        for (int c = 0; c < V; ++c) s[c] = __builtin_fmaf(wj, v[c], s[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < V; ++c) {
+        if (Y16)
+            ((uint16_t*)y)[idx + c] = bf16_rne(s[c]);
+        else
+            ((float*)y)[idx + c] = s[c];
+    }
 }
+
+// Batches of at least this many outputs take four per thread.
+constexpr size_t kCombineWide = (size_t)4 * 256 * 1024;
 
 // Plain [N][K/2] codes / [N][K/32] scales -> tiles of 64 columns, group-major
 // inside a tile (one 1 KiB block of codes and one 64-byte block of scales per
@@ -53,13 +68,21 @@ static int combine_common(const xp_dims* dims, int32_t rows, const float* out, c
     if (rows == 0) return XP_OK;
     if (!out || !topk_w || !y) return XP_ERR_NULL;
     const size_t n = (size_t)rows * dims->hidden;
-    const unsigned grid = (unsigned)((n + 255) / 256);
-    if (y16)
-        hipLaunchKernelGGL(combine_kernel<true>, dim3(grid), dim3(256), 0, (hipStream_t)stream, out, topk_w, rows,
-                           dims->hidden, dims->top_k, y);
-    else
-        hipLaunchKernelGGL(combine_kernel<false>, dim3(grid), dim3(256), 0, (hipStream_t)stream, out, topk_w, rows,
-                           dims->hidden, dims->top_k, y);
+    hipStream_t s = (hipStream_t)stream;
+    const int H = dims->hidden, k = dims->top_k;
+    if (n >= kCombineWide) {
+        const unsigned grid = (unsigned)((n / 4 + 255) / 256);
+        if (y16)
+            hipLaunchKernelGGL((combine_kernel<true, 4>), dim3(grid), dim3(256), 0, s, out, topk_w, rows, H, k, y);
+        else
+            hipLaunchKernelGGL((combine_kernel<false, 4>), dim3(grid), dim3(256), 0, s, out, topk_w, rows, H, k, y);
+    } else {
+        const unsigned grid = (unsigned)((n + 255) / 256);
+        if (y16)
+            hipLaunchKernelGGL((combine_kernel<true, 1>), dim3(grid), dim3(256), 0, s, out, topk_w, rows, H, k, y);
+        else
+            hipLaunchKernelGGL((combine_kernel<false, 1>), dim3(grid), dim3(256), 0, s, out, topk_w, rows, H, k, y);
+    }
     return launch_status();
 }
 

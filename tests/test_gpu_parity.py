@@ -188,6 +188,26 @@ def test_down_and_combine_bit_equal_to_fp32_replay(tiny_layer):
         assert np.array_equal(bits(y[r]), bits(oracle.combine32(w[r], o[r]))), r
 
 
+def test_wide_combine_bit_equal_to_fp32_replay():
+    # 300 rows of width 4096: 1,228,800 outputs, enough for the four-per-thread
+    # form. Every row against the fp32 replay of the slot-order chain, and the
+    # bf16 form against that result rounded to nearest even.
+    R, H, k = 300, 4096, 8
+    d = xp.dims(H, 2048, 256, k)
+    rng = np.random.default_rng(33)
+    o = rng.standard_normal((R, k, H)).astype(np.float32)
+    w = rng.random((R, k)).astype(np.float32)
+    y = torch.empty((R, H), dtype=torch.float32, device="cuda")
+    y16 = torch.empty((R, H), dtype=torch.int16, device="cuda")
+    xp.xp_combine(d, R, to_dev(o), to_dev(w), y)
+    xp.xp_combine_y16(d, R, to_dev(o), to_dev(w), y16)
+    torch.cuda.synchronize()
+    y, y16 = y.cpu().numpy(), y16.cpu().numpy()
+    for r in range(R):
+        assert np.array_equal(bits(y[r]), bits(oracle.combine32(w[r], o[r]))), r
+    assert np.array_equal(y16, synth.f32_to_bf16_bits(y).view(np.int16))
+
+
 # --------------------------------------------------------------- release widths
 @pytest.mark.parametrize("name", ["one_row", "four_same", "sixteen_random"])
 def test_release_layer_matches_oracle(release_layer, name):
