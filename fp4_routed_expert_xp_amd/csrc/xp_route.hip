@@ -66,10 +66,23 @@ __global__ __launch_bounds__(1024) void route_plan_kernel(int E, int nblk, WsPtr
     __shared__ int wsum[48];
     const int e = threadIdx.x;
     if (e < E) {
+        // the blocks' masks sixteen at a time (all loads in flight together),
+        // then their running counts
+        constexpr int kB = 16;
+        const unsigned long long* __restrict__ mk = w.masks + e;
+        int32_t* __restrict__ bs = w.base + e;
         int c = 0;
-        for (int b = 0; b < nblk; ++b) {
-            w.base[(size_t)b * E + e] = c;
-            c += __popcll(w.masks[(size_t)b * E + e]);
+        for (int b0 = 0; b0 < nblk; b0 += kB) {
+            int pc[kB];
+#pragma unroll
+            for (int i = 0; i < kB; ++i) pc[i] = __popcll(mk[(size_t)min(b0 + i, nblk - 1) * E]);
+#pragma unroll
+            for (int i = 0; i < kB; ++i) {
+                if (b0 + i < nblk) {
+                    bs[(size_t)(b0 + i) * E] = c;
+                    c += pc[i];
+                }
+            }
         }
         scnt[e] = c;
     }
