@@ -48,8 +48,8 @@ FP8_TRAFFIC = dict(sources="15929da9", fetch_kib=8532.4, write_kib=133.3)
 FP8_SOURCES = ("xp_fp8.hip", "xp_common.h")
 # The same for the two prefill kernels on the 4,096-row chunk (mean over 4 seeded
 # layers), tied to xp_prefill.hip and its headers.
-PF_GU_TRAFFIC = dict(sources="ea021dc9", fetch_kib=1780229.6, write_kib=262174.4)
-PF_DN_TRAFFIC = dict(sources="ea021dc9", fetch_kib=973971.3, write_kib=524300.5)
+PF_GU_TRAFFIC = dict(sources="0fc0abad", fetch_kib=1732689.0, write_kib=262618.5)
+PF_DN_TRAFFIC = dict(sources="0fc0abad", fetch_kib=900811.7, write_kib=524567.7)
 PREFILL_SOURCES = ("xp_prefill.hip", "xp_prefill_asm.h", "xp_common.h")
 
 
