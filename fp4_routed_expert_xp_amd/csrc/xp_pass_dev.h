@@ -91,13 +91,23 @@ __device__ __forceinline__ float e8m0(uint32_t b) {
 // every leaf walks ceil(G/8) of them, rounded up to whole loop trips of 2*D
 // groups, so the loop body has no branches (the ring's wait counts then follow
 // it exactly): a group past the end re-reads group G-1 and its product is
-// discarded by a select.
+// discarded by a select. EXACT = the walks end on the last group (G a
+// multiple of 8 whose leaves' group counts are multiples of 2*D), so no group
+// is past the end and the select is left out.
 // Activations: bf16 rows (xr[r] = the row's 16-bit pairs), or, when CODED,
 // E4M3FN codes (xr[r] = the row's code bytes, read as pairs) with one E8M0
 // scale per group (sr[r] = the row's scale bytes); a coded value enters the
 // chain as e4m3(code) * 2^(scale - 127), computed exactly in fp32, so the chain
 // is the bf16 path's on those values.
-template <int P, bool CODED>
+// True when every leaf's walk (ceil(G/8) groups rounded up to trips of 2*D)
+// ends exactly on its last group.
+template <int P>
+__device__ __forceinline__ bool exact_walk(int G) {
+    constexpr int D = GuDepth<P>::value;
+    return (G & 7) == 0 && ((G >> 3) % (2 * D)) == 0;
+}
+
+template <int P, bool CODED, bool EXACT>
 __device__ __forceinline__ void gu_leaf(gcodes_t cc, gbytes_t ss, const uint32_t* const (&xr)[P],
                                         const uint8_t* const (&sr)[P], int leaf, int G, int lane, float (&acc)[P]) {
     constexpr int D = GuDepth<P>::value;
@@ -151,7 +161,7 @@ __device__ __forceinline__ void gu_leaf(gcodes_t cc, gbytes_t ss, const uint32_t
             { float w[8]; decode8(cw[1], w); Chain<P>::tail1(w, xa, xb, p); }
             { float w[8]; decode8(cw[2], w); Chain<P>::tail2(w, xa, xb, p); }
             { float w[8]; decode8(cw[3], w); Chain<P>::tail3(w, xa, xb, p); }
-            const bool valid = leaf + 8 * i < G;
+            const bool valid = EXACT || leaf + 8 * i < G;
 #pragma unroll
             for (int r = 0; r < P; ++r) {
                 const float v = __builtin_fmaf(p[r], sc, acc[r]);
@@ -172,7 +182,7 @@ __device__ __forceinline__ void gu_leaf(gcodes_t cc, gbytes_t ss, const uint32_t
 // activations once, and the gate chain then the up chain run over the same
 // converted activations. Per matrix and row this is gu_leaf's arithmetic
 // exactly (the same chain, scaled fma and leaf), so the bits are gu_leaf's.
-template <int P, bool CODED>
+template <int P, bool CODED, bool EXACT>
 __device__ __forceinline__ void gu_leaf2(gcodes_t cg, gbytes_t sg, gcodes_t cu, gbytes_t su,
                                          const uint32_t* const (&xr)[P], const uint8_t* const (&sr)[P], int leaf,
                                          int G, int lane, float (&accg)[P], float (&accu)[P]) {
@@ -233,7 +243,7 @@ __device__ __forceinline__ void gu_leaf2(gcodes_t cg, gbytes_t sg, gcodes_t cu, 
             { float w[8]; decode8(cwg[1], w); Chain<P>::tail1(w, xa, xb, p); }
             { float w[8]; decode8(cwg[2], w); Chain<P>::tail2(w, xa, xb, p); }
             { float w[8]; decode8(cwg[3], w); Chain<P>::tail3(w, xa, xb, p); }
-            const bool valid = leaf + 8 * i < G;
+            const bool valid = EXACT || leaf + 8 * i < G;
 #pragma unroll
             for (int r = 0; r < P; ++r) {
                 const float v = __builtin_fmaf(p[r], scg, accg[r]);
@@ -296,14 +306,20 @@ __device__ __forceinline__ void gu_item(const xp_expert* __restrict__ experts, c
         const gcodes_t cc = (gcodes_t)(up ? ex.up_codes : ex.gate_codes) + tile_chunks + lane;
         const gbytes_t ss = (gbytes_t)(up ? ex.up_scales : ex.gate_scales) + tile_chunks + lane;
         float acc[P];
-        gu_leaf<P, CODED>(cc, ss, xr, sr, leaf, G, lane, acc);
+        if (exact_walk<P>(G))
+            gu_leaf<P, CODED, true>(cc, ss, xr, sr, leaf, G, lane, acc);
+        else
+            gu_leaf<P, CODED, false>(cc, ss, xr, sr, leaf, G, lane, acc);
 #pragma unroll
         for (int r = 0; r < P; ++r) red[(wave * P + r) * kTile + lane] = acc[r];
     } else {
         float accg[P], accu[P];
-        gu_leaf2<P, CODED>((gcodes_t)ex.gate_codes + tile_chunks + lane, (gbytes_t)ex.gate_scales + tile_chunks + lane,
-                           (gcodes_t)ex.up_codes + tile_chunks + lane, (gbytes_t)ex.up_scales + tile_chunks + lane,
-                           xr, sr, leaf, G, lane, accg, accu);
+        const gcodes_t cg = (gcodes_t)ex.gate_codes + tile_chunks + lane, cu = (gcodes_t)ex.up_codes + tile_chunks + lane;
+        const gbytes_t sg = (gbytes_t)ex.gate_scales + tile_chunks + lane, su = (gbytes_t)ex.up_scales + tile_chunks + lane;
+        if (exact_walk<P>(G))
+            gu_leaf2<P, CODED, true>(cg, sg, cu, su, xr, sr, leaf, G, lane, accg, accu);
+        else
+            gu_leaf2<P, CODED, false>(cg, sg, cu, su, xr, sr, leaf, G, lane, accg, accu);
 #pragma unroll
         for (int r = 0; r < P; ++r) {
             red[(leaf * P + r) * kTile + lane] = accg[r];

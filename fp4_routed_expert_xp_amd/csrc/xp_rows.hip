@@ -181,8 +181,9 @@ __global__ __launch_bounds__(64 * WAVES, 16 / WAVES) void route_gateup_rows_kern
 // T: output tiles per item (1, or 2: tiles 2*tile and 2*tile+1). With two, each
 // wave walks its leaf of both tiles over one load of the rows' act values, so
 // twice the weight bytes are in flight per wave; per tile the chain, scaled
-// fma, leaf order and tree are the one-tile item's.
-template <int P, bool A16, int T>
+// fma, leaf order and tree are the one-tile item's. EXACT: every leaf's walk
+// ends on its last group, so no product is discarded (see gu_leaf).
+template <int P, bool A16, int T, bool EXACT>
 __device__ __forceinline__ void dn_item(const xp_expert* __restrict__ experts, const void* __restrict__ act,
                         const int32_t* __restrict__ entry, int4 ps, int tile, int H, int I,
                         float* __restrict__ out, float* red) {
@@ -257,7 +258,7 @@ __device__ __forceinline__ void dn_item(const xp_expert* __restrict__ experts, c
                 load(set ^ 1, s, i + D);
                 { float w[8]; decode8(cw[0][0], w); Chain<P>::head_f32(w, xa, xb, p); }
             }
-            const bool valid = leaf + 8 * i < G;
+            const bool valid = EXACT || leaf + 8 * i < G;
 #pragma unroll
             for (int q = 0; q < T; ++q) {
                 if (q > 0) { float w[8]; decode8(cw[q][0], w); Chain<P>::head_f32(w, xa, xb, p); }
@@ -300,6 +301,24 @@ __device__ __forceinline__ void dn_item(const xp_expert* __restrict__ experts, c
 }
 
 // Down passes: work item = (pass, T consecutive output tiles).
+// True when every leaf's walk over G groups (rounded up to trips of 2*D)
+// ends exactly on its last group, so no product needs discarding.
+template <int P>
+__device__ __forceinline__ bool exact_dn_walk(int G) {
+    constexpr int D = DnDepth<P>::value;
+    return (G & 7) == 0 && ((G >> 3) % (2 * D)) == 0;
+}
+
+template <int P, bool A16, int T>
+__device__ __forceinline__ void dn_item_any(const xp_expert* __restrict__ experts, const void* __restrict__ act,
+                                            const int32_t* __restrict__ entry, int4 ps, int tile, int H, int I,
+                                            float* __restrict__ out, float* red) {
+    if (exact_dn_walk<P>(I >> 5))
+        dn_item<P, A16, T, true>(experts, act, entry, ps, tile, H, I, out, red);
+    else
+        dn_item<P, A16, T, false>(experts, act, entry, ps, tile, H, I, out, red);
+}
+
 template <bool A16, int T>
 __global__ __launch_bounds__(512, 4) void down_kernel(const xp_expert* __restrict__ experts,
                                                       const void* __restrict__ act,
@@ -316,14 +335,14 @@ __global__ __launch_bounds__(512, 4) void down_kernel(const xp_expert* __restric
         const int tile = item - pass * n_items_pass;
         const int4 ps = passes[pass];
         switch (ps.w) {
-            case 1: dn_item<1, A16, T>(tab, act, entry, ps, tile, H, I, out, red); break;
-            case 2: dn_item<2, A16, T>(tab, act, entry, ps, tile, H, I, out, red); break;
-            case 3: dn_item<3, A16, T>(tab, act, entry, ps, tile, H, I, out, red); break;
-            case 4: dn_item<4, A16, T>(tab, act, entry, ps, tile, H, I, out, red); break;
-            case 5: dn_item<5, A16, T>(tab, act, entry, ps, tile, H, I, out, red); break;
-            case 6: dn_item<6, A16, T>(tab, act, entry, ps, tile, H, I, out, red); break;
-            case 7: dn_item<7, A16, T>(tab, act, entry, ps, tile, H, I, out, red); break;
-            case 8: dn_item<8, A16, T>(tab, act, entry, ps, tile, H, I, out, red); break;
+            case 1: dn_item_any<1, A16, T>(tab, act, entry, ps, tile, H, I, out, red); break;
+            case 2: dn_item_any<2, A16, T>(tab, act, entry, ps, tile, H, I, out, red); break;
+            case 3: dn_item_any<3, A16, T>(tab, act, entry, ps, tile, H, I, out, red); break;
+            case 4: dn_item_any<4, A16, T>(tab, act, entry, ps, tile, H, I, out, red); break;
+            case 5: dn_item_any<5, A16, T>(tab, act, entry, ps, tile, H, I, out, red); break;
+            case 6: dn_item_any<6, A16, T>(tab, act, entry, ps, tile, H, I, out, red); break;
+            case 7: dn_item_any<7, A16, T>(tab, act, entry, ps, tile, H, I, out, red); break;
+            case 8: dn_item_any<8, A16, T>(tab, act, entry, ps, tile, H, I, out, red); break;
             default: break;
         }
     }
@@ -435,7 +454,7 @@ __global__ __launch_bounds__(1024) void down_combine_one_row_kernel(
 constexpr int kFusedEntries = 64;
 
 
-template <int P>
+template <int P, bool EXACT>
 __device__ __forceinline__ void dc_pass_leaf(const xp_expert* __restrict__ experts, const float* __restrict__ act,
                                              const int32_t* __restrict__ entry, int4 ps, int n, int I, int leaf,
                                              int lane, float* red_wave /* [kMaxPass][kTile] */) {
@@ -479,7 +498,7 @@ __device__ __forceinline__ void dc_pass_leaf(const xp_expert* __restrict__ exper
             { float w[8]; decode8(cw[1], w); Chain<P>::tail1(w, xa, xb, p); }
             { float w[8]; decode8(cw[2], w); Chain<P>::tail2(w, xa, xb, p); }
             { float w[8]; decode8(cw[3], w); Chain<P>::tail3(w, xa, xb, p); }
-            const bool valid = leaf + 8 * i < G;
+            const bool valid = EXACT || leaf + 8 * i < G;
 #pragma unroll
             for (int r = 0; r < P; ++r) {
                 const float v = __builtin_fmaf(p[r], sc, acc[r]);
@@ -518,14 +537,54 @@ __global__ __launch_bounds__(1024) void down_combine_rows_kernel(
         pw = max(pw, max(__builtin_amdgcn_readlane(ps.w, 32), __builtin_amdgcn_readlane(ps.w, 48)));
         float* rw = &red[wave][0];
         switch (pw) {
-            case 1: dc_pass_leaf<1>(experts, act, entry, ps, n, I, leaf, lane, rw); break;
-            case 2: dc_pass_leaf<2>(experts, act, entry, ps, n, I, leaf, lane, rw); break;
-            case 3: dc_pass_leaf<3>(experts, act, entry, ps, n, I, leaf, lane, rw); break;
-            case 4: dc_pass_leaf<4>(experts, act, entry, ps, n, I, leaf, lane, rw); break;
-            case 5: dc_pass_leaf<5>(experts, act, entry, ps, n, I, leaf, lane, rw); break;
-            case 6: dc_pass_leaf<6>(experts, act, entry, ps, n, I, leaf, lane, rw); break;
-            case 7: dc_pass_leaf<7>(experts, act, entry, ps, n, I, leaf, lane, rw); break;
-            case 8: dc_pass_leaf<8>(experts, act, entry, ps, n, I, leaf, lane, rw); break;
+            case 1:
+                if (exact_dn_walk<1>(I >> 5))
+                    dc_pass_leaf<1, true>(experts, act, entry, ps, n, I, leaf, lane, rw);
+                else
+                    dc_pass_leaf<1, false>(experts, act, entry, ps, n, I, leaf, lane, rw);
+                break;
+            case 2:
+                if (exact_dn_walk<2>(I >> 5))
+                    dc_pass_leaf<2, true>(experts, act, entry, ps, n, I, leaf, lane, rw);
+                else
+                    dc_pass_leaf<2, false>(experts, act, entry, ps, n, I, leaf, lane, rw);
+                break;
+            case 3:
+                if (exact_dn_walk<3>(I >> 5))
+                    dc_pass_leaf<3, true>(experts, act, entry, ps, n, I, leaf, lane, rw);
+                else
+                    dc_pass_leaf<3, false>(experts, act, entry, ps, n, I, leaf, lane, rw);
+                break;
+            case 4:
+                if (exact_dn_walk<4>(I >> 5))
+                    dc_pass_leaf<4, true>(experts, act, entry, ps, n, I, leaf, lane, rw);
+                else
+                    dc_pass_leaf<4, false>(experts, act, entry, ps, n, I, leaf, lane, rw);
+                break;
+            case 5:
+                if (exact_dn_walk<5>(I >> 5))
+                    dc_pass_leaf<5, true>(experts, act, entry, ps, n, I, leaf, lane, rw);
+                else
+                    dc_pass_leaf<5, false>(experts, act, entry, ps, n, I, leaf, lane, rw);
+                break;
+            case 6:
+                if (exact_dn_walk<6>(I >> 5))
+                    dc_pass_leaf<6, true>(experts, act, entry, ps, n, I, leaf, lane, rw);
+                else
+                    dc_pass_leaf<6, false>(experts, act, entry, ps, n, I, leaf, lane, rw);
+                break;
+            case 7:
+                if (exact_dn_walk<7>(I >> 5))
+                    dc_pass_leaf<7, true>(experts, act, entry, ps, n, I, leaf, lane, rw);
+                else
+                    dc_pass_leaf<7, false>(experts, act, entry, ps, n, I, leaf, lane, rw);
+                break;
+            case 8:
+                if (exact_dn_walk<8>(I >> 5))
+                    dc_pass_leaf<8, true>(experts, act, entry, ps, n, I, leaf, lane, rw);
+                else
+                    dc_pass_leaf<8, false>(experts, act, entry, ps, n, I, leaf, lane, rw);
+                break;
             default: break;
         }
         __syncthreads();
