@@ -34,22 +34,22 @@ CSRC = os.path.join(ROOT, "fp4_routed_expert_xp_amd", "csrc")
 # workload), from two rocprofv3 --pmc runs: FETCH_SIZE, then WRITE_SIZE, in KiB per
 # dispatch (mean over the dispatches of that workload). Each is scaled by what the
 # same counter read for a plain 2 GiB device-to-device copy: FETCH_SIZE read
-# 1,048,611.8 KiB for 2,097,152 KiB fetched, WRITE_SIZE read exactly 2,097,152 KiB.
+# 1,048,613.5 KiB for 2,097,152 KiB fetched, WRITE_SIZE read exactly 2,097,152 KiB.
 # The figure belongs to the sources the kernel is built from (their digest below);
 # after any change to them the bench reports traffic as null.
-TRAFFIC = dict(sources="7aa0b2f7", fetch_kib=34992.6, write_kib=66.4,
-               fetch_factor=2097152 / 1048611.8, write_factor=1.0)
+TRAFFIC = dict(sources="24b08809", fetch_kib=35001.6, write_kib=66.4,
+               fetch_factor=2097152 / 1048613.5, write_factor=1.0)
 ROOFLINE_SOURCES = ("xp_rows.hip", "xp_pass_dev.h", "xp_common.h", "xp_route_dev.h", "xp_chain_asm.h")
 # The same counters for the one-row down + combine launch (down_combine_one_row_kernel).
-DOWN_TRAFFIC = dict(sources="7aa0b2f7", fetch_kib=17729.7, write_kib=144.0)
+DOWN_TRAFFIC = dict(sources="24b08809", fetch_kib=17734.4, write_kib=144.0)
 # The same for the dense FP8 projection kernel at 4096 x 4096 (grid of 256
 # workgroups; mean over its launches at 1, 8 and 16 rows), tied to xp_fp8.hip.
 FP8_TRAFFIC = dict(sources="15929da9", fetch_kib=8532.4, write_kib=133.3)
 FP8_SOURCES = ("xp_fp8.hip", "xp_common.h")
 # The same for the two prefill kernels on the 4,096-row chunk (mean over 4 seeded
 # layers), tied to xp_prefill.hip and its headers.
-PF_GU_TRAFFIC = dict(sources="0fc0abad", fetch_kib=1732689.0, write_kib=262618.5)
-PF_DN_TRAFFIC = dict(sources="0fc0abad", fetch_kib=900811.7, write_kib=524567.7)
+PF_GU_TRAFFIC = dict(sources="0fc0abad", fetch_kib=1731469.8, write_kib=262622.2)
+PF_DN_TRAFFIC = dict(sources="0fc0abad", fetch_kib=900911.9, write_kib=524565.4)
 PREFILL_SOURCES = ("xp_prefill.hip", "xp_prefill_asm.h", "xp_common.h")
 
 
