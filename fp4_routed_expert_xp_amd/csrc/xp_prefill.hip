@@ -215,9 +215,6 @@ __device__ __forceinline__ int next_item(int32_t* ctr, int total) {
 #ifndef XP_PF_GU_DMAX
 #define XP_PF_GU_DMAX 4
 #endif
-#ifndef XP_PF_GU_DA
-#define XP_PF_GU_DA 2
-#endif
 // Down runs one workgroup of XP_PF_DN_WG_WAVES waves per CU when that is 8
 // (items of 256 columns: every act tile staged once serves twice the columns),
 // else two of four waves (items of 128 columns).
@@ -290,7 +287,7 @@ __device__ __forceinline__ void lds_weights(uint32_t waddr, uint32_t saddr, uint
 // every wave's, and reads and decodes the next group's weights while the
 // matrix work drains. A buffer is refilled only after the barrier that follows
 // every wave's last read of it.
-template <int NS, int D, int kDA>
+template <int NS, int D>
 __device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint8_t* sX, uint8_t* sW, uint8_t* sS,
                                         const int* sEntry) {
     constexpr int NB = XP_PF_GU_NB;
@@ -447,7 +444,7 @@ struct GuRun {
     uint8_t* sS;
     const int* sEntry;
     template <int NS, int D>
-    __device__ __forceinline__ void run() const { gu_item<NS, D, XP_PF_GU_DA>(a, it, sX, sW, sS, sEntry); }
+    __device__ __forceinline__ void run() const { gu_item<NS, D>(a, it, sX, sW, sS, sEntry); }
 };
 
 // act[entry][n] = silu(g) * u for the item's rows and columns, where g and u
