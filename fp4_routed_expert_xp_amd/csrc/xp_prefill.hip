@@ -155,16 +155,31 @@ __device__ __forceinline__ bool wave_scales_pow2(uint32_t a, uint32_t b, uint32_
 }
 
 // Item i -> (expert, first row of the block, rows in the block, column block).
+// An expert's items are contiguous. COL_MAJOR orders them column block first:
+// the expert's row blocks of one column block are neighbours, so they are in
+// flight together and read that column block's weights through one L2 (the
+// gate/up order: 1.5% fewer bytes fetched). Otherwise row block first, so one
+// block's act rows are read by neighbouring items (the down order: column block
+// first fetched 5% more there).
 struct Item {
     int e, m0, rows, nt;
 };
 
+template <bool COL_MAJOR>
 __device__ __forceinline__ Item item_at(int i, int n_tiles, const int* sP, int E, const int32_t* __restrict__ count) {
     Item it;
-    const int q = i / n_tiles;
-    it.nt = i - q * n_tiles;
-    it.e = find_expert(sP, E, q);
-    it.m0 = (q - sP[it.e]) * kPM;
+    if constexpr (COL_MAJOR) {
+        it.e = find_expert(sP, E, i / n_tiles);
+        const int nb = sP[it.e + 1] - sP[it.e];      // the expert's row blocks
+        const int local = i - sP[it.e] * n_tiles;
+        it.nt = local / nb;
+        it.m0 = (local - it.nt * nb) * kPM;
+    } else {
+        const int q = i / n_tiles;
+        it.nt = i - q * n_tiles;
+        it.e = find_expert(sP, E, q);
+        it.m0 = (q - sP[it.e]) * kPM;
+    }
     it.rows = min(kPM, count[it.e] - it.m0);
     return it;
 }
@@ -471,7 +486,7 @@ __global__ __launch_bounds__(kPThreads, XP_PF_GU_WAVES) void prefill_gateup_kern
         __syncthreads();
         const int i = sItem;
         if (i < 0) break;
-        const Item it = item_at(i, n_tiles, sP, E, count);
+        const Item it = item_at<true>(i, n_tiles, sP, E, count);
         if (t < kPM) sEntry[t] = entry[offset[it.e] + it.m0 + min(t, it.rows - 1)];
         __syncthreads();
         dispatch_item<XP_PF_GU_DMAX>(it.rows, a.G, GuRun{a, it, sX, sW, sS, sEntry});
@@ -660,7 +675,7 @@ __global__ __launch_bounds__(kDnThreads, XP_PF_DN_WAVES) void prefill_down_kerne
         __syncthreads();
         const int i = sItem;
         if (i < 0) break;
-        const Item it = item_at(i, n_tiles, sP, E, count);
+        const Item it = item_at<false>(i, n_tiles, sP, E, count);
         if (t < kPM) sEntry[t] = entry[offset[it.e] + it.m0 + min(t, it.rows - 1)];
         __syncthreads();
         dispatch_item<XP_PF_DN_DMAX>(it.rows, a.G, DnRun{a, it, sHi, sLo, sEntry});
