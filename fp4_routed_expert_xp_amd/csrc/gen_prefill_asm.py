@@ -21,10 +21,11 @@ so no output register is written after the block.
 gateup: fragment of slab s at x + 1024 s (16 rows x 32 bf16, the swizzled LDS tile),
         four products per slab: acc[s][c][m] += frag * b[2m + c] (c = 16-column
         tile, m = 0 gate / 1 up), i.e. b = {gate 0, gate 1, up 0, up 1}.
-down:   act as bf16 hi and lo halves at hi + 1024 s and lo + 1024 s; per slab
-        acc[s][c] += hi * b[c], then acc[s][c] += lo * b[c], in that order for
-        each accumulator (hi products of both slabs of a pair first, so the two
-        products into one accumulator are four instructions apart).
+down:   act as bf16 hi and lo halves at hi + 1024 s and lo + 1024 s; per slab and
+        16-column tile c (four: one 64-column packed tile) acc[s][c] += hi * b[c],
+        then acc[s][c] += lo * b[c], in that order for each accumulator (hi
+        products of both slabs of a pair first, so the two products into one
+        accumulator are eight instructions apart).
 
 Every accumulator gets exactly the products, in exactly the order, of the plain
 per-slab loop this replaces, so results are bit-for-bit the same.
@@ -73,7 +74,7 @@ def gateup(NS: int) -> str:
             % (NS, "\\n\\t".join(L), ", ".join(outs), ", ".join(ins)))
 
 
-def down(NS: int) -> str:
+def down(NS: int, C: int = 4) -> str:
     P = NS // 2
     L = []
 
@@ -93,18 +94,18 @@ def down(NS: int) -> str:
         for half in (0, 1):  # hi products of both slabs, then lo
             for j in range(2):
                 s = 2 * p + j
-                for c in range(2):
+                for c in range(C):
                     L.append("%s %%[c%d_%d], %%[f%d], %%[b%d], %%[c%d_%d]" % (MFMA, s, c, base + 2 * j + half, c, s, c))
         if p + 1 < P:
             L.append("s_waitcnt lgkmcnt(0)")
-    outs = ['[c%d_%d] "+v"(c[%d][%d])' % (s, cc, s, cc) for s in range(NS) for cc in range(2)]
+    outs = ['[c%d_%d] "+v"(c[%d][%d])' % (s, cc, s, cc) for s in range(NS) for cc in range(C)]
     outs += ['[f%d] "=&v"(f[%d])' % (i, i) for i in range(8)]
-    ins = ['[b%d] "v"(b[%d])' % (i, i) for i in range(2)] + ['[hi] "v"(hi)', '[lo] "v"(lo)']
-    return ("    static __device__ __forceinline__ void down(f32x4 (&c)[%d][2], const bf16x8 (&b)[2], uint32_t hi, "
+    ins = ['[b%d] "v"(b[%d])' % (i, i) for i in range(C)] + ['[hi] "v"(hi)', '[lo] "v"(lo)']
+    return ("    static __device__ __forceinline__ void down(f32x4 (&c)[%d][%d], const bf16x8 (&b)[%d], uint32_t hi, "
             "uint32_t lo) {\n"
             "        u32x4v f[8];\n"
             "        asm volatile(\"%s\"\n            : %s\n            : %s\n            : \"memory\");\n    }\n"
-            % (NS, "\\n\\t".join(L), ", ".join(outs), ", ".join(ins)))
+            % (NS, C, C, "\\n\\t".join(L), ", ".join(outs), ", ".join(ins)))
 
 
 def drain(NS: int, dims: str, idx: list) -> str:
@@ -132,7 +133,7 @@ def main() -> None:
         out.append(gateup(NS))
         out.append(down(NS))
         out.append(drain(NS, "[2][2]", ["[%d][%d][%d]" % (s, c, m) for s in range(NS) for c in range(2) for m in range(2)]))
-        out.append(drain(NS, "[2]", ["[%d][%d]" % (s, c) for s in range(NS) for c in range(2)]))
+        out.append(drain(NS, "[4]", ["[%d][%d]" % (s, c) for s in range(NS) for c in range(4)]))
         out.append("};")
         out.append("")
     out.append("}  // namespace xp")

@@ -15,12 +15,14 @@
 // on the same site's serving page]
 //
 // Work items are (expert, block of 128 of its rows, block of output columns).
-// Every wave owns 32 columns (two 16-column MFMA tiles) for all 128 rows (eight
-// 16-row slabs), so each wave decodes only its own columns' weights, and the
-// rows' activations are staged once per workgroup in LDS. Gate/up: workgroups
-// of four waves (128 columns of both matrices), two per CU. Down: workgroups of
-// eight waves (256 columns), one per CU, so each staged act tile serves twice
-// the columns; its act is four bytes per element against x's two. The grid is
+// Every wave owns its columns for all 128 rows (eight 16-row slabs), so each
+// wave decodes only its own columns' weights, and the rows' activations are
+// staged once per workgroup in LDS. Gate/up: a wave owns 32 columns (two
+// 16-column MFMA tiles) of both matrices, in workgroups of four waves (128
+// columns), two per CU. Down: a wave owns 64 columns (one packed tile; its hi
+// and lo products share the accumulators), in workgroups of eight waves (512
+// columns), one per CU, so each staged act tile serves 512 columns; its act is
+// four bytes per element against x's two. The grid is
 // persistent; items are laid out expert-major and dealt to the eight XCDs in
 // contiguous ranges so the workgroups sharing an expert's rows and weights
 // share one L2. Each group's matrix work runs in a generated asm body that
@@ -231,20 +233,20 @@ __device__ __forceinline__ int next_item(int32_t* ctr, int total) {
 #define XP_PF_GU_DMAX 4
 #endif
 // Down runs one workgroup of XP_PF_DN_WG_WAVES waves per CU when that is 8
-// (items of 256 columns: every act tile staged once serves twice the columns),
-// else two of four waves (items of 128 columns).
+// (items of 512 columns: every act tile staged once serves twice the columns),
+// else two of four waves (items of 256 columns).
 #ifndef XP_PF_DN_WG_WAVES
 #define XP_PF_DN_WG_WAVES 8
 #endif
 #define XP_PF_DN_WAVES (8 / XP_PF_DN_WG_WAVES)
 constexpr int kDnWaves = XP_PF_DN_WG_WAVES;
 constexpr int kDnThreads = 64 * kDnWaves;
-constexpr int kDnCols = 32 * kDnWaves;     // output columns per down item
+constexpr int kDnCols = 64 * kDnWaves;     // output columns per down item
 constexpr int kDnRowsPerWave = kPM / kDnWaves;
 constexpr int kAQ = kDnRowsPerWave / 8;    // act loads per thread and group
 static_assert(kDnWaves == 4 || kDnWaves == 8, "down workgroup of four or eight waves");
 #ifndef XP_PF_DN_DMAX
-#define XP_PF_DN_DMAX 4
+#define XP_PF_DN_DMAX 2
 #endif
 #ifndef XP_PF_DN_DA
 #define XP_PF_DN_DA 2
@@ -553,43 +555,44 @@ __device__ __forceinline__ void dn_item(const DnArgs& a, const Item& it, uint8_t
         }
     };
 
-    const int pt_raw = it.nt * (kDnWaves / 2) + (wave >> 1);
+    // this wave's columns: packed tile pt, 16-column tiles c = 0 .. 3 of it, column
+    // 16 c + lane % 16 (tile 0 when past the last tile: nothing is stored for it)
+    const int pt_raw = it.nt * kDnWaves + wave;
     const bool live = pt_raw * 64 < H;
     const int pt = live ? pt_raw : 0;
-    const int c0 = (wave & 1) * 32;
     const xp_expert ex = a.experts[it.e];
-    const int col = c0 + (lane & 15);
+    const int col = lane & 15;
     const int word = lane >> 4;
     const int frag_off = (lane & 15) * 64 + ((word ^ x_swz(lane & 15)) * 16);
     gwords_t dc = (gwords_t)(ex.down_codes) + (size_t)pt * G * 256 + col * 4 + word;
     gbytes1_t ds = (gbytes1_t)(ex.down_scales) + (size_t)pt * G * 64 + col;
-    uint32_t bc[D][2], bs[D][2];
+    uint32_t bc[D][4], bs[D][4];
     auto load_b = [&](int slot, int g) {
         g = min(g, G - 1);
-        bc[slot][0] = dc[g * 256];
-        bc[slot][1] = dc[g * 256 + 64];
-        bs[slot][0] = ds[g * 64];
-        bs[slot][1] = ds[g * 64 + 16];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            bc[slot][c] = dc[g * 256 + 64 * c];
+            bs[slot][c] = ds[g * 64 + 16 * c];
+        }
     };
-    bf16x8 bf[2][2];
+    bf16x8 bf[2][4];
     auto decode_b = [&](int buf, int slot) {
-        if (wave_scales_pow2(bs[slot][0], bs[slot][1], 0x38u, 0x38u)) {  // two fragments: pad with 1.0
-            bf[buf][0] = decode8_pow2(bc[slot][0], e4m3f(bs[slot][0]));
-            bf[buf][1] = decode8_pow2(bc[slot][1], e4m3f(bs[slot][1]));
+        if (wave_scales_pow2(bs[slot][0], bs[slot][1], bs[slot][2], bs[slot][3])) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) bf[buf][c] = decode8_pow2(bc[slot][c], e4m3f(bs[slot][c]));
         } else {
-            bf[buf][0] = decode8(bc[slot][0], e4m3f(bs[slot][0]));
-            bf[buf][1] = decode8(bc[slot][1], e4m3f(bs[slot][1]));
+#pragma unroll
+            for (int c = 0; c < 4; ++c) bf[buf][c] = decode8(bc[slot][c], e4m3f(bs[slot][c]));
         }
     };
 
     // LDS byte addresses of the two act halves
     const uint32_t hi_lds = (uint32_t)(size_t)(lvoid_t)sHi, lo_lds = (uint32_t)(size_t)(lvoid_t)sLo;
-    f32x4 acc[NS][2];
+    f32x4 acc[NS][4];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        acc[s][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-        acc[s][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[s][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
     for (int u = 0; u < D; ++u) load_b(u, u);
@@ -630,12 +633,12 @@ __device__ __forceinline__ void dn_item(const DnArgs& a, const Item& it, uint8_t
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
+            for (int c = 0; c < 4; ++c) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = s * 16 + (lane >> 4) * 4 + r;
                     if (row < it.rows)
-                        a.out[(size_t)sEntry[row] * H + pt * 64 + c0 + c * 16 + (lane & 15)] = acc[s][c][r];
+                        a.out[(size_t)sEntry[row] * H + pt * 64 + c * 16 + (lane & 15)] = acc[s][c][r];
                 }
             }
         }
