@@ -18,23 +18,34 @@ two register sets of a pair instead of one per slab. Every read the block issues
 landed when it ends (the last pair issues no reads, the others end on their wait),
 so no output register is written after the block.
 
-gateup: fragment of slab s at x + 1024 s (16 rows x 32 bf16, the swizzled LDS tile),
+gate/up: fragment of slab s at x + 1024 s (16 rows x 32 bf16, the swizzled LDS tile),
         four products per slab: acc[s][c][m] += frag * b[2m + c] (c = 16-column
-        tile, m = 0 gate / 1 up), i.e. b = {gate 0, gate 1, up 0, up 1}.
+        tile, m = 0 gate / 1 up), i.e. b = {gate 0, gate 1, up 0, up 1}. A group
+        is two asm statements: gateup_dec reads the four code words and the first
+        two fragments and, once the words are in, decodes them into n with their
+        power-of-two scales (frags only issues the fragment reads, for groups the
+        caller decodes itself); gateup_tail waits for the fragments and runs the
+        matrix instructions with the reads of the later pairs.
 down:   act as bf16 hi and lo halves at hi + 1024 s and lo + 1024 s; per slab and
         16-column tile c (four: one 64-column packed tile) acc[s][c] += hi * b[c],
         then acc[s][c] += lo * b[c], in that order for each accumulator (hi
         products of both slabs of a pair first, so the two products into one
-        accumulator are eight instructions apart).
+        accumulator are eight instructions apart). down_dec also decodes the next
+        group's weights into n while the first pair's reads are in flight.
 
-Every accumulator gets exactly the products, in exactly the order, of the plain
-per-slab loop this replaces, so results are bit-for-bit the same.
+The converts apply only the exponent of their fp32 scale operand, which is exact
+for power-of-two scales; for a group with another scale the caller decodes the
+words itself (gate/up before the body, down again after it). Every accumulator
+gets exactly the products, in exactly the order, of a plain per-slab loop.
 
 Hazards: a fragment register set is overwritten only by reads issued after the
 matrix instructions that read it (a read's data returns long after those have
-taken their A operands). The first matrix instruction of a block follows at least
-three instructions (two reads and a wait), more than the two wait states a
-matrix instruction needs after a VALU write of its B operand or accumulator.
+taken their A operands). The first matrix instruction of down_dec follows at least
+three instructions (reads and a wait), and gateup_tail opens with two wait states
+and a wait: more than the two wait states a matrix instruction needs after a VALU
+write of its B operand or accumulator. The fragment registers gateup_dec and
+frags leave in flight must not be touched before gateup_tail; the assembly is
+checked for that.
 The compiler does not see the matrix instructions inside the blocks, so the
 callers run `drain` (20 wait states, with the accumulators as operands) before
 any other instruction reads the accumulators.
@@ -44,17 +55,56 @@ import sys
 MFMA = "v_mfma_f32_16x16x32_bf16"
 
 
-def gateup(NS: int) -> str:
-    P = NS // 2
+def gateup_dec() -> str:
+    """First half of a gate/up group whose weights are decoded in the group body:
+    the four code words (gate 0, gate 1, up 0, up 1 of the wave's columns) and
+    the first two activation fragments are read, and once the words are in (the
+    fragments still in flight) they are decoded into n with their power-of-two
+    scales. gateup_tail waits for the fragments and runs the group."""
     L = []
+    for q, off in enumerate((0, 256, 2048, 2304)):
+        L.append("ds_read_b32 %%[w%d], %%[wa]%s" % (q, " offset:%d" % off if off else ""))
+    L.append("ds_read_b128 %[f0], %[x]")
+    L.append("ds_read_b128 %[f1], %[x] offset:1024")
+    L.append("s_waitcnt lgkmcnt(2)")
+    for q in range(4):
+        L.append("v_cvt_f32_fp8_e32 %%[n%d], %%[s%d]" % (4 * q + 3, q))
+        for b in range(4):
+            L.append("v_cvt_scalef32_pk_bf16_fp4 %%[n%d], %%[w%d], %%[n%d]%s"
+                     % (4 * q + b, q, 4 * q + 3, "" if b == 0 else " op_sel:[%d,%d,0]" % (b & 1, b >> 1)))
+    outs = ['[n%d] "=&v"(n[%d][%d])' % (4 * q + b, q, b) for q in range(4) for b in range(4)]
+    outs += ['[w%d] "=&v"(w[%d])' % (q, q) for q in range(4)]
+    outs += ['[f0] "=&v"(f[0])', '[f1] "=&v"(f[1])']
+    ins = ['[x] "v"(x)', '[wa] "v"(wa)'] + ['[s%d] "v"(sb[%d])' % (q, q) for q in range(4)]
+    return ("    static __device__ __forceinline__ void gateup_dec(uint32_t x, uint32_t wa, const uint32_t (&sb)[4], "
+            "uint32_t (&n)[4][4], u32x4v (&f)[2]) {\n"
+            "        uint32_t w[4];\n"
+            "        asm volatile(\"%s\"\n            : %s\n            : %s\n            : \"memory\");\n    }\n"
+            % ("\\n\\t".join(L), ", ".join(outs), ", ".join(ins)))
+
+
+def frags() -> str:
+    """The first two activation fragment reads of a gate/up group body, left in
+    flight for gateup_tail (the path that decodes its weights outside the body)."""
+    return ("    static __device__ __forceinline__ void frags(uint32_t x, u32x4v (&f)[2]) {\n"
+            "        asm volatile(\"ds_read_b128 %[f0], %[x]\\n\\tds_read_b128 %[f1], %[x] offset:1024\"\n"
+            "            : [f0] \"=&v\"(f[0]), [f1] \"=&v\"(f[1])\n            : [x] \"v\"(x)\n"
+            "            : \"memory\");\n    }\n")
+
+
+def gateup_tail(NS: int) -> str:
+    """The rest of a gate/up group after gateup_dec: the group body with its
+    first two fragments already requested (in f)."""
+    P = NS // 2
+    # two wait states for a VALU write of an accumulator or B register the
+    # compiler may place between the two halves
+    L = ["s_nop 1", "s_waitcnt lgkmcnt(0)"]
 
     def rd(buf: int, p: int) -> None:
         for j in range(2):
             off = (2 * p + j) * 1024
             L.append("ds_read_b128 %%[f%d], %%[x]%s" % (2 * buf + j, " offset:%d" % off if off else ""))
 
-    rd(0, 0)
-    L.append("s_waitcnt lgkmcnt(0)")
     for p in range(P):
         if p + 1 < P:
             rd((p + 1) % 2, p + 1)
@@ -66,15 +116,16 @@ def gateup(NS: int) -> str:
             L.append("s_waitcnt lgkmcnt(0)")
     outs = ['[c%d_%d_%d] "+v"(c[%d][%d][%d])' % (s, cc, m, s, cc, m)
             for s in range(NS) for cc in range(2) for m in range(2)]
-    outs += ['[f%d] "=&v"(f[%d])' % (i, i) for i in range(4)]
+    outs += ['[f0] "+v"(f[0])', '[f1] "+v"(f[1])', '[f2] "=&v"(g[0])', '[f3] "=&v"(g[1])']
     ins = ['[b%d] "v"(b[%d])' % (i, i) for i in range(4)] + ['[x] "v"(x)']
-    return ("    static __device__ __forceinline__ void gateup(f32x4 (&c)[%d][2][2], const bf16x8 (&b)[4], uint32_t x) {\n"
-            "        u32x4v f[4];\n"
+    return ("    static __device__ __forceinline__ void gateup_tail(f32x4 (&c)[%d][2][2], const bf16x8 (&b)[4], "
+            "u32x4v (&f)[2], uint32_t x) {\n"
+            "        u32x4v g[2];\n"
             "        asm volatile(\"%s\"\n            : %s\n            : %s\n            : \"memory\");\n    }\n"
             % (NS, "\\n\\t".join(L), ", ".join(outs), ", ".join(ins)))
 
 
-def down(NS: int, C: int = 4) -> str:
+def down(NS: int, C: int = 4, dec: bool = False) -> str:
     P = NS // 2
     L = []
 
@@ -86,6 +137,15 @@ def down(NS: int, C: int = 4) -> str:
             L.append("ds_read_b128 %%[f%d], %%[lo]%s" % (4 * buf + 2 * j + 1, o))
 
     rd(0, 0)
+    if dec:
+        # the next group's weights, decoded while the first pair's reads are in
+        # flight: word q's E4M3 scale byte to fp32 into n[q][3], which then serves
+        # as the scale operand of the four converts (the last one overwrites it)
+        for q in range(C):
+            L.append("v_cvt_f32_fp8_e32 %%[n%d], %%[s%d]" % (4 * q + 3, q))
+            for b in range(4):
+                L.append("v_cvt_scalef32_pk_bf16_fp4 %%[n%d], %%[w%d], %%[n%d]%s"
+                         % (4 * q + b, q, 4 * q + 3, "" if b == 0 else " op_sel:[%d,%d,0]" % (b & 1, b >> 1)))
     L.append("s_waitcnt lgkmcnt(0)")
     for p in range(P):
         if p + 1 < P:
@@ -101,11 +161,18 @@ def down(NS: int, C: int = 4) -> str:
     outs = ['[c%d_%d] "+v"(c[%d][%d])' % (s, cc, s, cc) for s in range(NS) for cc in range(C)]
     outs += ['[f%d] "=&v"(f[%d])' % (i, i) for i in range(8)]
     ins = ['[b%d] "v"(b[%d])' % (i, i) for i in range(C)] + ['[hi] "v"(hi)', '[lo] "v"(lo)']
-    return ("    static __device__ __forceinline__ void down(f32x4 (&c)[%d][%d], const bf16x8 (&b)[%d], uint32_t hi, "
-            "uint32_t lo) {\n"
-            "        u32x4v f[8];\n"
+    if dec:
+        outs += ['[n%d] "=&v"(n[%d][%d])' % (4 * q + b, q, b) for q in range(C) for b in range(4)]
+        ins += ['[w%d] "v"(w[%d])' % (q, q) for q in range(C)] + ['[s%d] "v"(sb[%d])' % (q, q) for q in range(C)]
+        head = ("    static __device__ __forceinline__ void down_dec(f32x4 (&c)[%d][%d], const bf16x8 (&b)[%d], "
+                "uint32_t hi, uint32_t lo, const uint32_t (&w)[%d], const uint32_t (&sb)[%d], uint32_t (&n)[%d][4]) {\n"
+                % (NS, C, C, C, C, C))
+    else:
+        head = ("    static __device__ __forceinline__ void down(f32x4 (&c)[%d][%d], const bf16x8 (&b)[%d], uint32_t hi, "
+                "uint32_t lo) {\n" % (NS, C, C))
+    return (head + "        u32x4v f[8];\n"
             "        asm volatile(\"%s\"\n            : %s\n            : %s\n            : \"memory\");\n    }\n"
-            % (NS, C, C, "\\n\\t".join(L), ", ".join(outs), ", ".join(ins)))
+            % ("\\n\\t".join(L), ", ".join(outs), ", ".join(ins)))
 
 
 def drain(NS: int, dims: str, idx: list) -> str:
@@ -128,10 +195,15 @@ def main() -> None:
         "template <int NS> struct PfGroup;",
         "",
     ]
+    out.append("struct PfDec {")
+    out.append(gateup_dec())
+    out.append(frags())
+    out.append("};")
+    out.append("")
     for NS in (2, 4, 6, 8):
         out.append("template <> struct PfGroup<%d> {" % NS)
-        out.append(gateup(NS))
-        out.append(down(NS))
+        out.append(gateup_tail(NS))
+        out.append(down(NS, dec=True))
         out.append(drain(NS, "[2][2]", ["[%d][%d][%d]" % (s, c, m) for s in range(NS) for c in range(2) for m in range(2)]))
         out.append(drain(NS, "[4]", ["[%d][%d]" % (s, c) for s in range(NS) for c in range(4)]))
         out.append("};")

@@ -272,21 +272,24 @@ constexpr int kSTile = 4 * 64;     // scale bytes per group: (matrix, packed til
 #define XP_PF_GU_NB 4              // LDS buffers per ring (groups staged ahead: NB - 1)
 #endif
 
-// A wave's four weight words (gate tile 0, gate tile 1, up tile 0, up tile 1
-// of its columns) and their four scale bytes from the LDS ring, waited for
-// inside the asm block: the reads follow direct global-to-LDS loads whose
-// completion the kernel orders itself (vmcnt and a barrier), and the compiler,
-// which cannot tell the ring's buffers apart, would otherwise wait for every
-// load in flight before each read. The activation fragments are read the same
-// way, inside the generated group bodies.
-__device__ __forceinline__ void lds_weights(uint32_t waddr, uint32_t saddr, uint32_t (&bc)[4], uint32_t (&bs)[4]) {
-    asm volatile("ds_read_b32 %0, %8\n\tds_read_b32 %1, %8 offset:256\n\t"
-                 "ds_read_b32 %2, %8 offset:2048\n\tds_read_b32 %3, %8 offset:2304\n\t"
-                 "ds_read_u8 %4, %9\n\tds_read_u8 %5, %9 offset:16\n\t"
-                 "ds_read_u8 %6, %9 offset:128\n\tds_read_u8 %7, %9 offset:144\n\ts_waitcnt lgkmcnt(0)"
-                 : "=&v"(bc[0]), "=&v"(bc[1]), "=&v"(bc[2]), "=&v"(bc[3]), "=&v"(bs[0]), "=&v"(bs[1]), "=&v"(bs[2]),
-                   "=&v"(bs[3])
-                 : "v"(waddr), "v"(saddr) : "memory");
+// A wave's four scale bytes (gate tile 0, gate tile 1, up tile 0, up tile 1 of
+// its columns), or its four weight words, from the LDS ring, waited for inside
+// the asm block: the reads follow direct global-to-LDS loads whose completion
+// the kernel orders itself (vmcnt and a barrier), and the compiler, which
+// cannot tell the ring's buffers apart, would otherwise wait for every load in
+// flight before each read. The activation fragments are read the same way,
+// inside the generated group bodies.
+__device__ __forceinline__ void lds_scales(uint32_t saddr, uint32_t (&bs)[4]) {
+    asm volatile("ds_read_u8 %0, %4\n\tds_read_u8 %1, %4 offset:16\n\t"
+                 "ds_read_u8 %2, %4 offset:128\n\tds_read_u8 %3, %4 offset:144\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(bs[0]), "=&v"(bs[1]), "=&v"(bs[2]), "=&v"(bs[3])
+                 : "v"(saddr) : "memory");
+}
+__device__ __forceinline__ void lds_codes(uint32_t waddr, uint32_t (&bc)[4]) {
+    asm volatile("ds_read_b32 %0, %4\n\tds_read_b32 %1, %4 offset:256\n\t"
+                 "ds_read_b32 %2, %4 offset:2048\n\tds_read_b32 %3, %4 offset:2304\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(bc[0]), "=&v"(bc[1]), "=&v"(bc[2]), "=&v"(bc[3])
+                 : "v"(waddr) : "memory");
 }
 
 // Every operand of a group arrives by direct global-to-LDS loads, NB - 1
@@ -298,12 +301,15 @@ __device__ __forceinline__ void lds_weights(uint32_t waddr, uint32_t saddr, uint
 // 16L .. 16L+15 of it, i.e. row L/4 of the 16 and chunk position L%4, so it
 // reads the row's chunk (L%4) ^ swz(L/4).
 // Per group step a wave issues those four loads (compiler fences keep the
-// order), reads the group's activation fragments, runs its matrix
+// order), reads and decodes the group's weights and runs its matrix
 // instructions, waits until its own loads of the next group have landed (a
 // fixed vmcnt: the loads issued after them), passes a barrier that publishes
-// every wave's, and reads and decodes the next group's weights while the
-// matrix work drains. A buffer is refilled only after the barrier that follows
-// every wave's last read of it.
+// every wave's, and reads the next group's scale bytes. When every scale byte
+// of the wave is a power of two (the vote taken on them), the group body reads
+// the code words and the first activation fragments together and decodes the
+// words while the fragments are in flight; otherwise the words are read and
+// decoded in full before the body. A buffer is refilled only after the barrier
+// that follows every wave's last read of it.
 template <int NS, int D>
 __device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint8_t* sX, uint8_t* sW, uint8_t* sS,
                                         const int* sEntry) {
@@ -350,17 +356,7 @@ __device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint8_t
     // its weights in the ring: block (matrix, wave/2), column c0 + t*16 + lane%16, word `word`
     const uint32_t w_lds = (uint32_t)(size_t)(lvoid_t)sW + (wave >> 1) * 1024 + (c0 + (lane & 15)) * 16 + word * 4;
     const uint32_t s_lds = (uint32_t)(size_t)(lvoid_t)sS + (wave >> 1) * 64 + c0 + (lane & 15);
-    uint32_t bc[4], bs[4];
-    bf16x8 bf[2][4];
-    auto decode_b = [&](int buf) {
-        if (wave_scales_pow2(bs[0], bs[1], bs[2], bs[3])) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) bf[buf][q] = decode8_pow2(bc[q], e4m3f(bs[q]));
-        } else {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) bf[buf][q] = decode8(bc[q], e4m3f(bs[q]));
-        }
-    };
+    uint32_t bs[4];
     // fragment reads: row 16s + (lane & 15), chunk `word`, at its swizzled position
     const int frag_off = (lane & 15) * 64 + ((word ^ x_swz(lane & 15)) * 16);
     const uint32_t x_lds = (uint32_t)(size_t)(lvoid_t)sX + frag_off;   // LDS byte address
@@ -382,19 +378,33 @@ __device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint8_t
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_imm<0, true>());
     __syncthreads();
-    lds_weights(w_lds, s_lds, bc, bs);
-    decode_b(0);
+    lds_scales(s_lds, bs);
+    bool pow2 = wave_scales_pow2(bs[0], bs[1], bs[2], bs[3]);
 
     for (int g0 = 0; g0 < G; g0 += D) {
 #pragma unroll
         for (int u = 0; u < D; ++u) {
             const int g = g0 + u;
-            const int cur = u & 1;
             // group g + NB - 1 into the buffers group g - 1 used (every wave
             // finished reading them before the last barrier)
             dma(g + NB - 1);
             mem_fence_compiler();
-            PfGroup<NS>::gateup(acc, bf[cur], x_lds + (uint32_t)((g % NB) * kXTile));
+            const uint32_t xb = x_lds + (uint32_t)((g % NB) * kXTile), wb = w_lds + (uint32_t)((g % NB) * kWTile);
+            bf16x8 b[4];
+            u32x4v f[2];
+            if (pow2) {
+                uint32_t n[4][4];
+                PfDec::gateup_dec(xb, wb, bs, n, f);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) b[q] = __builtin_bit_cast(bf16x8, u32x4v{n[q][0], n[q][1], n[q][2], n[q][3]});
+            } else {
+                uint32_t bc[4];
+                lds_codes(wb, bc);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) b[q] = decode8(bc[q], e4m3f(bs[q]));
+                PfDec::frags(xb, f);
+            }
+            PfGroup<NS>::gateup_tail(acc, b, f, xb);
             // this wave's loads of group g+1 have landed; the barrier publishes
             // every wave's (a plain barrier: __syncthreads' release fence would
             // wait for every load in flight)
@@ -402,9 +412,8 @@ __device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint8_t
             __builtin_amdgcn_s_waitcnt(waitcnt_imm<kAfter, true>());
             __builtin_amdgcn_s_barrier();
             mem_fence_compiler();
-            const uint32_t nb = (uint32_t)((g + 1) % NB);
-            lds_weights(w_lds + nb * kWTile, s_lds + nb * kSTile, bc, bs);
-            decode_b(cur ^ 1);
+            lds_scales(s_lds + (uint32_t)(((g + 1) % NB) * kSTile), bs);
+            pow2 = wave_scales_pow2(bs[0], bs[1], bs[2], bs[3]);
         }
     }
     // no load of this item may still be in flight into the buffers
@@ -613,9 +622,20 @@ __device__ __forceinline__ void dn_item(const DnArgs& a, const Item& it, uint8_t
             const int cur = u & 1;
             const int buf = (g >> 1) & 1;  // LDS buffers hold two groups each
             const uint32_t off = (uint32_t)((buf * 2 + cur) * kXTile + frag_off);
-            PfGroup<NS>::down(acc, bf[cur], hi_lds + off, lo_lds + off);
             const int nslot = (u + 1) % D;
-            decode_b(cur ^ 1, nslot);
+            // group g's matrix work, with group g+1's weights decoded inside the
+            // same asm body (while its first fragment reads are in flight) by the
+            // convert that applies a power-of-two scale; when any scale of the
+            // wave is not one, they are decoded again in full after it
+            uint32_t n[4][4];
+            PfGroup<NS>::down_dec(acc, bf[cur], hi_lds + off, lo_lds + off, bc[nslot], bs[nslot], n);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                bf[cur ^ 1][c] = __builtin_bit_cast(bf16x8, u32x4v{n[c][0], n[c][1], n[c][2], n[c][3]});
+            if (!wave_scales_pow2(bs[nslot][0], bs[nslot][1], bs[nslot][2], bs[nslot][3])) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) bf[cur ^ 1][c] = decode8(bc[nslot][c], e4m3f(bs[nslot][c]));
+            }
             load_b(nslot, g + 1 + D);
             if (u & 1) {
                 const int s0 = (u + 1) % kDA, s1 = (u + 2) % kDA;
