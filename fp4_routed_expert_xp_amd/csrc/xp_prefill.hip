@@ -545,13 +545,18 @@ __device__ __forceinline__ void dn_item(const DnArgs& a, const Item& it, uint8_t
         arow_q[q] = a.act + (size_t)sEntry[r] * I + 4 * c8;
         soff_q[q] = (uint32_t)(r * 64 + (((c8 >> 1) ^ x_swz(r & 15)) * 16) + (c8 & 1) * 8);
     }
+    // Only the waves whose rows fall in the item's NS slabs stage act: the
+    // matrix work reads no other rows (the condition is uniform per wave).
+    const bool stage = __builtin_amdgcn_readfirstlane(wave) * kDnRowsPerWave < NS * 16;
     u32x4v ra[kDA][kAQ];
     auto load_a = [&](int slot, int g) {
+        if (!stage) return;
         g = min(g, G - 1);
 #pragma unroll
         for (int q = 0; q < kAQ; ++q) ra[slot][q] = *(const u32x4v*)(arow_q[q] + 32 * g);
     };
     auto store_a = [&](int buf, int slot, int half) {
+        if (!stage) return;
         uint8_t* th = (uint8_t*)sHi + (size_t)(buf * 2 + half) * kXTile;
         uint8_t* tl = (uint8_t*)sLo + (size_t)(buf * 2 + half) * kXTile;
 #pragma unroll
