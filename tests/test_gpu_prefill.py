@@ -247,6 +247,27 @@ def test_prefill_chunk_release_width(prefill_layer):
     log("  %d chosen rows: worst per-row relative error %.2e" % (len(rows), worst))
 
 
+# hidden 1536: an odd number (three) of 512-column down items per row block
+WIDE = dataclasses.replace(TINY, name="wide", H=1536, I=256, E=16, k=4, seed=1121, weight_seed=1121)
+
+
+@pytest.mark.parametrize("R", [5, 100, 600])
+def test_short_last_blocks_match_oracle(R):
+    """Experts whose last row block has at most two slabs, against the float64
+    oracle on every row: few rows per expert (every block short), and 150 rows
+    per expert on average (full blocks and short ones side by side)."""
+    layer = DeviceLayer(WIDE, 0)
+    x = synth.activations(WIDE.seed, R, R, WIDE.H)
+    lg = synth.logits(WIDE.seed, R, R, WIDE.E, bias_sigma=0.5)
+    res = run_prefill(layer, x, lg)
+    count = np.bincount(res["topk_id"].ravel(), minlength=WIDE.E)
+    tails = int(np.sum((count > 0) & (count - ((count - 1) // 128) * 128 <= 32)))
+    log("wide R=%d: %d experts with a last block of at most 32 rows" % (R, tails))
+    assert tails > 0
+    worst = check_rows(res, oracle_rows(layer, x, lg))
+    log("  worst per-row relative error %.2e" % worst)
+
+
 def test_prefill_largest_experts_and_topk():
     """1024 experts and top-16 (four experts per thread in the workgroups' block scan)."""
     cfg = dataclasses.replace(TINY, name="maxed", H=128, I=64, E=1024, k=16, seed=1202, weight_seed=1202)
