@@ -3,7 +3,8 @@
 
 Run: python3 gen_prefill_asm.py > xp_prefill_asm.h   (the header is committed; the build does not run this)
 
-Each helper runs one group (K = 32) for NS 16-row slabs of one wave's tile, reading
+Each helper runs one group (K = 32) for NS 16-row slabs of one wave's tile (NS = 1..8;
+slabs go in pairs, the last alone when NS is odd), reading
 the activation fragments from LDS itself so that the reads of the next two slabs
 are in flight while the current two slabs' matrix instructions issue:
 
@@ -95,20 +96,20 @@ def frags() -> str:
 def gateup_tail(NS: int) -> str:
     """The rest of a gate/up group after gateup_dec: the group body with its
     first two fragments already requested (in f)."""
-    P = NS // 2
+    P = (NS + 1) // 2
     # two wait states for a VALU write of an accumulator or B register the
     # compiler may place between the two halves
     L = ["s_nop 1", "s_waitcnt lgkmcnt(0)"]
 
     def rd(buf: int, p: int) -> None:
-        for j in range(2):
+        for j in range(min(2, NS - 2 * p)):
             off = (2 * p + j) * 1024
             L.append("ds_read_b128 %%[f%d], %%[x]%s" % (2 * buf + j, " offset:%d" % off if off else ""))
 
     for p in range(P):
         if p + 1 < P:
             rd((p + 1) % 2, p + 1)
-        for j in range(2):
+        for j in range(min(2, NS - 2 * p)):
             s, f = 2 * p + j, 2 * (p % 2) + j
             for c, m in ((0, 0), (1, 0), (0, 1), (1, 1)):
                 L.append("%s %%[c%d_%d_%d], %%[f%d], %%[b%d], %%[c%d_%d_%d]" % (MFMA, s, c, m, f, 2 * m + c, s, c, m))
@@ -126,11 +127,11 @@ def gateup_tail(NS: int) -> str:
 
 
 def down(NS: int, C: int = 4, dec: bool = False) -> str:
-    P = NS // 2
+    P = (NS + 1) // 2
     L = []
 
     def rd(buf: int, p: int) -> None:
-        for j in range(2):
+        for j in range(min(2, NS - 2 * p)):
             off = (2 * p + j) * 1024
             o = " offset:%d" % off if off else ""
             L.append("ds_read_b128 %%[f%d], %%[hi]%s" % (4 * buf + 2 * j, o))
@@ -152,7 +153,7 @@ def down(NS: int, C: int = 4, dec: bool = False) -> str:
             rd((p + 1) % 2, p + 1)
         base = 4 * (p % 2)
         for half in (0, 1):  # hi products of both slabs, then lo
-            for j in range(2):
+            for j in range(min(2, NS - 2 * p)):
                 s = 2 * p + j
                 for c in range(C):
                     L.append("%s %%[c%d_%d], %%[f%d], %%[b%d], %%[c%d_%d]" % (MFMA, s, c, base + 2 * j + half, c, s, c))
@@ -200,7 +201,7 @@ def main() -> None:
     out.append(frags())
     out.append("};")
     out.append("")
-    for NS in (2, 4, 6, 8):
+    for NS in range(1, 9):
         out.append("template <> struct PfGroup<%d> {" % NS)
         out.append(gateup_tail(NS))
         out.append(down(NS, dec=True))

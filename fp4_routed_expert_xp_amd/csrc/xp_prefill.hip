@@ -188,8 +188,8 @@ __device__ __forceinline__ Item item_at(int i, int n_tiles, const int* sP, int E
 
 // Item dealing. The eight XCDs own contiguous eighths of the item list
 // (workgroup b runs on XCD b % 8), so the workgroups that share an expert's
-// rows and weights share an L2. Items differ up to fourfold in cost (2 to 8
-// slabs), so a workgroup takes its next item from its XCD's counter and, once
+// rows and weights share an L2. Items differ up to eightfold in matrix work (1
+// to 8 slabs), so a workgroup takes its next item from its XCD's counter and, once
 // that range is done, from the other XCDs' in turn. The counters are int32
 // slots of the workspace header, zeroed by pf_counters_zero before each launch.
 constexpr int kPfCtrGateUp = 32;   // header slots 32 .. 39
@@ -222,7 +222,7 @@ __device__ __forceinline__ int next_item(int32_t* ctr, int total) {
 // g's matrix instructions drain. The loop bodies have no branches (D divides
 // the group count; refills past the end re-read the last group), so the wait
 // counts follow the rings exactly. NS = 16-row slabs computed: the item's rows
-// rounded up to 2, 4, 6 or 8 slabs.
+// rounded up to a multiple of 16.
 //
 // Per kernel: resident workgroups per CU (gate/up; down's follows from its
 // workgroup size), the deepest weight ring and down's activation ring.
@@ -439,12 +439,11 @@ __device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint8_t
     }
 }
 
-// Slab count class (2, 4, 6 or 8) and ring depth (8, 4 or 1: the largest that
-// divides the group count), then the item.
+// Slab count (the item's rows in 16-row slabs, 1 to 8) and ring depth (the
+// deepest allowed that divides the group count), then the item.
 template <int kDMax, typename F>
 __device__ __forceinline__ void dispatch_item(int rows, int G, F&& f) {
-    const int slabs = (rows + 15) >> 4;
-    const int ns = slabs <= 2 ? 2 : slabs <= 4 ? 4 : slabs <= 6 ? 6 : 8;
+    const int ns = (rows + 15) >> 4;
     // ring depths are even (a step is two groups) and G is even (H and I are
     // multiples of 64): the deepest that divides G, else half of it, else 2
     static_assert(kDMax % 2 == 0, "weight ring depth must be even");
@@ -452,13 +451,17 @@ __device__ __forceinline__ void dispatch_item(int rows, int G, F&& f) {
     const int d = (G % dh == 0) ? dh : (G % dl == 0) ? dl : 2;
 #define XP_PF_CASE(NS_, D_) \
     if (ns == NS_ && d == D_) { f.template run<NS_, D_>(); return; }
-    XP_PF_CASE(2, dh) XP_PF_CASE(4, dh) XP_PF_CASE(6, dh) XP_PF_CASE(8, dh)
+#define XP_PF_CASES(D_) \
+    XP_PF_CASE(1, D_) XP_PF_CASE(2, D_) XP_PF_CASE(3, D_) XP_PF_CASE(4, D_) \
+    XP_PF_CASE(5, D_) XP_PF_CASE(6, D_) XP_PF_CASE(7, D_) XP_PF_CASE(8, D_)
+    XP_PF_CASES(dh)
     if constexpr (dl != dh) {
-        XP_PF_CASE(2, dl) XP_PF_CASE(4, dl) XP_PF_CASE(6, dl) XP_PF_CASE(8, dl)
+        XP_PF_CASES(dl)
     }
     if constexpr (dl != 2 && dh != 2) {
-        XP_PF_CASE(2, 2) XP_PF_CASE(4, 2) XP_PF_CASE(6, 2) XP_PF_CASE(8, 2)
+        XP_PF_CASES(2)
     }
+#undef XP_PF_CASES
 #undef XP_PF_CASE
 }
 

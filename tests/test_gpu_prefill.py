@@ -177,14 +177,13 @@ def prefill_layer():
 
 
 def slab_class(rows_in_block: int) -> int:
-    """16-row slabs a 128-row block of an expert computes: its rows rounded up to 2, 4, 6 or 8."""
-    s = (rows_in_block + 15) // 16
-    return 2 if s <= 2 else 4 if s <= 4 else 6 if s <= 6 else 8
+    """16-row slabs a 128-row block of an expert computes: its rows rounded up to a multiple of 16."""
+    return (rows_in_block + 15) // 16
 
 
 def shape_chosen_rows(count, offset, entry, k, R, seed=5):
-    """Rows of a chunk picked by the work items they fall in: for every slab class
-    2/4/6/8, the first and last row of the last (ragged) block of two experts of
+    """Rows of a chunk picked by the work items they fall in: for every slab count
+    1 to 8, the first and last row of the last (ragged) block of two experts of
     that class; the last row of the busiest expert's ragged block and the first
     row of one of its full blocks; every row of the least-loaded routed expert
     (up to four); the first and last chunk rows; and random rows up to 40."""
@@ -192,7 +191,7 @@ def shape_chosen_rows(count, offset, entry, k, R, seed=5):
     E = len(count)
     routed = [e for e in range(E) if count[e] > 0]
     members = lambda e: [int(entry[i]) // k for i in range(offset[e], offset[e + 1])]
-    by_class = {2: [], 4: [], 6: [], 8: []}
+    by_class = {c: [] for c in range(1, 9)}
     for e in routed:
         last = count[e] - 128 * ((count[e] - 1) // 128)
         by_class[slab_class(last)].append(e)
@@ -219,7 +218,7 @@ def test_prefill_chunk_release_width(prefill_layer):
 
     Routing, counts, offsets and entries are bit-exact for every row; act, out
     and y are compared with the float64 oracle on 40 rows chosen by the work
-    item they fall in (every slab class of an expert's ragged last block, the
+    item they fall in (every slab count of an expert's ragged last block, the
     busiest expert's full and ragged blocks, the least-loaded expert) plus
     random rows; the whole chunk is checked to be finite.
     """
@@ -237,10 +236,10 @@ def test_prefill_chunk_release_width(prefill_layer):
     for name in ("act", "out", "y"):
         assert np.all(np.isfinite(res[name])), name
     rows, by_class, busiest, least = shape_chosen_rows(count, offset, entry, cfg.k, cfg.R)
-    log("  busiest expert %d with %d rows, least-loaded %d with %d; %d experts routed; experts per slab class %s"
+    log("  busiest expert %d with %d rows, least-loaded %d with %d; %d experts routed; experts per slab count %s"
         % (busiest, count[busiest], least, count[least], int((count > 0).sum()),
            {c: len(v) for c, v in by_class.items()}))
-    assert all(len(v) > 0 for v in by_class.values()), "the chunk exercises every slab class"
+    assert all(len(v) > 0 for v in by_class.values()), "the chunk exercises every slab count"
     assert len(rows) >= 32
     ref = oracle_rows(prefill_layer, x[rows], lg[rows])
     worst = check_rows(res, ref, rows)
