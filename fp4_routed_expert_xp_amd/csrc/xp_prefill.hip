@@ -318,7 +318,7 @@ __device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint8_t
     constexpr int kPerStep = 4;                      // loads per wave per group
     constexpr int kAfter = kPerStep * (NB - 2);      // issued after group g+1's, at step g's wait
     static_assert(kAfter <= 63, "vmcnt range");
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int G = a.G, I = a.I;
 
     // activation sources of this lane (rows 32w + L/4 and 32w + 16 + L/4)
@@ -529,7 +529,7 @@ template <int NS, int D, int kDA>
 __device__ __forceinline__ void dn_item(const DnArgs& a, const Item& it, uint8_t* sHi, uint8_t* sLo,
                                         const int* sEntry) {
     static_assert(kDA % 2 == 0 && D % kDA == 0, "rings hold whole steps of two groups");
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int G = a.G, H = a.H, I = a.I;
 
     // act staging: thread (wave w, lane L) moves floats 4c .. 4c+3 (c = L % 8) of
