@@ -144,16 +144,16 @@ __device__ __forceinline__ bf16x8 decode8_pow2(uint32_t v, float s) {
     return __builtin_bit_cast(bf16x8, r);
 }
 
-// True on every lane when the four E4M3 scale bytes a..d of every lane of the
-// wave are positive normal powers of two (sign and mantissa bits clear,
-// exponent field non-zero); then decode8_pow2 is exact for the whole group.
+// True on every lane when the four E4M3 scale bytes a..d (each zero-extended
+// to 32 bits) of every lane of the wave are positive normal powers of two: no
+// byte has a sign or mantissa bit (their OR has none), and then each byte is
+// its exponent field alone, which must be non-zero (their minimum is). Then
+// decode8_pow2 is exact for the whole group.
 __device__ __forceinline__ bool wave_scales_pow2(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-    const uint32_t v = a | (b << 8) | (c << 16) | (d << 24);
-    const bool sign_mant_clear = (v & 0x87878787u) == 0u;
-    // each byte's exponent field (a multiple of 8 in 0x08..0x78) plus 0x78 sets
-    // that byte's top bit exactly when the field is non-zero
-    const bool exp_nonzero = (((v & 0x78787878u) + 0x78787878u) & 0x80808080u) == 0x80808080u;
-    return __all(sign_mant_clear && exp_nonzero);
+    const uint32_t o = a | b | c | d;
+    const uint32_t m = min(min(a, b), min(c, d));
+    return (__builtin_amdgcn_ballot_w64((o & 0x87u) == 0u) & __builtin_amdgcn_ballot_w64(m != 0u)) ==
+           __builtin_amdgcn_read_exec();
 }
 
 // Item i -> (expert, first row of the block, rows in the block, column block).
@@ -331,18 +331,21 @@ __device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint8_t
     const xp_expert ex = a.experts[it.e];
     const int fpt_raw = it.nt * 2 + (wave & 1);
     const int fpt = fpt_raw * 64 < I ? fpt_raw : 0;
-    const uint8_t* wsrc = (wave >> 1 ? ex.up_codes : ex.gate_codes) + (size_t)fpt * G * 1024 + lane * 16;
-    const uint8_t* ssrc = (wave >> 1 ? ex.up_scales : ex.gate_scales) + (size_t)fpt * G * 64 + (lane & 15) * 4;
+    // a uniform base and a per-lane 32-bit offset, so each group's load takes
+    // the scalar-base address form (the group step is a scalar add)
+    const uint8_t* wbase = (wave >> 1 ? ex.up_codes : ex.gate_codes) + (size_t)fpt * G * 1024;
+    const uint8_t* sbase = (wave >> 1 ? ex.up_scales : ex.gate_scales) + (size_t)fpt * G * 64;
+    const uint32_t woff = (uint32_t)lane * 16, soff = (uint32_t)(lane & 15) * 4;
     auto dma = [&](int g) {
         const int gc = min(g, G - 1);
         const int buf = g % NB;
         uint8_t* dx = sX + (size_t)buf * kXTile + wave * 2048;
         __builtin_amdgcn_global_load_lds((gvoid_t)(xa0 + gc * 32), (lvoid_t)dx, 16, 0, 0);
         __builtin_amdgcn_global_load_lds((gvoid_t)(xa1 + gc * 32), (lvoid_t)(dx + 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((gvoid_t)(wsrc + (size_t)gc * 1024),
+        __builtin_amdgcn_global_load_lds((gvoid_t)(wbase + (size_t)gc * 1024 + woff),
                                          (lvoid_t)(sW + (size_t)buf * kWTile + wave * 1024), 16, 0, 0);
         if (lane < 16)
-            __builtin_amdgcn_global_load_lds((gvoid_t)(ssrc + (size_t)gc * 64),
+            __builtin_amdgcn_global_load_lds((gvoid_t)(sbase + (size_t)gc * 64 + soff),
                                              (lvoid_t)(sS + (size_t)buf * kSTile + wave * 64), 4, 0, 0);
     };
 
@@ -500,7 +503,12 @@ __global__ __launch_bounds__(kPThreads, XP_PF_GU_WAVES) void prefill_gateup_kern
         __syncthreads();
         const int i = sItem;
         if (i < 0) break;
-        const Item it = item_at<true>(i, n_tiles, sP, E, count);
+        Item it = item_at<true>(i, n_tiles, sP, E, count);
+        // uniform: the expert table entry and the weight bases are then scalar
+        it.e = __builtin_amdgcn_readfirstlane(it.e);
+        it.nt = __builtin_amdgcn_readfirstlane(it.nt);
+        it.m0 = __builtin_amdgcn_readfirstlane(it.m0);
+        it.rows = __builtin_amdgcn_readfirstlane(it.rows);
         if (t < kPM) sEntry[t] = entry[offset[it.e] + it.m0 + min(t, it.rows - 1)];
         __syncthreads();
         dispatch_item<XP_PF_GU_DMAX>(it.rows, a.G, GuRun{a, it, sX, sW, sS, sEntry});
@@ -581,15 +589,18 @@ __device__ __forceinline__ void dn_item(const DnArgs& a, const Item& it, uint8_t
     const int col = lane & 15;
     const int word = lane >> 4;
     const int frag_off = (lane & 15) * 64 + ((word ^ x_swz(lane & 15)) * 16);
-    gwords_t dc = (gwords_t)(ex.down_codes) + (size_t)pt * G * 256 + col * 4 + word;
-    gbytes1_t ds = (gbytes1_t)(ex.down_scales) + (size_t)pt * G * 64 + col;
+    // uniform bases and per-lane 32-bit offsets, so the loads take the
+    // scalar-base address form
+    gwords_t dc = (gwords_t)(ex.down_codes) + (size_t)pt * G * 256;
+    gbytes1_t ds = (gbytes1_t)(ex.down_scales) + (size_t)pt * G * 64;
+    const uint32_t dco = (uint32_t)(col * 4 + word), dso = (uint32_t)col;
     uint32_t bc[D][4], bs[D][4];
     auto load_b = [&](int slot, int g) {
         g = min(g, G - 1);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            bc[slot][c] = dc[g * 256 + 64 * c];
-            bs[slot][c] = ds[g * 64 + 16 * c];
+            bc[slot][c] = dc[(size_t)(g * 256 + 64 * c) + dco];
+            bs[slot][c] = ds[(size_t)(g * 64 + 16 * c) + dso];
         }
     };
     bf16x8 bf[2][4];
@@ -706,7 +717,12 @@ __global__ __launch_bounds__(kDnThreads, XP_PF_DN_WAVES) void prefill_down_kerne
         __syncthreads();
         const int i = sItem;
         if (i < 0) break;
-        const Item it = item_at<false>(i, n_tiles, sP, E, count);
+        Item it = item_at<false>(i, n_tiles, sP, E, count);
+        // uniform: the expert table entry and the weight bases are then scalar
+        it.e = __builtin_amdgcn_readfirstlane(it.e);
+        it.nt = __builtin_amdgcn_readfirstlane(it.nt);
+        it.m0 = __builtin_amdgcn_readfirstlane(it.m0);
+        it.rows = __builtin_amdgcn_readfirstlane(it.rows);
         if (t < kPM) sEntry[t] = entry[offset[it.e] + it.m0 + min(t, it.rows - 1)];
         __syncthreads();
         dispatch_item<XP_PF_DN_DMAX>(it.rows, a.G, DnRun{a, it, sHi, sLo, sEntry});
