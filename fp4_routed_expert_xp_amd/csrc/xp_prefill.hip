@@ -257,7 +257,13 @@ struct GuArgs {
     const xp_expert* experts;
     float* act;
     int k, H, I, G;
+    uint32_t x_bytes;   // bytes of x (below 4 GiB)
 };
+
+// Word 3 of a raw buffer resource on gfx9: 32-bit data format, no swizzle or
+// stride, so a buffer load reads bytes base + offset, and offsets at or past
+// the record count read zero.
+constexpr int kBufWord3 = 0x00020000;
 
 // Activation tiles of one 32-wide group: 128 rows x 64 B, no padding; the
 // four 16-byte chunks of row r sit at chunk position c ^ swz(r % 16), swz(p) =
@@ -324,29 +330,33 @@ __device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint8_t
     // activation sources of this lane (rows 32w + L/4 and 32w + 16 + L/4)
     const int lrow = lane >> 2;
     const int lchunk = (lane & 3) ^ x_swz(lrow);
-    const uint16_t* xa0 = a.x + (size_t)(sEntry[32 * wave + lrow] / a.k) * a.H + lchunk * 8;
-    const uint16_t* xa1 = a.x + (size_t)(sEntry[32 * wave + 16 + lrow] / a.k) * a.H + lchunk * 8;
+    // All loads below are buffer loads into LDS: a per-lane 32-bit offset and
+    // the group's step as a scalar offset, so they cost no vector instructions
+    // per group (x is below 4 GiB, checked by the entry point).
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, (short)0, (int)a.x_bytes, kBufWord3);
+    const uint32_t xo0 = (uint32_t)(sEntry[32 * wave + lrow] / a.k) * (uint32_t)(a.H * 2) + (uint32_t)(lchunk * 16);
+    const uint32_t xo1 = (uint32_t)(sEntry[32 * wave + 16 + lrow] / a.k) * (uint32_t)(a.H * 2) + (uint32_t)(lchunk * 16);
     // weight block fetched by this wave: matrix wave/2, packed tile it.nt*2 + wave%2
     // (tile 0 when past the last tile: I not a multiple of 128; nothing is stored for it)
     const xp_expert ex = a.experts[it.e];
     const int fpt_raw = it.nt * 2 + (wave & 1);
     const int fpt = fpt_raw * 64 < I ? fpt_raw : 0;
-    // a uniform base and a per-lane 32-bit offset, so each group's load takes
-    // the scalar-base address form (the group step is a scalar add)
     const uint8_t* wbase = (wave >> 1 ? ex.up_codes : ex.gate_codes) + (size_t)fpt * G * 1024;
     const uint8_t* sbase = (wave >> 1 ? ex.up_scales : ex.gate_scales) + (size_t)fpt * G * 64;
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc((void*)wbase, (short)0, G * 1024, kBufWord3);
+    const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc((void*)sbase, (short)0, G * 64, kBufWord3);
     const uint32_t woff = (uint32_t)lane * 16, soff = (uint32_t)(lane & 15) * 4;
     auto dma = [&](int g) {
         const int gc = min(g, G - 1);
         const int buf = g % NB;
         uint8_t* dx = sX + (size_t)buf * kXTile + wave * 2048;
-        __builtin_amdgcn_global_load_lds((gvoid_t)(xa0 + gc * 32), (lvoid_t)dx, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((gvoid_t)(xa1 + gc * 32), (lvoid_t)(dx + 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((gvoid_t)(wbase + (size_t)gc * 1024 + woff),
-                                         (lvoid_t)(sW + (size_t)buf * kWTile + wave * 1024), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lvoid_t)dx, 16, xo0, (uint32_t)gc * 64, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lvoid_t)(dx + 1024), 16, xo1, (uint32_t)gc * 64, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lvoid_t)(sW + (size_t)buf * kWTile + wave * 1024), 16, woff,
+                                                 (uint32_t)gc * 1024, 0, 0);
         if (lane < 16)
-            __builtin_amdgcn_global_load_lds((gvoid_t)(sbase + (size_t)gc * 64 + soff),
-                                             (lvoid_t)(sS + (size_t)buf * kSTile + wave * 64), 4, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lvoid_t)(sS + (size_t)buf * kSTile + wave * 64), 4, soff,
+                                                     (uint32_t)gc * 64, 0, 0);
     };
 
     // This wave's columns: packed tile pt, columns c0 .. c0+31 of it. A wave past
@@ -484,7 +494,7 @@ struct GuRun {
 __global__ __launch_bounds__(kPThreads, XP_PF_GU_WAVES) void prefill_gateup_kernel(
     const xp_expert* __restrict__ experts, const uint16_t* __restrict__ x, const int32_t* __restrict__ count,
     const int32_t* __restrict__ offset, const int32_t* __restrict__ entry, int E, int k, int H, int I,
-    float* __restrict__ act, int32_t* __restrict__ ctr) {
+    uint32_t x_bytes, float* __restrict__ act, int32_t* __restrict__ ctr) {
     __shared__ __attribute__((aligned(1024))) uint8_t sX[XP_PF_GU_NB * kXTile];
     __shared__ __attribute__((aligned(1024))) uint8_t sW[XP_PF_GU_NB * kWTile];
     __shared__ __attribute__((aligned(256))) uint8_t sS[XP_PF_GU_NB * kSTile];
@@ -495,7 +505,7 @@ __global__ __launch_bounds__(kPThreads, XP_PF_GU_WAVES) void prefill_gateup_kern
     const int t = threadIdx.x;
     const int n_tiles = (I + kPN - 1) / kPN;
     const int total = block_prefix<kPThreads>(count, E, sP, swave) * n_tiles;
-    const GuArgs a{x, experts, act, k, H, I, H / 32};
+    const GuArgs a{x, experts, act, k, H, I, H / 32, x_bytes};
     __shared__ int sItem;
 
     for (;;) {
@@ -761,13 +771,16 @@ XP_API int xp_prefill_gateup(const xp_dims* dims, int32_t rows, const uint16_t* 
     if (rows == 0) return XP_OK;
     if (!x || !experts || !workspace || !act) return XP_ERR_NULL;
     if (ws_bytes < ws_layout(dims, rows).total) return XP_ERR_WORKSPACE;
+    const unsigned long long x_bytes = (unsigned long long)rows * (unsigned long long)dims->hidden * 2ull;
+    if (x_bytes >= (1ull << 32)) return XP_ERR_SHAPE;   // x is addressed with 32-bit offsets
     WsPtrs w = ws_ptrs(workspace, dims, rows);
     const int n_tiles = (dims->inter + kPN - 1) / kPN;
     const int grid = prefill_grid(rows, dims->top_k, dims->n_experts, n_tiles, XP_PF_GU_WAVES);
     int32_t* ctr = w.hdr + kPfCtrGateUp;
     hipLaunchKernelGGL(pf_counters_zero, dim3(1), dim3(64), 0, (hipStream_t)stream, ctr);
     hipLaunchKernelGGL(prefill_gateup_kernel, dim3(grid), dim3(kPThreads), 0, (hipStream_t)stream, experts, x,
-                       w.count, w.offset, w.entry, dims->n_experts, dims->top_k, dims->hidden, dims->inter, act, ctr);
+                       w.count, w.offset, w.entry, dims->n_experts, dims->top_k, dims->hidden, dims->inter,
+                       (uint32_t)x_bytes, act, ctr);
     return launch_status();
 }
 

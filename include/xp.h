@@ -204,7 +204,9 @@ int xp_decode_static(const xp_dims* dims, int32_t rows, const float* logits, con
  * xp_gateup_rows / xp_down_rows, and meet the per-row tolerance (max |err| /
  * max |ref| <= 1e-3 against the float64 definition) instead. act must be
  * finite for xp_prefill_down (an infinite act gives NaN in out). Any row count
- * is accepted; xp_combine finishes the layer. Each call launches a one-block
+ * is accepted for which x (rows x H bf16) is below 4 GiB: xp_prefill_gateup
+ * addresses x with 32-bit offsets and refuses a larger x with XP_ERR_SHAPE
+ * (524,287 rows at H = 4096). xp_combine finishes the layer. Each call launches a one-block
  * kernel that zeroes its work counters in the workspace header (int32 slots
  * 32..39 for gate/up, 40..47 for down; the plan is only read), then the
  * contraction, whose workgroups take items from those counters: prefill calls

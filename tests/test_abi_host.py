@@ -104,6 +104,10 @@ def test_null_rows_and_workspace_checks():
     assert L.xp_prefill_gateup(ctypes.byref(d), 4, None, P, P, need, P, None) == xp.XP_ERR_NULL
     assert L.xp_prefill_down(ctypes.byref(d), 4, P, P, P, need, None, None) == xp.XP_ERR_NULL
     assert L.xp_prefill_gateup(ctypes.byref(d), 4, P, P, P, need - 1, P, None) == xp.XP_ERR_WORKSPACE
+    # x of 4 GiB or more is refused (its loads use 32-bit offsets), before any launch
+    big = (1 << 32) // (2 * d.hidden)
+    assert L.xp_prefill_gateup(ctypes.byref(d), big, P, P, P, xp.xp_workspace_bytes(d, big), P,
+                               None) == xp.XP_ERR_SHAPE
     assert L.xp_prefill_down(ctypes.byref(d), 4, P, P, P, need - 1, P, None) == xp.XP_ERR_WORKSPACE
     assert L.xp_pack_matrix(100, 64, P, P, P, P, None) == xp.XP_ERR_SHAPE
     assert L.xp_pack_matrix(64, 48, P, P, P, P, None) == xp.XP_ERR_SHAPE
