@@ -214,15 +214,17 @@ __device__ __forceinline__ int next_item(int32_t* ctr, int total) {
 
 // ------------------------------------------------------------------ gate/up
 // The K loops are software-pipelined over 32-wide groups. Gate/up stages every
-// operand by direct global-to-LDS loads into a ring of NB groups (below). Down
-// keeps the weight words and scale bytes of the next D groups in flight in a
-// register ring, each thread keeps the act of the next kDA groups in flight and
-// stages the next two groups (as bf16 hi and lo) in LDS at every other group
-// (one barrier per two groups). Both decode group g+1's weights while group
-// g's matrix instructions drain. The loop bodies have no branches (D divides
-// the group count; refills past the end re-read the last group), so the wait
-// counts follow the rings exactly. NS = 16-row slabs computed: the item's rows
-// rounded up to a multiple of 16.
+// operand by buffer loads into LDS, a ring of NB groups (below). Down keeps the
+// weight words and scale bytes of the next D groups in flight in a register
+// ring, each thread keeps the act of the next kDA groups in flight and stages
+// the next two groups (as bf16 hi and lo) in LDS at every other group (one
+// barrier per two groups). Where the scales are powers of two the weights are
+// decoded inside the generated group bodies while the first activation
+// fragments are in flight: gate/up its own group's, down the next group's. The
+// loop bodies branch only on that per-group choice of decode, uniform per wave
+// (D divides the group count; refills past the end re-read the last group), so
+// the wait counts follow the rings exactly. NS = 16-row slabs computed: the
+// item's rows rounded up to a multiple of 16.
 //
 // Per kernel: resident workgroups per CU (gate/up; down's follows from its
 // workgroup size), the deepest weight ring and down's activation ring.
@@ -298,8 +300,9 @@ __device__ __forceinline__ void lds_codes(uint32_t waddr, uint32_t (&bc)[4]) {
                  : "v"(waddr) : "memory");
 }
 
-// Every operand of a group arrives by direct global-to-LDS loads, NB - 1
-// groups ahead, into a ring of NB buffers: per wave and group one 16-byte load
+// Every operand of a group arrives by buffer loads into LDS (the LDS side is
+// M0 plus 16 or 4 bytes per lane), NB - 1 groups ahead, into a ring of NB
+// buffers: per wave and group one 16-byte load
 // per lane for each of two 16-row halves of its 32 activation rows, one 16-byte
 // load per lane of weight codes (wave w fetches the 1 KiB of (matrix w/2,
 // packed tile w%2): 64 columns x 16 B) and one 4-byte load on lanes 0-15 of that
