@@ -48,8 +48,8 @@ FP8_TRAFFIC = dict(sources="15929da9", fetch_kib=8532.4, write_kib=133.3)
 FP8_SOURCES = ("xp_fp8.hip", "xp_common.h")
 # The same for the two prefill kernels on the 4,096-row chunk (mean over 4 seeded
 # layers), tied to xp_prefill.hip and its headers.
-PF_GU_TRAFFIC = dict(sources="ec5e4973", fetch_kib=1736928.7, write_kib=263390.1)
-PF_DN_TRAFFIC = dict(sources="ec5e4973", fetch_kib=864590.7, write_kib=524467.1)
+PF_GU_TRAFFIC = dict(sources="eb15eb68", fetch_kib=1735580.1, write_kib=262586.3)
+PF_DN_TRAFFIC = dict(sources="eb15eb68", fetch_kib=865989.7, write_kib=524464.3)
 PREFILL_SOURCES = ("xp_prefill.hip", "xp_prefill_asm.h", "xp_common.h")
 
 

@@ -156,6 +156,16 @@ __device__ __forceinline__ bool wave_scales_pow2(uint32_t a, uint32_t b, uint32_
            __builtin_amdgcn_read_exec();
 }
 
+// silu(g) = g / (1 + e^-g) with the hardware exponential and reciprocal (a few
+// ulp each; this path is held to the per-row tolerance against the float64
+// definition, not to the decode chain's bits): six instructions instead of a
+// library exp and a correctly rounded division. Large negative g gives -0 or
+// 0 (e^-g overflows to +inf), large positive g gives g, NaN stays NaN.
+__device__ __forceinline__ float silu_fast(float g) {
+    const float e = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);
+    return g * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
 // Item i -> (expert, first row of the block, rows in the block, column block).
 // An expert's items are contiguous. COL_MAJOR orders them column block first:
 // the expert's row blocks of one column block are neighbours, so they are in
@@ -446,8 +456,7 @@ __device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint8_t
                     const int row = s * 16 + (lane >> 4) * 4 + r;
                     if (row < it.rows) {
                         const float gv = acc[s][c][0][r], uv = acc[s][c][1][r];
-                        a.act[(size_t)sEntry[row] * I + pt * 64 + c0 + c * 16 + (lane & 15)] =
-                            (gv / (1.0f + expf(-gv))) * uv;
+                        a.act[(size_t)sEntry[row] * I + pt * 64 + c0 + c * 16 + (lane & 15)] = silu_fast(gv) * uv;
                     }
                 }
             }
