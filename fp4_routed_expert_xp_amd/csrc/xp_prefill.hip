@@ -446,19 +446,17 @@ __device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint8_t
     __builtin_amdgcn_s_waitcnt(waitcnt_imm<0, false>());
     PfGroup<NS>::drain(acc);
 
+    // Rows past it.rows in the last slab repeat the item's last row (sEntry is
+    // clamped), so their results are that row's bits: storing them to its
+    // address writes the same values, and needs no per-lane branch.
     if (live) {
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
+            for (int r = 0; r < 4; ++r) {
+                float* dst = a.act + (size_t)sEntry[s * 16 + (lane >> 4) * 4 + r] * I + pt * 64 + c0 + (lane & 15);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = s * 16 + (lane >> 4) * 4 + r;
-                    if (row < it.rows) {
-                        const float gv = acc[s][c][0][r], uv = acc[s][c][1][r];
-                        a.act[(size_t)sEntry[row] * I + pt * 64 + c0 + c * 16 + (lane & 15)] = silu_fast(gv) * uv;
-                    }
-                }
+                for (int c = 0; c < 2; ++c) dst[c * 16] = silu_fast(acc[s][c][0][r]) * acc[s][c][1][r];
             }
         }
     }
@@ -692,15 +690,13 @@ __device__ __forceinline__ void dn_item(const DnArgs& a, const Item& it, uint8_t
     PfGroup<NS>::drain(acc);
     if (live) {
 #pragma unroll
+        // rows past it.rows repeat the last row (see gu_item): no per-lane branch
         for (int s = 0; s < NS; ++s) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
+            for (int r = 0; r < 4; ++r) {
+                float* dst = a.out + (size_t)sEntry[s * 16 + (lane >> 4) * 4 + r] * H + pt * 64 + (lane & 15);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = s * 16 + (lane >> 4) * 4 + r;
-                    if (row < it.rows)
-                        a.out[(size_t)sEntry[row] * H + pt * 64 + c * 16 + (lane & 15)] = acc[s][c][r];
-                }
+                for (int c = 0; c < 4; ++c) dst[c * 16] = acc[s][c][r];
             }
         }
     }
