@@ -48,8 +48,8 @@ FP8_TRAFFIC = dict(sources="15929da9", fetch_kib=8532.4, write_kib=133.3)
 FP8_SOURCES = ("xp_fp8.hip", "xp_common.h")
 # The same for the two prefill kernels on the 4,096-row chunk (mean over 4 seeded
 # layers), tied to xp_prefill.hip and its headers.
-PF_GU_TRAFFIC = dict(sources="02dae003", fetch_kib=1735081.3, write_kib=262483.5)
-PF_DN_TRAFFIC = dict(sources="02dae003", fetch_kib=866518.6, write_kib=524459.5)
+PF_GU_TRAFFIC = dict(sources="228f5abb", fetch_kib=1654531.8, write_kib=262468.0)
+PF_DN_TRAFFIC = dict(sources="228f5abb", fetch_kib=865250.3, write_kib=524458.8)
 PREFILL_SOURCES = ("xp_prefill.hip", "xp_prefill_asm.h", "xp_common.h")
 
 

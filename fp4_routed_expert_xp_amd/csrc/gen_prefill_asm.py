@@ -3,8 +3,8 @@
 
 Run: python3 gen_prefill_asm.py > xp_prefill_asm.h   (the header is committed; the build does not run this)
 
-Each helper runs one group (K = 32) for NS 16-row slabs of one wave's tile (NS = 1..8;
-slabs go in pairs, the last alone when NS is odd), reading
+Each helper runs one group (K = 32) for NS 16-row slabs of one wave's tile (NS = 1..10
+for gate/up, 1..8 for down; slabs go in pairs, the last alone when NS is odd), reading
 the activation fragments from LDS itself so that the reads of the next two slabs
 are in flight while the current two slabs' matrix instructions issue:
 
@@ -201,12 +201,13 @@ def main() -> None:
     out.append(frags())
     out.append("};")
     out.append("")
-    for NS in range(1, 9):
+    for NS in range(1, 11):   # gate/up up to 10 slabs (a block with a short last block merged), down up to 8
         out.append("template <> struct PfGroup<%d> {" % NS)
         out.append(gateup_tail(NS))
-        out.append(down(NS, dec=True))
         out.append(drain(NS, "[2][2]", ["[%d][%d][%d]" % (s, c, m) for s in range(NS) for c in range(2) for m in range(2)]))
-        out.append(drain(NS, "[4]", ["[%d][%d]" % (s, c) for s in range(NS) for c in range(4)]))
+        if NS <= 8:
+            out.append(down(NS, dec=True))
+            out.append(drain(NS, "[4]", ["[%d][%d]" % (s, c) for s in range(NS) for c in range(4)]))
         out.append("};")
         out.append("")
     out.append("}  // namespace xp")

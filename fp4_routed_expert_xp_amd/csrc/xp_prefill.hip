@@ -14,8 +14,11 @@
 // layer math; the prefill chunk of 4,096 rows is the prompt step's default size
 // on the same site's serving page]
 //
-// Work items are (expert, block of 128 of its rows, block of output columns).
-// Every wave owns its columns for all 128 rows (eight 16-row slabs), so each
+// Work items are (expert, block of 128 of its rows, block of output columns);
+// for gate/up, an expert's last block of at most 32 rows joins the full block
+// before it (an item of up to 160 rows, ten slabs), so those rows do not stream
+// the expert's weights a second time. Every wave owns its columns for all of
+// the item's rows (up to eight or ten 16-row slabs), so each
 // wave decodes only its own columns' weights, and the rows' activations are
 // staged once per workgroup in LDS. Gate/up: a wave owns 32 columns (two
 // 16-column MFMA tiles) of both matrices, in workgroups of four waves (128
@@ -34,7 +37,8 @@
 
 namespace xp {
 
-constexpr int kPM = 128;        // rows per item
+constexpr int kPM = 128;        // rows per row block
+constexpr int kPMGU = 160;      // rows per gate/up item at most: a full block with a last block of <= 32 rows merged
 constexpr int kPN = 128;        // output columns per gate/up item (two packed 64-column tiles)
 constexpr int kPThreads = 256;  // four waves
 
@@ -65,11 +69,24 @@ constexpr int waitcnt_imm() {
     return (N & 15) | ((N >> 4) << 14) | (7 << 4) | ((LGKM0 ? 0 : 15) << 8);
 }
 
-// Item bookkeeping shared by both kernels: per-expert blocks of 128 rows and
-// their prefix, rebuilt by each workgroup from the plan's counts.
-// sP[e] = row blocks of experts before e (sP[E] = all); all threads call.
-template <int NT>
-__device__ __forceinline__ int block_prefix(const int32_t* __restrict__ count, int E, int* sP, int* swave) {
+// Row blocks of an expert with c rows: 128 each, the last one short.
+__device__ __forceinline__ int row_blocks(int c) { return (c + kPM - 1) / kPM; }
+
+// Gate/up's row blocks: the same, except that a last block of at most 32 rows
+// after a full one joins it (an item of up to 160 rows), so the weights of the
+// expert's columns are streamed once for those rows instead of twice.
+__device__ __forceinline__ int gu_blocks(int c) {
+    const int nb = row_blocks(c);
+    return (nb >= 2 && c - (nb - 1) * kPM <= kPMGU - kPM) ? nb - 1 : nb;
+}
+
+// Item bookkeeping shared by both kernels: per-expert row blocks (BLOCKS(c)
+// for an expert of c rows) and their prefix, rebuilt by each workgroup from
+// the plan's counts. sP[e] = row blocks of experts before e (sP[E] = all); all
+// threads call.
+template <int NT, typename BLOCKS>
+__device__ __forceinline__ int block_prefix(const int32_t* __restrict__ count, int E, int* sP, int* swave,
+                                            BLOCKS blocks) {
     static_assert(NT >= 256, "E <= 1024 experts at most four per thread");
     const int t = threadIdx.x;
     const int per = (E + NT - 1) / NT;  // experts per thread
@@ -78,7 +95,7 @@ __device__ __forceinline__ int block_prefix(const int32_t* __restrict__ count, i
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int e = t * per + j;
-        loc[j] = (j < per && e < E) ? (count[e] + kPM - 1) / kPM : 0;
+        loc[j] = (j < per && e < E) ? blocks(count[e]) : 0;
         sum += loc[j];
     }
     const int incl = wave_incl_sum(sum);
@@ -167,6 +184,8 @@ __device__ __forceinline__ float silu_fast(float g) {
 }
 
 // Item i -> (expert, first row of the block, rows in the block, column block).
+// The last of an expert's blocks takes all its remaining rows (up to 160 with
+// gate/up's merged blocks), the others 128.
 // An expert's items are contiguous. COL_MAJOR orders them column block first:
 // the expert's row blocks of one column block are neighbours, so they are in
 // flight together and read that column block's weights through one L2 (the
@@ -192,14 +211,15 @@ __device__ __forceinline__ Item item_at(int i, int n_tiles, const int* sP, int E
         it.e = find_expert(sP, E, q);
         it.m0 = (q - sP[it.e]) * kPM;
     }
-    it.rows = min(kPM, count[it.e] - it.m0);
+    const int nb = sP[it.e + 1] - sP[it.e];
+    it.rows = it.m0 == (nb - 1) * kPM ? count[it.e] - it.m0 : kPM;
     return it;
 }
 
 // Item dealing. The eight XCDs own contiguous eighths of the item list
 // (workgroup b runs on XCD b % 8), so the workgroups that share an expert's
-// rows and weights share an L2. Items differ up to eightfold in matrix work (1
-// to 8 slabs), so a workgroup takes its next item from its XCD's counter and, once
+// rows and weights share an L2. Items differ up to tenfold in matrix work (1
+// to 10 slabs), so a workgroup takes its next item from its XCD's counter and, once
 // that range is done, from the other XCDs' in turn. The counters are int32
 // slots of the workspace header, zeroed by pf_counters_zero before each launch.
 constexpr int kPfCtrGateUp = 32;   // header slots 32 .. 39
@@ -277,13 +297,14 @@ struct GuArgs {
 // the record count read zero.
 constexpr int kBufWord3 = 0x00020000;
 
-// Activation tiles of one 32-wide group: 128 rows x 64 B, no padding; the
+// Activation tiles of one 32-wide group: 128 rows (gate/up: 160) x 64 B, no padding; the
 // four 16-byte chunks of row r sit at chunk position c ^ swz(r % 16), swz(p) =
 // ((p >> 1) ^ (p >> 3)) & 3, so a fragment read (16 rows at one chunk) is free
 // of bank conflicts whether the LDS serves 8 lanes a cycle from 32 banks or 16
 // lanes from 64.
 __device__ __forceinline__ int x_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
-constexpr int kXTile = kPM * 64;   // activation bytes per group
+constexpr int kXTile = kPM * 64;   // activation bytes per group (down's act halves)
+constexpr int kXTileGU = kPMGU * 64;   // gate/up's activation tile per group
 constexpr int kWTile = 4 * 1024;   // weight code bytes per group: (matrix, packed tile) x 64 columns x 16 B
 constexpr int kSTile = 4 * 64;     // scale bytes per group: (matrix, packed tile) x 64 columns
 #ifndef XP_PF_GU_NB
@@ -334,7 +355,7 @@ __device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint8_t
                                         const int* sEntry) {
     constexpr int NB = XP_PF_GU_NB;
     static_assert(NB >= 3 && NB <= 8, "ring");
-    constexpr int kPerStep = 4;                      // loads per wave per group
+    constexpr int kPerStep = NS > 8 ? 5 : 4;         // loads per wave per group
     constexpr int kAfter = kPerStep * (NB - 2);      // issued after group g+1's, at step g's wait
     static_assert(kAfter <= 63, "vmcnt range");
     const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -349,6 +370,11 @@ __device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint8_t
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, (short)0, (int)a.x_bytes, kBufWord3);
     const uint32_t xo0 = (uint32_t)(sEntry[32 * wave + lrow] / a.k) * (uint32_t)(a.H * 2) + (uint32_t)(lchunk * 16);
     const uint32_t xo1 = (uint32_t)(sEntry[32 * wave + 16 + lrow] / a.k) * (uint32_t)(a.H * 2) + (uint32_t)(lchunk * 16);
+    // rows 128 .. 159 (items of more than 8 slabs): eight more per wave, from its
+    // lanes 0 .. 31, at rows 128 + 8w + L/4 of the tile (slab 8 + w/2)
+    const int erow = 8 * (wave & 1) + ((lane & 31) >> 2);
+    const uint32_t xo2 = (uint32_t)(sEntry[kPM + 8 * wave + ((lane & 31) >> 2)] / a.k) * (uint32_t)(a.H * 2) +
+                         (uint32_t)((((lane & 3) ^ x_swz(erow))) * 16);
     // weight block fetched by this wave: matrix wave/2, packed tile it.nt*2 + wave%2
     // (tile 0 when past the last tile: I not a multiple of 128; nothing is stored for it)
     const xp_expert ex = a.experts[it.e];
@@ -362,9 +388,14 @@ __device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint8_t
     auto dma = [&](int g) {
         const int gc = min(g, G - 1);
         const int buf = g % NB;
-        uint8_t* dx = sX + (size_t)buf * kXTile + wave * 2048;
+        uint8_t* dx = sX + (size_t)buf * kXTileGU + wave * 2048;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lvoid_t)dx, 16, xo0, (uint32_t)gc * 64, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lvoid_t)(dx + 1024), 16, xo1, (uint32_t)gc * 64, 0, 0);
+        if constexpr (NS > 8) {
+            if (lane < 32)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lvoid_t)(sX + (size_t)buf * kXTileGU + 8 * 1024 + wave * 512),
+                                                         16, xo2, (uint32_t)gc * 64, 0, 0);
+        }
         __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lvoid_t)(sW + (size_t)buf * kWTile + wave * 1024), 16, woff,
                                                  (uint32_t)gc * 1024, 0, 0);
         if (lane < 16)
@@ -415,7 +446,7 @@ __device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint8_t
             // finished reading them before the last barrier)
             dma(g + NB - 1);
             mem_fence_compiler();
-            const uint32_t xb = x_lds + (uint32_t)((g % NB) * kXTile), wb = w_lds + (uint32_t)((g % NB) * kWTile);
+            const uint32_t xb = x_lds + (uint32_t)((g % NB) * kXTileGU), wb = w_lds + (uint32_t)((g % NB) * kWTile);
             bf16x8 b[4];
             u32x4v f[2];
             if (pow2) {
@@ -462,9 +493,9 @@ __device__ __forceinline__ void gu_item(const GuArgs& a, const Item& it, uint8_t
     }
 }
 
-// Slab count (the item's rows in 16-row slabs, 1 to 8) and ring depth (the
+// Slab count (the item's rows in 16-row slabs, 1 to kNSMax) and ring depth (the
 // deepest allowed that divides the group count), then the item.
-template <int kDMax, typename F>
+template <int kDMax, int kNSMax, typename F>
 __device__ __forceinline__ void dispatch_item(int rows, int G, F&& f) {
     const int ns = (rows + 15) >> 4;
     // ring depths are even (a step is two groups) and G is even (H and I are
@@ -476,7 +507,8 @@ __device__ __forceinline__ void dispatch_item(int rows, int G, F&& f) {
     if (ns == NS_ && d == D_) { f.template run<NS_, D_>(); return; }
 #define XP_PF_CASES(D_) \
     XP_PF_CASE(1, D_) XP_PF_CASE(2, D_) XP_PF_CASE(3, D_) XP_PF_CASE(4, D_) \
-    XP_PF_CASE(5, D_) XP_PF_CASE(6, D_) XP_PF_CASE(7, D_) XP_PF_CASE(8, D_)
+    XP_PF_CASE(5, D_) XP_PF_CASE(6, D_) XP_PF_CASE(7, D_) XP_PF_CASE(8, D_) \
+    if constexpr (kNSMax > 8) { XP_PF_CASE(9, D_) XP_PF_CASE(10, D_) }
     XP_PF_CASES(dh)
     if constexpr (dl != dh) {
         XP_PF_CASES(dl)
@@ -505,16 +537,16 @@ __global__ __launch_bounds__(kPThreads, XP_PF_GU_WAVES) void prefill_gateup_kern
     const xp_expert* __restrict__ experts, const uint16_t* __restrict__ x, const int32_t* __restrict__ count,
     const int32_t* __restrict__ offset, const int32_t* __restrict__ entry, int E, int k, int H, int I,
     uint32_t x_bytes, float* __restrict__ act, int32_t* __restrict__ ctr) {
-    __shared__ __attribute__((aligned(1024))) uint8_t sX[XP_PF_GU_NB * kXTile];
+    __shared__ __attribute__((aligned(1024))) uint8_t sX[XP_PF_GU_NB * kXTileGU];
     __shared__ __attribute__((aligned(1024))) uint8_t sW[XP_PF_GU_NB * kWTile];
     __shared__ __attribute__((aligned(256))) uint8_t sS[XP_PF_GU_NB * kSTile];
-    __shared__ int sEntry[kPM];
+    __shared__ int sEntry[kPMGU];
     __shared__ int sP[kMaxExperts + 1];
     __shared__ int swave[4];
 
     const int t = threadIdx.x;
     const int n_tiles = (I + kPN - 1) / kPN;
-    const int total = block_prefix<kPThreads>(count, E, sP, swave) * n_tiles;
+    const int total = block_prefix<kPThreads>(count, E, sP, swave, [](int c) { return gu_blocks(c); }) * n_tiles;
     const GuArgs a{x, experts, act, k, H, I, H / 32, x_bytes};
     __shared__ int sItem;
 
@@ -529,9 +561,9 @@ __global__ __launch_bounds__(kPThreads, XP_PF_GU_WAVES) void prefill_gateup_kern
         it.nt = __builtin_amdgcn_readfirstlane(it.nt);
         it.m0 = __builtin_amdgcn_readfirstlane(it.m0);
         it.rows = __builtin_amdgcn_readfirstlane(it.rows);
-        if (t < kPM) sEntry[t] = entry[offset[it.e] + it.m0 + min(t, it.rows - 1)];
+        if (t < kPMGU) sEntry[t] = entry[offset[it.e] + it.m0 + min(t, it.rows - 1)];
         __syncthreads();
-        dispatch_item<XP_PF_GU_DMAX>(it.rows, a.G, GuRun{a, it, sX, sW, sS, sEntry});
+        dispatch_item<XP_PF_GU_DMAX, 10>(it.rows, a.G, GuRun{a, it, sX, sW, sS, sEntry});
         __syncthreads();  // sItem, sEntry and the ring are rewritten by the next item
     }
 }
@@ -726,7 +758,7 @@ __global__ __launch_bounds__(kDnThreads, XP_PF_DN_WAVES) void prefill_down_kerne
 
     const int t = threadIdx.x;
     const int n_tiles = (H + kDnCols - 1) / kDnCols;
-    const int total = block_prefix<kDnThreads>(count, E, sP, swave) * n_tiles;
+    const int total = block_prefix<kDnThreads>(count, E, sP, swave, [](int c) { return row_blocks(c); }) * n_tiles;
     const DnArgs a{act, experts, out, H, I, I / 32};
     __shared__ int sItem;
 
@@ -743,7 +775,7 @@ __global__ __launch_bounds__(kDnThreads, XP_PF_DN_WAVES) void prefill_down_kerne
         it.rows = __builtin_amdgcn_readfirstlane(it.rows);
         if (t < kPM) sEntry[t] = entry[offset[it.e] + it.m0 + min(t, it.rows - 1)];
         __syncthreads();
-        dispatch_item<XP_PF_DN_DMAX>(it.rows, a.G, DnRun{a, it, sHi, sLo, sEntry});
+        dispatch_item<XP_PF_DN_DMAX, 8>(it.rows, a.G, DnRun{a, it, sHi, sLo, sEntry});
         __syncthreads();
     }
 }

@@ -181,25 +181,39 @@ def slab_class(rows_in_block: int) -> int:
     return (rows_in_block + 15) // 16
 
 
+def merged_first_row(n: int):
+    """Gate/up computes an expert of n rows whose last 128-row block has at most
+    32 rows after a full one as one item of n - 128 (b - 1) rows, b its block
+    count (9 or 10 slabs); returns that item's first row within the expert, or
+    None when the expert has no such item."""
+    b = (n + 127) // 128
+    return 128 * (b - 2) if b >= 2 and n - 128 * (b - 1) <= 32 else None
+
+
 def shape_chosen_rows(count, offset, entry, k, R, seed=5):
     """Rows of a chunk picked by the work items they fall in: for every slab count
     1 to 8, the first and last row of the last (ragged) block of two experts of
-    that class; the last row of the busiest expert's ragged block and the first
+    that class; for gate/up's merged items of 9 and 10 slabs, the first row of
+    two such items of each count; the last row of the busiest expert's ragged block and the first
     row of one of its full blocks; every row of the least-loaded routed expert
     (up to four); the first and last chunk rows; and random rows up to 40."""
     rows = set([0, R - 1])
     E = len(count)
     routed = [e for e in range(E) if count[e] > 0]
     members = lambda e: [int(entry[i]) // k for i in range(offset[e], offset[e + 1])]
-    by_class = {c: [] for c in range(1, 9)}
+    by_class = {c: [] for c in range(1, 11)}
     for e in routed:
         last = count[e] - 128 * ((count[e] - 1) // 128)
         by_class[slab_class(last)].append(e)
+        if merged_first_row(count[e]) is not None:
+            by_class[slab_class(count[e] - merged_first_row(count[e]))].append(e)
     for cls, es in by_class.items():
         for e in es[:2]:
             m = members(e)
             b0 = 128 * ((len(m) - 1) // 128)
             rows.update([m[b0], m[-1]])
+            if cls > 8:
+                rows.add(m[merged_first_row(len(m))])
     busiest = int(np.argmax(count))
     m = members(busiest)
     rows.add(m[-1])
@@ -220,7 +234,9 @@ def test_prefill_chunk_release_width(prefill_layer):
     and y are compared with the float64 oracle on 40 rows chosen by the work
     item they fall in (every slab count of an expert's ragged last block, the
     busiest expert's full and ragged blocks, the least-loaded expert) plus
-    random rows; the whole chunk is checked to be finite.
+    random rows; the whole chunk is checked to be finite. Gate/up's merged
+    items (a full block with a last block of at most 32 rows, 9 or 10 slabs) are
+    among the slab counts.
     """
     cfg = PREFILL
     x, lg = synth.layer_inputs(cfg, 0)
@@ -254,15 +270,19 @@ WIDE = dataclasses.replace(TINY, name="wide", H=1536, I=256, E=16, k=4, seed=112
 def test_short_last_blocks_match_oracle(R):
     """Experts whose last row block has at most two slabs, against the float64
     oracle on every row: few rows per expert (every block short), and 150 rows
-    per expert on average (full blocks and short ones side by side)."""
+    per expert on average (full blocks and short ones side by side, which
+    gate/up computes as single items of 129 to 160 rows)."""
     layer = DeviceLayer(WIDE, 0)
     x = synth.activations(WIDE.seed, R, R, WIDE.H)
     lg = synth.logits(WIDE.seed, R, R, WIDE.E, bias_sigma=0.5)
     res = run_prefill(layer, x, lg)
     count = np.bincount(res["topk_id"].ravel(), minlength=WIDE.E)
     tails = int(np.sum((count > 0) & (count - ((count - 1) // 128) * 128 <= 32)))
-    log("wide R=%d: %d experts with a last block of at most 32 rows" % (R, tails))
+    merged = sum(merged_first_row(int(n)) is not None for n in count)
+    log("wide R=%d: %d experts with a last block of at most 32 rows, %d after a full block" % (R, tails, merged))
     assert tails > 0
+    if R == 600:
+        assert merged > 0
     worst = check_rows(res, oracle_rows(layer, x, lg))
     log("  worst per-row relative error %.2e" % worst)
 
