@@ -287,6 +287,45 @@ def test_short_last_blocks_match_oracle(R):
     log("  worst per-row relative error %.2e" % worst)
 
 
+# Expert row counts on both sides of gate/up's merge rule (a last 128-row block
+# of at most 32 rows joins the full block before it): 129..160 and 288 merge,
+# 161 and 289 do not; 128 is one full block, 32 and 33 a lone short block.
+BOUNDARY_COUNTS = [129, 144, 145, 160, 161, 288, 289, 32, 33, 1, 128, 17, 0, 16, 57, 68]
+
+
+def routed_logits(counts, R, k, seed):
+    """Logits that route exactly counts[e] of the R rows' k slots to expert e:
+    the experts' slots laid out expert by expert and written column-major into
+    an R x k table (every count at most R, so no row gets an expert twice);
+    row r gives its k experts logits k, k-1, .., 1 in column order and every
+    other expert a value in [-2, -1)."""
+    E = len(counts)
+    assert sum(counts) == R * k and max(counts) <= R
+    seq = np.repeat(np.arange(E), counts)
+    table = seq.reshape(k, R).T
+    rng = np.random.default_rng(seed)
+    lg = (-2.0 + rng.random((R, E))).astype(np.float32)
+    for j in range(k):
+        lg[np.arange(R), table[:, j]] = np.float32(k - j)
+    return lg
+
+
+def test_merge_boundaries_match_oracle():
+    """Experts with exactly 129, 144, 145, 160 (one gate/up item of 9 or 10
+    slabs), 161 (a full item and a three-slab one), 288 (two items, the second
+    of 160 rows) and 289 rows, beside experts of 0, 1, 16, 17, 32, 33, 57, 68
+    and 128 rows, against the float64 oracle on every row."""
+    R = sum(BOUNDARY_COUNTS) // WIDE.k
+    layer = DeviceLayer(WIDE, 0)
+    x = synth.activations(WIDE.seed, R, R, WIDE.H)
+    lg = routed_logits(BOUNDARY_COUNTS, R, WIDE.k, seed=77)
+    res = run_prefill(layer, x, lg)
+    plan = read_plan(layer.d, R, res["ws"])
+    assert np.array_equal(plan["count"], np.array(BOUNDARY_COUNTS))
+    worst = check_rows(res, oracle_rows(layer, x, lg))
+    log("merge boundaries R=%d: worst per-row relative error %.2e" % (R, worst))
+
+
 def test_prefill_largest_experts_and_topk():
     """1024 experts and top-16 (four experts per thread in the workgroups' block scan)."""
     cfg = dataclasses.replace(TINY, name="maxed", H=128, I=64, E=1024, k=16, seed=1202, weight_seed=1202)
